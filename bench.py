@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""Fused linear cross-entropy forward + backward on one MI355X.
+
+One step = flce_forward + flce_backward (every kernel of the path) over one
+batch of synthetic input already resident in HBM.  The default workload is the
+Qwen2-7B-like LM head: B=1, T=8192 (N=8192 rows), H=3584, V=152064, bf16,
+Zipf(1.1) labels, first 20% of the sequence masked, next-token shift, mean.
+
+Prints ONE JSON line with the throughput (tokens/s over all N rows), the
+fraction of the bf16 dense MFMA peak on the 6NHV model-FLOP basis, the peak
+extra device memory, a roofline entry for the dominant kernel (its average
+launch duration measured with HIP events on its own stream inside the timed
+region) and the float64 oracle timed on the host cores on a bounded row sample.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+BF16_PEAK = 2.5e15        # MI355X dense bf16 MFMA, FLOP/s
+F32_PEAK = 157.3e12       # MI355X dense fp32 MFMA, FLOP/s
+HBM_PEAK = 8.0e12         # MI355X HBM3E, B/s
+KERNELS = ("k_fwd_lse", "k_bwd_g", "k_bwd_dw", "k_bwd_dx")
+METRIC = "fused linear-CE fwd+bwd tokens/sec and % bf16 MFMA peak; peak extra HBM bytes"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="qwen2_7b_head")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=1024)
+    return ap.parse_args()
+
+
+class HipEvents:
+    """Raw hipEvent_t handles from the HIP runtime PyTorch loaded."""
+
+    def __init__(self, n):
+        import torch  # noqa: F401  (the runtime is already in the process)
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.arr[i] = h
+        self.n = n
+
+    def elapsed_ms(self, i):
+        self.hip.hipEventSynchronize(self.arr[i + 1])
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), self.arr[i], self.arr[i + 1]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def address(self):
+        return ctypes.addressof(self.arr)
+
+    def close(self):
+        for i in range(self.n):
+            self.hip.hipEventDestroy(self.arr[i])
+
+
+def oracle_baseline(w, rows_wanted):
+    """The float64 oracle on a bounded sample of valid rows (full per-row work:
+    logits rows, softmax, dX rows and their dW contribution), extrapolated to
+    the workload's valid rows."""
+    import numpy as np
+
+    import oracle
+    y, valid = oracle.targets(w.labels, w.shift, w.ignore_index)
+    vrows = np.flatnonzero(valid)
+    n = len(vrows)
+    r = min(rows_wanted, n)
+    pick = vrows[np.linspace(0, n - 1, r).astype(np.int64)]
+    Xs = w.X[pick]
+    ys = y[pick].reshape(1, -1)
+    t0 = time.perf_counter()
+    oracle.flce(Xs, w.W, ys, ignore_index=w.ignore_index, reduction=w.reduction,
+                shift=False, mode="global")
+    t = time.perf_counter() - t0
+    t_full = t * n / r
+    cores = len(os.sched_getaffinity(0))
+    for var in ("OPENBLAS_NUM_THREADS", "OMP_NUM_THREADS"):
+        if os.environ.get(var, "").isdigit():
+            cores = min(cores, int(os.environ[var]))
+            break
+    return {
+        "value": w.N / t_full, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+        "sample": f"{r} of {n} valid rows of the {w.N}x{w.H}x{w.V} workload, forward + "
+                  f"backward in float64 numpy ({t:.1f} s), time scaled by {n}/{r}",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path "
+              "has no multi-GPU mode", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import lm_head_linear_flce_amd as F
+    import synth
+
+    dev = torch.device("cuda:0")
+    print(f"[bench] generating {args.workload}", file=sys.stderr, flush=True)
+    w = synth.workload(args.workload)
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    X = torch.from_numpy(w.X).to(dev).to(dt)
+    W = torch.from_numpy(w.W).to(dev).to(dt)
+    lab = torch.from_numpy(w.labels).to(dev)
+    dcode = F.FLCE_DTYPE_BF16 if w.dtype == "bf16" else F.FLCE_DTYPE_F32
+    n_valid = int(((lab[:, 1:] if w.shift else lab) != w.ignore_index).sum())
+    ws, ws_bytes = F.workspace(w.B, w.T, w.H, w.V, dcode, dev)
+    torch.cuda.synchronize()
+
+    def step():
+        loss, lse, _, _ = F.forward(X, W, lab, w.ignore_index, w.shift, w.reduction, ws=ws)
+        dX, dW, _ = F.backward(X, W, lab, lse, ignore_index=w.ignore_index, shift=w.shift,
+                               reduction=w.reduction, ws=ws)
+        return loss, dX, dW
+
+    # peak extra device memory of one step (inputs already resident)
+    del ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    ws, ws_bytes = F.workspace(w.B, w.T, w.H, w.V, dcode, dev)
+    loss, dX, dW = step()
+    torch.cuda.synchronize()
+    peak_extra = torch.cuda.max_memory_allocated() - base
+    out_bytes = dX.numel() * dX.element_size() + dW.numel() * dW.element_size() + 4 * w.N
+    del loss, dX, dW
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    cap = 4096
+    evs = HipEvents(2 * cap)
+
+    def timed_pass(kname, steps):
+        """`steps` steps bracketed by synchronisation; HIP events around every
+        launch of kernel `kname`.  Returns (ms per step, [launch durations])."""
+        count = ctypes.c_int(0)
+        F.flce_set_timing(kname, evs.address(), cap, count)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        F.flce_set_timing(None, 0, 0, None)
+        return ms, [evs.elapsed_ms(2 * i) for i in range(count.value)]
+
+    # per-kernel breakdown (one short pass per kernel) picks the dominant kernel
+    per_kernel = {}
+    for kname in KERNELS:
+        _, durs = timed_pass(kname, 2)
+        per_kernel[kname] = dict(total_ms_per_step=sum(durs) / 2,
+                                 avg_launch_ms=sum(durs) / max(len(durs), 1),
+                                 launches_per_step=len(durs) // 2)
+        print(f"[bench] {kname}: {len(durs) // 2} launches/step, "
+              f"{sum(durs) / 2:.3f} ms/step", file=sys.stderr, flush=True)
+    dom = max(KERNELS, key=lambda k: per_kernel[k]["total_ms_per_step"])
+
+    # the timed region: K steps, events on the dominant kernel's launches
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    step_ms, durs = timed_pass(dom, args.steps)
+    evs.close()
+    per_kernel[dom]["avg_launch_ms"] = sum(durs) / len(durs)
+    per_kernel[dom]["total_ms_per_step"] = sum(durs) / args.steps
+    launches_per_step = {k: v["launches_per_step"] for k, v in per_kernel.items()}
+
+    N, H, V, n = w.N, w.H, w.V, n_valid
+    model_flops = 6.0 * N * H * V
+    exec_flops = 8.0 * n * H * V
+    t = step_ms / 1e3
+    peak = BF16_PEAK if w.dtype == "bf16" else F32_PEAK
+    pk = per_kernel[dom]
+    # algorithmic flops of one launch of the dominant kernel: 2 n H (vocab it covers)
+    vocab_per_launch = V / max(launches_per_step[dom], 1)
+    ach = 2.0 * n * H * vocab_per_launch / (pk["avg_launch_ms"] / 1e3)
+    result = {
+        "metric": METRIC,
+        "value": N / t,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": step_ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: B={w.B} T={w.T} N={N} H={H} V={V} {w.dtype}, "
+                               f"shift={w.shift}, {w.reduction}, n_valid={n}",
+                   "global_batch": w.B, "seq_len": w.T, "parallelism": "none"},
+        "mfma_frac_model": model_flops / t / peak,
+        "tflops_model": model_flops / t / 1e12,
+        "tflops_executed": exec_flops / t / 1e12,
+        "mfma_frac_executed": exec_flops / t / peak,
+        "peak_extra_bytes": int(peak_extra),
+        "workspace_bytes": int(ws_bytes),
+        "output_bytes": int(out_bytes),
+        "logits_bytes_avoided": int(N * V * 2),
+        "kernels": {k: {kk: round(vv, 4) if isinstance(vv, float) else vv
+                        for kk, vv in v.items()} for k, v in per_kernel.items()},
+        "roofline": {"bound": "mfma", "kernel": dom, "achieved": ach / 1e12,
+                     "peak": peak / 1e12, "unit": "TFLOP/s", "frac": ach / peak,
+                     "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] oracle on the host", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = oracle_baseline(w, args.cpu_rows)
+    else:
+        result["cpu_baseline"] = None
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,154 @@
+/*
+ * flce.h -- C ABI of the fused linear cross-entropy engine for AMD MI355X
+ * (gfx950).
+ *
+ * The engine computes, for hidden states X [N, H] (N = B*T rows), an output
+ * weight W [V, H] and integer labels [B, T]:
+ *
+ *   loss = CE(X . W^T, y)      without ever holding the [N, V] logits,
+ *   dX   = G . W,  dW = G^T . X,  G = c * (softmax(X . W^T) - onehot(y))
+ *
+ * with c = grad_scale / n_valid for the mean and c = grad_scale for the sum.
+ * The identities Z = X.W^T, dX = dZ.W, dW = dZ^T.X are the ones of the ms-swift
+ * PR "feat(sft): Add optional fused linear ce for qwen2/qwen3 on npu", section
+ * "Mathematical Equivalence".  The argument set (hidden, weight, labels,
+ * ignore_index = -100, shift, reduction = "mean") is that of the
+ * linear_cross_entropy call in the LoRA-SFT blog post's CCE patch, where W is
+ * stored (vocab_size, hidden_dim).  dX is accumulated in FP32 over the whole
+ * vocabulary and rounded to the input type once, as item 2 of Megatron-LM PR
+ * "[Dev] Fix Linear-Cross-Entropy Convergence Issue" prescribes.
+ *
+ * Conventions
+ *   - Targets: with shift != 0, row (b, t) is scored against labels[b, t+1] and
+ *     the last row of every sequence has no target; with shift == 0 row i is
+ *     scored against labels[i].  A target equal to ignore_index (compared as an
+ *     int64, before any range check) marks the row as ignored.
+ *   - n_valid counts the rows that have a target; the mean divides by it.  With
+ *     n_valid == 0 the loss is 0 and all gradients are 0.
+ *   - Layouts are row-major and dense: X is [B*T, H] with H contiguous, W is
+ *     [V, H] with H contiguous, labels are [B, T] int64.
+ *   - dtype FLCE_DTYPE_BF16: X, W are bfloat16; products run on bf16 MFMA with
+ *     FP32 accumulation.  FLCE_DTYPE_F32: X, W are float32 on fp32 MFMA.
+ *   - All pointers except the workspace-size query are DEVICE pointers on the
+ *     current HIP device, 16-byte aligned, owned by the caller.  The library
+ *     allocates nothing and keeps no state between calls; the only scratch it
+ *     uses is the caller's workspace.  Calls are asynchronous on `stream`
+ *     (a hipStream_t; NULL = the null stream) and never synchronise the host.
+ *   - Two calls may run concurrently only with separate workspaces.
+ *
+ * Errors
+ *   Host-side checks run before anything is launched; on failure the function
+ *   returns a nonzero FLCE_ERR_* code and touches no output.  A label that is
+ *   neither ignore_index nor in [0, V) is found on the device: it sets
+ *   *status = FLCE_ERR_LABEL_RANGE (when status is non-NULL), the forward loss
+ *   becomes NaN and the backward gradients become NaN.  Launch failures return
+ *   FLCE_ERR_HIP.
+ */
+#ifndef FLCE_H_
+#define FLCE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define FLCE_OK 0
+#define FLCE_ERR_NULL 1        /* a required pointer is NULL               */
+#define FLCE_ERR_SHAPE 2       /* B, T, H or V out of range, or N too large */
+#define FLCE_ERR_ALIGN 3       /* H % 8 != 0 or a pointer not 16B aligned   */
+#define FLCE_ERR_DTYPE 4       /* unknown dtype / grad dtype                */
+#define FLCE_ERR_REDUCTION 5   /* unknown reduction                         */
+#define FLCE_ERR_WORKSPACE 6   /* workspace NULL or smaller than required   */
+#define FLCE_ERR_HIP 7         /* a HIP launch or query failed              */
+#define FLCE_ERR_LABEL_RANGE 8 /* device: a valid label outside [0, V)      */
+#define FLCE_ERR_ALIAS 9       /* an output aliases an input                */
+
+/* element types */
+#define FLCE_DTYPE_F32 0
+#define FLCE_DTYPE_BF16 1
+
+/* reductions */
+#define FLCE_REDUCTION_MEAN 0
+#define FLCE_REDUCTION_SUM 1
+
+/*
+ * flce_workspace_size -- bytes of device scratch that flce_forward and
+ * flce_backward need for this shape and dtype (one buffer serves both).
+ * Host-only arithmetic, no HIP call.  The figure is the engine's whole extra
+ * device memory: it grows linearly in N (per-row indices, a compacted copy of
+ * the valid rows of X, an FP32 dX accumulator and a bounded slab of softmax
+ * gradients covering a fixed vocabulary block), never with N*V.
+ *   B, T, H, V : problem sizes (B*T = N rows)
+ *   dtype      : FLCE_DTYPE_*
+ *   bytes      : out, host pointer
+ */
+int flce_workspace_size(int64_t B, int64_t T, int64_t H, int64_t V, int dtype,
+                        size_t* bytes);
+
+/*
+ * flce_forward -- loss and per-row log-sum-exp.
+ *   X [B*T, H], W [V, H] : dtype elements, device
+ *   labels [B, T]        : int64, device
+ *   ignore_index         : label value that marks a row as ignored (e.g. -100)
+ *   reduction            : FLCE_REDUCTION_MEAN or FLCE_REDUCTION_SUM
+ *   shift                : nonzero = next-token targets inside each sequence
+ *   loss                 : out, float32 scalar, device
+ *   lse [B*T]            : out, float32, device; log sum_v exp(z_iv) of every
+ *                          row with a target, 0.0 for ignored rows.  Keep it
+ *                          for flce_backward.
+ *   n_valid              : out, int64 scalar, device, may be NULL
+ *   status               : out, int32 scalar, device, may be NULL; 0 or
+ *                          FLCE_ERR_LABEL_RANGE
+ *   workspace, workspace_bytes : device scratch of flce_workspace_size bytes
+ *   stream               : hipStream_t
+ */
+int flce_forward(const void* X, const void* W, const int64_t* labels,
+                 int64_t B, int64_t T, int64_t H, int64_t V, int dtype,
+                 int64_t ignore_index, int reduction, int shift,
+                 float* loss, float* lse, int64_t* n_valid, int32_t* status,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * flce_backward -- gradients of grad_scale * loss with respect to X and W.
+ *   X, W, labels, sizes, dtype, ignore_index, reduction, shift : as forward
+ *   lse [B*T]     : float32, device, the forward's output for the same inputs
+ *   grad_scale    : float32 scalar, device (the upstream dL/dloss); NULL = 1
+ *   dX [B*T, H]   : out, device, fully overwritten (ignored rows are 0)
+ *   dW [V, H]     : out, device, fully overwritten
+ *   grad_dtype    : element type of dX and dW: the input dtype, or
+ *                   FLCE_DTYPE_F32 to receive the FP32 accumulators unrounded
+ *   status, workspace, workspace_bytes, stream : as forward
+ * dX must not alias X and dW must not alias W.  The FP32 accumulation and the
+ * single final rounding follow Megatron-LM PR "[Dev] Fix Linear-Cross-Entropy
+ * Convergence Issue", item 2.
+ */
+int flce_backward(const void* X, const void* W, const int64_t* labels,
+                  int64_t B, int64_t T, int64_t H, int64_t V, int dtype,
+                  int64_t ignore_index, int reduction, int shift,
+                  const float* lse, const float* grad_scale,
+                  void* dX, void* dW, int grad_dtype, int32_t* status,
+                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * flce_set_timing -- measurement hook for benchmarks and profilers.  While set,
+ * every launch of the kernel named `kernel` ("k_fwd_lse", "k_bwd_g",
+ * "k_bwd_dw" or "k_bwd_dx") made by flce_forward / flce_backward records
+ * events[2*i] on its stream right before the launch and events[2*i+1] right
+ * after it, where i = *count, and then increments *count (a host int), until
+ * *count reaches `capacity`.  `events` holds 2*capacity hipEvent_t handles
+ * created by the caller.  kernel == NULL (or events / count NULL) switches the
+ * hook off.  Process-wide and not thread-safe; the computation is unchanged.
+ */
+int flce_set_timing(const char* kernel, void* const* events, int capacity, int* count);
+
+/* flce_status_string -- static, NUL-terminated description of a status code. */
+const char* flce_status_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FLCE_H_ */

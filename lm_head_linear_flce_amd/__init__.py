@@ -1,0 +1,301 @@
+"""Python binding of the fused linear cross-entropy engine for MI355X.
+
+Two layers, both argument marshalling only -- every step of the computation runs
+in the HIP kernels of ``libflce.so``:
+
+* ``flce_workspace_size``, ``flce_forward``, ``flce_backward`` and
+  ``flce_status_string`` mirror the C ABI of ``include/flce.h`` one to one and
+  take raw device addresses (Python ints) and sizes;
+* ``linear_cross_entropy(hidden, weight, labels, ignore_index=-100,
+  shift=False, reduction="mean")`` is the tensor-level call with autograd, the
+  argument set of the ``linear_cross_entropy`` call in the LoRA-SFT blog post's
+  CCE patch.  PyTorch only provides device memory and the current stream.
+
+Importing the package loads ``libflce.so`` and fails loudly if it is missing;
+there is no fallback implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "FLCE_OK", "FLCE_DTYPE_F32", "FLCE_DTYPE_BF16", "FLCE_REDUCTION_MEAN",
+    "FLCE_REDUCTION_SUM", "FlceError", "flce_workspace_size", "flce_forward",
+    "flce_backward", "flce_set_timing", "flce_status_string", "linear_cross_entropy",
+    "library_path",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflce.so")
+
+# mirrors include/flce.h
+FLCE_OK = 0
+FLCE_ERR_NULL = 1
+FLCE_ERR_SHAPE = 2
+FLCE_ERR_ALIGN = 3
+FLCE_ERR_DTYPE = 4
+FLCE_ERR_REDUCTION = 5
+FLCE_ERR_WORKSPACE = 6
+FLCE_ERR_HIP = 7
+FLCE_ERR_LABEL_RANGE = 8
+FLCE_ERR_ALIAS = 9
+FLCE_DTYPE_F32 = 0
+FLCE_DTYPE_BF16 = 1
+FLCE_REDUCTION_MEAN = 0
+FLCE_REDUCTION_SUM = 1
+
+EXPORTS = ("flce_workspace_size", "flce_forward", "flce_backward", "flce_set_timing",
+           "flce_status_string")
+
+
+class FlceError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {flce_status_string(code)} (status {code})")
+
+
+def _load() -> ctypes.CDLL:
+    # PyTorch ships its own HIP runtime under the same soname; load it first so
+    # that this library binds to that one runtime and shares its streams.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with "
+            "`python lm_head_linear_flce_amd/build.py` (hipcc, gfx950)")
+    lib = ctypes.CDLL(LIB_PATH)
+    i64, i32, vp, sz = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+    lib.flce_workspace_size.argtypes = [i64, i64, i64, i64, i32, ctypes.POINTER(sz)]
+    lib.flce_workspace_size.restype = i32
+    lib.flce_forward.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, i64, i32, i32,
+                                 vp, vp, vp, vp, vp, sz, vp]
+    lib.flce_forward.restype = i32
+    lib.flce_backward.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, i64, i32, i32,
+                                  vp, vp, vp, vp, i32, vp, vp, sz, vp]
+    lib.flce_backward.restype = i32
+    lib.flce_set_timing.argtypes = [ctypes.c_char_p, vp, i32, ctypes.POINTER(i32)]
+    lib.flce_set_timing.restype = i32
+    lib.flce_status_string.argtypes = [i32]
+    lib.flce_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+_LIB = _load()
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+# ---------------------------------------------------------------------------
+# C ABI, one to one (device addresses as Python ints, 0 = NULL)
+# ---------------------------------------------------------------------------
+
+def flce_status_string(code: int) -> str:
+    return _LIB.flce_status_string(int(code)).decode()
+
+
+def flce_workspace_size(B: int, T: int, H: int, V: int, dtype: int) -> int:
+    out = ctypes.c_size_t(0)
+    rc = _LIB.flce_workspace_size(B, T, H, V, dtype, ctypes.byref(out))
+    if rc != FLCE_OK:
+        raise FlceError(rc, "flce_workspace_size")
+    return int(out.value)
+
+
+def flce_forward(X, W, labels, B, T, H, V, dtype, ignore_index, reduction, shift,
+                 loss, lse, n_valid, status, workspace, workspace_bytes, stream) -> int:
+    """Returns the status code (0 on success); raises nothing."""
+    return _LIB.flce_forward(X or None, W or None, labels or None, B, T, H, V, dtype,
+                             ignore_index, reduction, int(bool(shift)), loss or None,
+                             lse or None, n_valid or None, status or None,
+                             workspace or None, workspace_bytes, stream or None)
+
+
+def flce_backward(X, W, labels, B, T, H, V, dtype, ignore_index, reduction, shift,
+                  lse, grad_scale, dX, dW, grad_dtype, status, workspace,
+                  workspace_bytes, stream) -> int:
+    """Returns the status code (0 on success); raises nothing."""
+    return _LIB.flce_backward(X or None, W or None, labels or None, B, T, H, V, dtype,
+                              ignore_index, reduction, int(bool(shift)), lse or None,
+                              grad_scale or None, dX or None, dW or None, grad_dtype,
+                              status or None, workspace or None, workspace_bytes,
+                              stream or None)
+
+
+def flce_set_timing(kernel, events, capacity, count) -> int:
+    """kernel: str or None; events: address of 2*capacity hipEvent_t handles;
+    count: a ctypes.c_int the library increments (keep it alive while set)."""
+    return _LIB.flce_set_timing(kernel.encode() if kernel else None, events or None,
+                                capacity, ctypes.byref(count) if count is not None
+                                else None)
+
+
+# ---------------------------------------------------------------------------
+# Tensor level
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return FLCE_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return FLCE_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}; use bfloat16 or float32")
+
+
+def _reduction_code(reduction: str) -> int:
+    if reduction == "mean":
+        return FLCE_REDUCTION_MEAN
+    if reduction == "sum":
+        return FLCE_REDUCTION_SUM
+    raise ValueError(f"unsupported reduction {reduction!r} (mean or sum)")
+
+
+def _shape(hidden, weight, labels):
+    if labels.dim() == 2:
+        B, T = labels.shape
+    elif labels.dim() == 1:
+        B, T = 1, labels.shape[0]
+    else:
+        raise ValueError("labels must be [B, T] or [N]")
+    H = hidden.shape[-1]
+    if hidden.numel() != B * T * H:
+        raise ValueError(f"hidden {tuple(hidden.shape)} does not match labels "
+                         f"{tuple(labels.shape)}")
+    if weight.dim() != 2 or weight.shape[1] != H:
+        raise ValueError(f"weight must be [V, {H}], got {tuple(weight.shape)}")
+    return int(B), int(T), int(H), int(weight.shape[0])
+
+
+def _check_tensors(hidden, weight, labels):
+    torch = _torch()
+    for name, t in (("hidden", hidden), ("weight", weight), ("labels", labels)):
+        if not t.is_cuda:
+            raise ValueError(f"{name} must be a device tensor")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if hidden.dtype != weight.dtype:
+        raise TypeError("hidden and weight must have the same dtype")
+    if labels.dtype != torch.int64:
+        raise TypeError("labels must be int64")
+    if hidden.device != weight.device or hidden.device != labels.device:
+        raise ValueError("all tensors must be on one device")
+
+
+def _stream_handle(device) -> int:
+    torch = _torch()
+    return int(torch.cuda.current_stream(device).cuda_stream)
+
+
+def workspace(B, T, H, V, dtype_code, device):
+    torch = _torch()
+    nbytes = flce_workspace_size(B, T, H, V, dtype_code)
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device), nbytes
+
+
+def forward(hidden, weight, labels, ignore_index=-100, shift=False, reduction="mean",
+            ws=None):
+    """(loss, lse, n_valid, status) as device tensors, no host synchronisation."""
+    torch = _torch()
+    _check_tensors(hidden, weight, labels)
+    B, T, H, V = _shape(hidden, weight, labels)
+    dt = _dtype_code(hidden)
+    dev = hidden.device
+    if ws is None:
+        ws, nbytes = workspace(B, T, H, V, dt, dev)
+    else:
+        nbytes = ws.numel()
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    lse = torch.empty(B * T, dtype=torch.float32, device=dev)
+    n_valid = torch.empty((), dtype=torch.int64, device=dev)
+    status = torch.empty((), dtype=torch.int32, device=dev)
+    rc = flce_forward(hidden.data_ptr(), weight.data_ptr(), labels.data_ptr(), B, T, H, V,
+                      dt, int(ignore_index), _reduction_code(reduction), shift,
+                      loss.data_ptr(), lse.data_ptr(), n_valid.data_ptr(),
+                      status.data_ptr(), ws.data_ptr(), nbytes, _stream_handle(dev))
+    if rc != FLCE_OK:
+        raise FlceError(rc, "flce_forward")
+    return loss, lse, n_valid, status
+
+
+def backward(hidden, weight, labels, lse, grad_scale=None, ignore_index=-100,
+             shift=False, reduction="mean", grad_dtype=None, ws=None):
+    """(dX, dW, status); grad_scale is a device float32 scalar or None (= 1)."""
+    torch = _torch()
+    _check_tensors(hidden, weight, labels)
+    B, T, H, V = _shape(hidden, weight, labels)
+    dt = _dtype_code(hidden)
+    gd = dt if grad_dtype is None else _dtype_code(torch.empty(0, dtype=grad_dtype))
+    out_dtype = torch.float32 if gd == FLCE_DTYPE_F32 else hidden.dtype
+    dev = hidden.device
+    if ws is None:
+        ws, nbytes = workspace(B, T, H, V, dt, dev)
+    else:
+        nbytes = ws.numel()
+    dX = torch.empty(hidden.shape, dtype=out_dtype, device=dev)
+    dW = torch.empty(weight.shape, dtype=out_dtype, device=dev)
+    status = torch.empty((), dtype=torch.int32, device=dev)
+    gs = 0
+    if grad_scale is not None:
+        grad_scale = grad_scale.to(device=dev, dtype=torch.float32).contiguous()
+        gs = grad_scale.data_ptr()
+    lse = lse.to(device=dev, dtype=torch.float32).contiguous()
+    rc = flce_backward(hidden.data_ptr(), weight.data_ptr(), labels.data_ptr(), B, T, H,
+                       V, dt, int(ignore_index), _reduction_code(reduction), shift,
+                       lse.data_ptr(), gs, dX.data_ptr(), dW.data_ptr(), gd,
+                       status.data_ptr(), ws.data_ptr(), nbytes, _stream_handle(dev))
+    if rc != FLCE_OK:
+        raise FlceError(rc, "flce_backward")
+    return dX, dW, status
+
+
+def _autograd_function():
+    torch = _torch()
+
+    class LinearCrossEntropy(torch.autograd.Function):
+        @staticmethod
+        def forward(ctx, hidden, weight, labels, ignore_index, shift, reduction):
+            loss, lse, _, _ = forward(hidden, weight, labels, ignore_index, shift,
+                                      reduction)
+            ctx.save_for_backward(hidden, weight, labels, lse)
+            ctx.args = (ignore_index, shift, reduction)
+            return loss
+
+        @staticmethod
+        def backward(ctx, grad_out):
+            hidden, weight, labels, lse = ctx.saved_tensors
+            ignore_index, shift, reduction = ctx.args
+            dX, dW, _ = backward(hidden, weight, labels, lse,
+                                 grad_scale=grad_out.reshape(()),
+                                 ignore_index=ignore_index, shift=shift,
+                                 reduction=reduction)
+            return dX, dW, None, None, None, None
+
+    return LinearCrossEntropy
+
+
+_FN = None
+
+
+def linear_cross_entropy(hidden, weight, labels, ignore_index=-100, shift=False,
+                         reduction="mean"):
+    """Fused ``cross_entropy(hidden @ weight.T, targets)`` without the logits.
+
+    hidden [B, T, H] or [N, H]; weight [V, H]; labels [B, T] (or [N], one
+    sequence); bfloat16 or float32 on the GPU.  Returns a float32 scalar loss
+    tensor that backpropagates into hidden and weight."""
+    global _FN
+    if _FN is None:
+        _FN = _autograd_function()
+    if reduction not in ("mean", "sum"):
+        raise ValueError(f"unsupported reduction {reduction!r} (mean or sum)")
+    return _FN.apply(hidden.contiguous(), weight.contiguous(), labels.contiguous(),
+                     int(ignore_index), bool(shift), reduction)

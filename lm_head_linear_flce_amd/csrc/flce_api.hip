@@ -1,0 +1,407 @@
+// flce_api.hip -- host side of the C ABI declared in include/flce.h:
+// argument checks, workspace layout and the launch sequence on the caller's
+// stream.  Nothing here allocates device memory or synchronises the host.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <algorithm>
+
+#include "flce.h"
+#include "flce_kernels.h"
+
+namespace flce {
+namespace {
+
+constexpr int64_t kAlign = 256;
+constexpr int64_t kGSlabBudget = 512ll << 20;   // bytes of the G slab (target)
+constexpr int64_t kMaxI32 = 0x7FFFFFFFll;
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+int64_t cdiv(int64_t x, int64_t m) { return (x + m - 1) / m; }
+
+// Problem geometry shared by the size query and the two calls.
+struct Plan {
+  int64_t N, rows_pad, H, V, es;
+  int64_t TT, VT;           // token tiles (upper bound), vocabulary tiles
+  int64_t P;                // forward vocabulary ranges (multiple of 8)
+  int64_t Vb;               // backward vocabulary block (multiple of 256)
+  // workspace offsets (bytes)
+  int64_t o_ctr, o_idx, o_tgt, o_rowpos, o_xc;
+  int64_t o_part, o_zt, o_bsum;            // forward region
+  int64_t o_lse2, o_g, o_dx32;             // backward region
+  int64_t total;
+};
+
+int make_plan(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, Plan* p) {
+  if (B < 0 || T < 0 || H <= 0 || V <= 0) return FLCE_ERR_SHAPE;
+  if (dtype != FLCE_DTYPE_F32 && dtype != FLCE_DTYPE_BF16) return FLCE_ERR_DTYPE;
+  if (H % 8 != 0) return FLCE_ERR_ALIGN;
+  const int64_t N = B * T;
+  if (B > kMaxI32 || T > kMaxI32 || N > (1ll << 24) || H > 65536 || V > kMaxI32 - 512)
+    return FLCE_ERR_SHAPE;
+  Plan q;
+  q.N = N;
+  q.H = H;
+  q.V = V;
+  q.es = dtype == FLCE_DTYPE_BF16 ? 2 : 4;
+  q.rows_pad = round_up(N > 0 ? N : 1, kTile);
+  q.TT = q.rows_pad / kTile;
+  q.VT = cdiv(V, kTile);
+  // forward: about four launch waves of 256 CUs in (range x token tile) items
+  int64_t P = 8 * std::max<int64_t>(1, cdiv(1024, 8 * q.TT));
+  P = std::min<int64_t>(P, round_up(q.VT, 8));
+  q.P = std::max<int64_t>(8, P);
+  // backward: vocabulary block so that the G slab stays near the budget
+  int64_t vb = kGSlabBudget / (q.rows_pad * q.es);
+  vb = std::max<int64_t>(kTile, vb / kTile * kTile);
+  vb = std::min<int64_t>(vb, round_up(V, kTile));
+  q.Vb = vb;
+  // 32-bit offsets inside the kernels
+  if (q.rows_pad * q.Vb * q.es > kMaxI32 || q.rows_pad * H * 4 > kMaxI32 ||
+      (int64_t)kTile * H * q.es * 2 > kMaxI32)
+    return FLCE_ERR_SHAPE;
+
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) {
+    const int64_t o = off;
+    off = round_up(off + bytes, kAlign);
+    return o;
+  };
+  q.o_ctr = take(sizeof(Counters));
+  q.o_idx = take(4 * q.rows_pad);
+  q.o_tgt = take(4 * q.rows_pad);
+  q.o_rowpos = take(4 * q.rows_pad);
+  q.o_xc = take(q.rows_pad * H * q.es);
+  const int64_t common = off;
+  q.o_part = take(8 * q.P * q.rows_pad);
+  q.o_zt = take(4 * q.rows_pad);
+  q.o_bsum = take(4 * cdiv(q.rows_pad, 256));
+  const int64_t fwd_end = off;
+  off = common;
+  q.o_lse2 = take(4 * q.rows_pad);
+  q.o_g = take(q.rows_pad * q.Vb * q.es);
+  q.o_dx32 = take(4 * q.rows_pad * H);
+  const int64_t bwd_end = off;
+  q.total = std::max(fwd_end, bwd_end);
+  *p = q;
+  return FLCE_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
+}
+
+template <class K>
+hipError_t allow_big_lds(K kernel) {
+  return hipFuncSetAttribute((const void*)kernel,
+                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+}
+
+// Launch bookkeeping: the first failing launch is remembered.
+struct Launch {
+  hipStream_t s;
+  hipError_t err = hipSuccess;
+  void check() {
+    if (err == hipSuccess) err = hipGetLastError();
+  }
+};
+
+int64_t pad8(int64_t n) { return round_up(n, 8); }
+
+// Measurement hook (flce_set_timing): events recorded around the launches of
+// one named kernel.
+struct TimingHook {
+  char name[64] = {0};
+  hipEvent_t* events = nullptr;
+  int capacity = 0;
+  int* count = nullptr;
+};
+TimingHook g_timing;
+
+struct Timed {
+  bool on;
+  hipStream_t s;
+  Timed(const char* kernel, hipStream_t stream) : s(stream) {
+    on = g_timing.events != nullptr && g_timing.count != nullptr &&
+         *g_timing.count < g_timing.capacity && strcmp(kernel, g_timing.name) == 0;
+    if (on) hipEventRecord(g_timing.events[2 * *g_timing.count], s);
+  }
+  ~Timed() {
+    if (on) {
+      hipEventRecord(g_timing.events[2 * *g_timing.count + 1], s);
+      ++*g_timing.count;
+    }
+  }
+};
+
+template <class E>
+int forward_impl(const Plan& pl, const void* X, const void* W, const int64_t* labels,
+                 int64_t B, int64_t T, int64_t ignore_index, int reduction, int shift,
+                 float* loss, float* lse, int64_t* n_valid, int32_t* status,
+                 char* ws, hipStream_t stream) {
+  Launch L{stream};
+  Counters* ctr = (Counters*)(ws + pl.o_ctr);
+  int* idx = (int*)(ws + pl.o_idx);
+  int* tgt = (int*)(ws + pl.o_tgt);
+  int* rowpos = (int*)(ws + pl.o_rowpos);
+  char* xc = ws + pl.o_xc;
+  float2* part = (float2*)(ws + pl.o_part);
+  float* zt = (float*)(ws + pl.o_zt);
+  float* bsum = (float*)(ws + pl.o_bsum);
+  const int rows_pad = (int)pl.rows_pad;
+  const int row_bytes = (int)(pl.H * E::kBytes);
+
+  hipLaunchKernelGGL(k_prep, dim3(1), dim3(1024), 0, stream, labels, (int)B, (int)T,
+                     ignore_index, pl.V, shift, reduction, (const float*)nullptr, idx,
+                     tgt, rowpos, ctr, status);
+  L.check();
+  hipLaunchKernelGGL(k_gather, dim3((unsigned)cdiv(rows_pad, 4)), dim3(256), 0, stream,
+                     (const char*)X, row_bytes, (const int*)idx, (const Counters*)ctr,
+                     xc, rows_pad, (const float*)nullptr, (float*)nullptr,
+                     (float*)nullptr, 0);
+  L.check();
+  hipLaunchKernelGGL(k_target<E>, dim3((unsigned)cdiv(rows_pad, 4)), dim3(256), 0, stream,
+                     (const char*)xc, (const char*)W, (int)pl.H, (const int*)tgt,
+                     (const Counters*)ctr, zt);
+  L.check();
+  FwdArgs fa;
+  fa.W = (const char*)W;
+  fa.Xc = xc;
+  fa.H = (int)pl.H;
+  fa.V = (int)pl.V;
+  fa.rows_pad = rows_pad;
+  fa.P = (int)pl.P;
+  fa.TT = (int)pl.TT;
+  fa.VT = (int)pl.VT;
+  fa.nblocks = (int)pad8(pl.P * pl.TT);
+  fa.ctr = ctr;
+  fa.part = part;
+  if (L.err == hipSuccess) L.err = allow_big_lds(k_fwd_lse<E>);
+  {
+    Timed t("k_fwd_lse", stream);
+    hipLaunchKernelGGL(k_fwd_lse<E>, dim3(fa.nblocks), dim3(kThreads), kLdsBytes, stream, fa);
+    L.check();
+  }
+  const int nb = (int)cdiv(pl.N, 256);
+  hipLaunchKernelGGL(k_merge, dim3(nb), dim3(256), 0, stream, (const float2*)part,
+                     (int)pl.P, rows_pad, (const int*)rowpos, (const float*)zt,
+                     (int)pl.N, lse, bsum);
+  L.check();
+  hipLaunchKernelGGL(k_loss, dim3(1), dim3(256), 0, stream, (const float*)bsum, nb,
+                     (const Counters*)ctr, reduction, loss, n_valid);
+  L.check();
+  return L.err == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
+}
+
+template <class E>
+int backward_impl(const Plan& pl, const void* X, const void* W, const int64_t* labels,
+                  int64_t B, int64_t T, int64_t ignore_index, int reduction, int shift,
+                  const float* lse, const float* grad_scale, void* dX, void* dW,
+                  int grad_f32, int32_t* status, char* ws, hipStream_t stream) {
+  Launch L{stream};
+  Counters* ctr = (Counters*)(ws + pl.o_ctr);
+  int* idx = (int*)(ws + pl.o_idx);
+  int* tgt = (int*)(ws + pl.o_tgt);
+  int* rowpos = (int*)(ws + pl.o_rowpos);
+  char* xc = ws + pl.o_xc;
+  float* lse2 = (float*)(ws + pl.o_lse2);
+  char* g = ws + pl.o_g;
+  float* dx32 = (float*)(ws + pl.o_dx32);
+  const int rows_pad = (int)pl.rows_pad;
+  const int row_bytes = (int)(pl.H * E::kBytes);
+
+  hipLaunchKernelGGL(k_prep, dim3(1), dim3(1024), 0, stream, labels, (int)B, (int)T,
+                     ignore_index, pl.V, shift, reduction, grad_scale, idx, tgt, rowpos,
+                     ctr, status);
+  L.check();
+  hipLaunchKernelGGL(k_gather, dim3((unsigned)cdiv(rows_pad, 4)), dim3(256), 0, stream,
+                     (const char*)X, row_bytes, (const int*)idx, (const Counters*)ctr,
+                     xc, rows_pad, lse, lse2, dx32, (int)(pl.H * 4));
+  L.check();
+
+  BwdArgs a;
+  a.W = (const char*)W;
+  a.Xc = xc;
+  a.G = g;
+  a.lse2 = lse2;
+  a.tgt = tgt;
+  a.dx32 = dx32;
+  a.dW = (char*)dW;
+  a.ctr = ctr;
+  a.H = (int)pl.H;
+  a.V = (int)pl.V;
+  a.rows_pad = rows_pad;
+  a.Vb = (int)pl.Vb;
+  a.TT = (int)pl.TT;
+  a.HT = (int)cdiv(pl.H, kTile);
+  a.dw_f32 = grad_f32;
+  if (L.err == hipSuccess) L.err = allow_big_lds(k_bwd_g<E>);
+  if (L.err == hipSuccess) L.err = allow_big_lds(k_bwd_dw<E>);
+  if (L.err == hipSuccess) L.err = allow_big_lds(k_bwd_dx<E>);
+  for (int64_t v0 = 0; v0 < pl.V && L.err == hipSuccess; v0 += pl.Vb) {
+    a.v0 = (int)v0;
+    a.vb = (int)std::min<int64_t>(pl.Vb, pl.V - v0);
+    a.VTb = (int)cdiv(a.vb, kTile);
+    // G slab
+    a.nblocks = (int)pad8((int64_t)a.VTb * a.TT);
+    a.splits = 1;
+    {
+      Timed t("k_bwd_g", stream);
+      hipLaunchKernelGGL(k_bwd_g<E>, dim3(a.nblocks), dim3(kThreads), kLdsBytes, stream, a);
+      L.check();
+    }
+    hipLaunchKernelGGL(k_fixup<E>, dim3((unsigned)cdiv(rows_pad, 256)), dim3(256), 0,
+                       stream, a);
+    L.check();
+    // dW rows of the block
+    a.nblocks = (int)pad8((int64_t)a.HT * a.VTb);
+    {
+      Timed t("k_bwd_dw", stream);
+      hipLaunchKernelGGL(k_bwd_dw<E>, dim3(a.nblocks), dim3(kThreads), kLdsBytes, stream, a);
+      L.check();
+    }
+    // dX accumulation, split over the block's vocabulary so the launch fills
+    // the machine (about 2 waves of 256 workgroups at least)
+    const int64_t tiles = (int64_t)a.HT * a.TT;
+    const int64_t ksteps = cdiv(a.vb, E::kKStep);
+    int64_t sp = std::max<int64_t>(1, cdiv(512, tiles));
+    sp = std::min<int64_t>(sp, std::max<int64_t>(1, ksteps / 16));
+    a.splits = (int)sp;
+    a.nblocks = (int)pad8(sp * tiles);
+    {
+      Timed t("k_bwd_dx", stream);
+      hipLaunchKernelGGL(k_bwd_dx<E>, dim3(a.nblocks), dim3(kThreads), kLdsBytes, stream, a);
+      L.check();
+    }
+  }
+  hipLaunchKernelGGL(k_dx_final, dim3((unsigned)cdiv(pl.N, 4)), dim3(256), 0, stream,
+                     (const float*)dx32, (const int*)rowpos, (int)pl.N, (int)pl.H,
+                     (char*)dX, grad_f32);
+  L.check();
+  return L.err == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
+}
+
+}  // namespace
+}  // namespace flce
+
+using namespace flce;
+
+extern "C" {
+
+int flce_workspace_size(int64_t B, int64_t T, int64_t H, int64_t V, int dtype,
+                        size_t* bytes) {
+  if (bytes == nullptr) return FLCE_ERR_NULL;
+  Plan p;
+  const int rc = make_plan(B, T, H, V, dtype, &p);
+  if (rc != FLCE_OK) return rc;
+  *bytes = (size_t)p.total;
+  return FLCE_OK;
+}
+
+int flce_forward(const void* X, const void* W, const int64_t* labels, int64_t B,
+                 int64_t T, int64_t H, int64_t V, int dtype, int64_t ignore_index,
+                 int reduction, int shift, float* loss, float* lse, int64_t* n_valid,
+                 int32_t* status, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+  if (loss == nullptr) return FLCE_ERR_NULL;
+  Plan p;
+  int rc = make_plan(B, T, H, V, dtype, &p);
+  if (rc != FLCE_OK) return rc;
+  if (reduction != FLCE_REDUCTION_MEAN && reduction != FLCE_REDUCTION_SUM)
+    return FLCE_ERR_REDUCTION;
+  hipStream_t s = (hipStream_t)stream;
+  if (p.N == 0) {
+    hipLaunchKernelGGL(k_empty, dim3(1), dim3(1), 0, s, loss, n_valid, status);
+    return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
+  }
+  if (X == nullptr || W == nullptr || labels == nullptr || lse == nullptr)
+    return FLCE_ERR_NULL;
+  if (!aligned16(X) || !aligned16(W) || ((uintptr_t)labels & 7u) ||
+      ((uintptr_t)lse & 3u) || ((uintptr_t)loss & 3u))
+    return FLCE_ERR_ALIGN;
+  if (workspace == nullptr) return FLCE_ERR_WORKSPACE;
+  if ((int64_t)workspace_bytes < p.total || !aligned16(workspace))
+    return FLCE_ERR_WORKSPACE;
+  if (dtype == FLCE_DTYPE_BF16)
+    return forward_impl<BF16>(p, X, W, labels, B, T, ignore_index, reduction, shift,
+                              loss, lse, n_valid, status, (char*)workspace, s);
+  return forward_impl<F32>(p, X, W, labels, B, T, ignore_index, reduction, shift, loss,
+                           lse, n_valid, status, (char*)workspace, s);
+}
+
+int flce_backward(const void* X, const void* W, const int64_t* labels, int64_t B,
+                  int64_t T, int64_t H, int64_t V, int dtype, int64_t ignore_index,
+                  int reduction, int shift, const float* lse, const float* grad_scale,
+                  void* dX, void* dW, int grad_dtype, int32_t* status, void* workspace,
+                  size_t workspace_bytes, void* stream) {
+  Plan p;
+  int rc = make_plan(B, T, H, V, dtype, &p);
+  if (rc != FLCE_OK) return rc;
+  if (reduction != FLCE_REDUCTION_MEAN && reduction != FLCE_REDUCTION_SUM)
+    return FLCE_ERR_REDUCTION;
+  if (grad_dtype != dtype && grad_dtype != FLCE_DTYPE_F32) return FLCE_ERR_DTYPE;
+  if (W == nullptr || dW == nullptr) return FLCE_ERR_NULL;
+  if (p.N > 0 && (X == nullptr || labels == nullptr || lse == nullptr || dX == nullptr))
+    return FLCE_ERR_NULL;
+  const int64_t ges = grad_dtype == FLCE_DTYPE_F32 ? 4 : 2;
+  if (!aligned16(W) || !aligned16(dW) || (p.N > 0 && (!aligned16(X) || !aligned16(dX))) ||
+      ((uintptr_t)labels & 7u) || ((uintptr_t)lse & 3u))
+    return FLCE_ERR_ALIGN;
+  if (overlaps(dW, p.V * p.H * ges, W, p.V * p.H * p.es)) return FLCE_ERR_ALIAS;
+  if (p.N > 0 && overlaps(dX, p.N * p.H * ges, X, p.N * p.H * p.es)) return FLCE_ERR_ALIAS;
+  if (workspace == nullptr) return FLCE_ERR_WORKSPACE;
+  if ((int64_t)workspace_bytes < p.total || !aligned16(workspace))
+    return FLCE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const int gf32 = grad_dtype == FLCE_DTYPE_F32 ? 1 : 0;
+  if (p.N == 0) {
+    // no rows: dW = 0 (dX is empty)
+    const hipError_t e = hipMemsetAsync(dW, 0, (size_t)(p.V * p.H * ges), s);
+    if (status != nullptr && e == hipSuccess) {
+      hipLaunchKernelGGL(k_empty, dim3(1), dim3(1), 0, s, (float*)nullptr,
+                         (int64_t*)nullptr, status);
+    }
+    return e == hipSuccess && hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
+  }
+  if (dtype == FLCE_DTYPE_BF16)
+    return backward_impl<BF16>(p, X, W, labels, B, T, ignore_index, reduction, shift, lse,
+                               grad_scale, dX, dW, gf32, status, (char*)workspace, s);
+  return backward_impl<F32>(p, X, W, labels, B, T, ignore_index, reduction, shift, lse,
+                            grad_scale, dX, dW, gf32, status, (char*)workspace, s);
+}
+
+int flce_set_timing(const char* kernel, void* const* events, int capacity, int* count) {
+  if (kernel == nullptr || events == nullptr || count == nullptr || capacity <= 0) {
+    g_timing = TimingHook();
+    return FLCE_OK;
+  }
+  if (strlen(kernel) >= sizeof(g_timing.name)) return FLCE_ERR_SHAPE;
+  g_timing = TimingHook();
+  strcpy(g_timing.name, kernel);
+  g_timing.events = (hipEvent_t*)events;
+  g_timing.capacity = capacity;
+  g_timing.count = count;
+  return FLCE_OK;
+}
+
+const char* flce_status_string(int code) {
+  switch (code) {
+    case FLCE_OK: return "ok";
+    case FLCE_ERR_NULL: return "a required pointer is NULL";
+    case FLCE_ERR_SHAPE: return "sizes out of the supported range";
+    case FLCE_ERR_ALIGN: return "H must be a multiple of 8 and buffers 16-byte aligned";
+    case FLCE_ERR_DTYPE: return "unknown or unsupported dtype";
+    case FLCE_ERR_REDUCTION: return "unknown reduction";
+    case FLCE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case FLCE_ERR_HIP: return "a HIP launch failed";
+    case FLCE_ERR_LABEL_RANGE: return "a label is neither ignore_index nor in [0, V)";
+    case FLCE_ERR_ALIAS: return "an output buffer overlaps an input buffer";
+    default: return "unknown status code";
+  }
+}
+
+}  // extern "C"

@@ -1,0 +1,630 @@
+// flce_kernels.h -- the kernels of the fused linear cross-entropy engine.
+//
+// Notation: X [N, H] hidden states, W [V, H] output weight, y the per-row
+// targets, n the number of rows with a target ("valid" rows), c the gradient
+// scale (grad_scale / n for the mean, grad_scale for the sum).  All GEMM-shaped
+// kernels compute one or more 256 x 256 tiles with flce_tile.h.
+//
+// Forward  (loss, lse):
+//   k_prep      targets, validity, compaction of the valid rows (idx, tgt)
+//   k_gather    Xc[k] = X[idx[k]] for k < n, zero rows up to a tile multiple
+//   k_target    zt[k] = <Xc[k], W[tgt[k]]>
+//   k_fwd_lse   logits tiles W.Xc^T on MFMA, online max / sum-exp2 per row
+//               over a range of vocabulary tiles -> (m, s) partials
+//   k_merge     lse = merge of the partials, loss_i = lse_i - zt_i, block sums
+//   k_loss      fixed-order sum of the block sums -> loss
+// Backward (dX, dW), per vocabulary block [v0, v0 + vb):
+//   k_bwd_g     logits recomputed on MFMA, G = c * exp(z - lse) stored (bf16 or
+//               fp32) into a bounded [rows x block] slab
+//   k_fixup     G[k, y_k - v0] -= c for targets inside the block
+//   k_bwd_dw    dW[v0 + m, :] = sum_k G[k, m] Xc[k, :]   (complete, stored once)
+//   k_bwd_dx    dX32[k, :] += sum_m G[k, m] W[v0 + m, :] (FP32, split over m)
+// then k_dx_final rounds dX32 once and scatters it to the original rows.
+#pragma once
+
+#include "flce_tile.h"
+
+namespace flce {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct Counters {
+  int n;         // valid rows
+  int status;    // 0 or FLCE_ERR_LABEL_RANGE
+  float c;       // gradient scale (backward)
+  int pad;
+};
+
+constexpr int kStatusLabelRange = 8;
+
+// ---------------------------------------------------------------------------
+// k_prep: one workgroup of 1024 threads walks the rows in order, so the
+// compacted order is the row order (deterministic).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void k_prep(
+    const int64_t* __restrict__ labels, int B, int T, int64_t ignore,
+    int64_t V, int shift, int reduction, const float* __restrict__ grad_scale,
+    int* __restrict__ idx, int* __restrict__ tgt, int* __restrict__ rowpos,
+    Counters* __restrict__ ctr, int32_t* __restrict__ status_out) {
+  __shared__ int wsum[16];
+  __shared__ int base_s;
+  __shared__ int bad_s;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int N = B * T;
+  if (tid == 0) {
+    base_s = 0;
+    bad_s = 0;
+  }
+  __syncthreads();
+  for (int i0 = 0; i0 < N; i0 += 1024) {
+    const int i = i0 + tid;
+    bool valid = false;
+    int64_t y = ignore;
+    if (i < N) {
+      if (shift) {
+        const int t = i % T;
+        y = (t + 1 < T) ? labels[i + 1] : ignore;
+      } else {
+        y = labels[i];
+      }
+      if (y != ignore) {
+        if (y < 0 || y >= V) bad_s = 1;
+        else valid = true;
+      }
+    }
+    const uint64_t m = __ballot(valid);
+    const int pre = __popcll(m & ((1ull << lane) - 1ull));
+    if (lane == 0) wsum[w] = __popcll(m);
+    __syncthreads();
+    int pos = base_s + pre;
+    for (int q = 0; q < w; ++q) pos += wsum[q];
+    if (i < N) {
+      rowpos[i] = valid ? pos : -1;
+      if (valid) {
+        idx[pos] = i;
+        tgt[pos] = (int)y;
+      }
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int tot = 0;
+      for (int q = 0; q < 16; ++q) tot += wsum[q];
+      base_s += tot;
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    const int n = base_s;
+    const int st = bad_s ? kStatusLabelRange : 0;
+    const float gs = grad_scale ? *grad_scale : 1.0f;
+    float c = reduction == 0 ? (n > 0 ? gs / (float)n : 0.0f) : gs;
+    if (st) c = __builtin_nanf("");
+    ctr->n = n;
+    ctr->status = st;
+    ctr->c = c;
+    if (status_out) *status_out = st;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// k_gather: one wave per compacted row k in [0, rows_pad).  Row k < n copies
+// X[idx[k]]; the rest is zero.  In the backward it also stages
+// lse2[k] = lse[idx[k]] * log2(e) and clears the FP32 dX accumulator row.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_gather(
+    const char* __restrict__ X, int row_bytes, const int* __restrict__ idx,
+    const Counters* __restrict__ ctr, char* __restrict__ Xc, int rows_pad,
+    const float* __restrict__ lse, float* __restrict__ lse2,
+    float* __restrict__ dx32, int dx32_row_bytes) {
+  const int k = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (k >= rows_pad) return;
+  const int n = ctr->n;
+  const int chunks = row_bytes >> 4;
+  i32x4* dst = (i32x4*)(Xc + (int64_t)k * row_bytes);
+  if (k < n) {
+    const i32x4* src = (const i32x4*)(X + (int64_t)idx[k] * row_bytes);
+    for (int c = lane; c < chunks; c += 64) dst[c] = src[c];
+  } else {
+    for (int c = lane; c < chunks; c += 64) dst[c] = i32x4{0, 0, 0, 0};
+  }
+  if (lse2 != nullptr && lane == 0) lse2[k] = k < n ? lse[idx[k]] * kLog2e : 0.f;
+  if (dx32 != nullptr) {
+    i32x4* d = (i32x4*)((char*)dx32 + (int64_t)k * dx32_row_bytes);
+    for (int c = lane; c < (dx32_row_bytes >> 4); c += 64) d[c] = i32x4{0, 0, 0, 0};
+  }
+}
+
+// ---------------------------------------------------------------------------
+// k_target: zt[k] = <Xc[k], W[tgt[k]]> in fp32, one wave per valid row.
+// ---------------------------------------------------------------------------
+template <class E>
+__global__ __launch_bounds__(256) void k_target(
+    const char* __restrict__ Xc, const char* __restrict__ W, int H,
+    const int* __restrict__ tgt, const Counters* __restrict__ ctr,
+    float* __restrict__ zt) {
+  const int k = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (k >= ctr->n) return;
+  const int row_bytes = H * E::kBytes;
+  const i32x4* x = (const i32x4*)(Xc + (int64_t)k * row_bytes);
+  const i32x4* w = (const i32x4*)(W + (int64_t)tgt[k] * row_bytes);
+  float acc = 0.f;
+  for (int c = lane; c < (row_bytes >> 4); c += 64) {
+    const i32x4 a = x[c], b = w[c];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if constexpr (E::kBytes == 2) {
+        const uint32_t ua = (uint32_t)a[q], ub = (uint32_t)b[q];
+        acc = fmaf(bf2f(ua & 0xFFFFu), bf2f(ub & 0xFFFFu), acc);
+        acc = fmaf(bf2f(ua >> 16), bf2f(ub >> 16), acc);
+      } else {
+        acc = fmaf(__builtin_bit_cast(float, a[q]), __builtin_bit_cast(float, b[q]), acc);
+      }
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  if (lane == 0) zt[k] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// Online (max, sum of 2^(z - max)) pairs, kept in log2 units.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  const float M = fmaxf(m, m2);
+  if (M == -INFINITY) return;            // both empty
+  s = s * __builtin_amdgcn_exp2f(m - M) + s2 * __builtin_amdgcn_exp2f(m2 - M);
+  m = M;
+}
+
+// Online update of the per-lane (max, sum) of 4 token columns with one tile
+// of logits.  kMasked: tile rows r with (32i + 8(r/4) + r%4) >= lim are past
+// the vocabulary end and are skipped (lim already holds the lane's offset).
+template <bool kMasked>
+__device__ __forceinline__ void lse_update(const f32x16 (&acc)[4][4], float (&m)[4],
+                                           float (&s)[4], int lim) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (!kMasked || 32 * i + 8 * (r >> 2) + (r & 3) < lim)
+          tmax = fmaxf(tmax, acc[i][j][r]);
+    if (tmax != -INFINITY) {
+      const float M = fmaxf(m[j], tmax * kLog2e);
+      float sum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float e = __builtin_amdgcn_exp2f(fmaf(acc[i][j][r], kLog2e, -M));
+          if (!kMasked || 32 * i + 8 * (r >> 2) + (r & 3) < lim) sum += e;
+        }
+      s[j] = s[j] * __builtin_amdgcn_exp2f(m[j] - M) + sum;
+      m[j] = M;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// k_fwd_lse: work item (p, tau) = vocabulary range p x token tile tau.  The
+// workgroup walks the range's 256-wide vocabulary tiles; A = W rows (vocab),
+// B = Xc rows (tokens), so each lane's accumulators hold 64 vocabulary entries
+// of 4 tokens and the per-token reduction is mostly in registers.
+// ---------------------------------------------------------------------------
+struct FwdArgs {
+  const char* W;
+  const char* Xc;
+  int H, V, rows_pad;
+  int P, TT, VT, nblocks;
+  const Counters* ctr;
+  float2* part;      // [P][rows_pad] (m in log2 units, s)
+};
+
+template <class E>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_fwd_lse(FwdArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem_[];
+  lds_t* smem = (lds_t*)smem_;
+  const int item = xcd_item(blockIdx.x, a.nblocks);
+  if (item >= a.P * a.TT) return;
+  const int p = item / a.TT, tau = item - p * a.TT;
+  const int n = a.ctr->n;
+  if (tau * kTile >= n) return;
+  const int vt0 = (int)((int64_t)p * a.VT / a.P), vt1 = (int)((int64_t)(p + 1) * a.VT / a.P);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const FragOffsets fo(wm, wn);
+  const int ldb = a.H * E::kBytes;
+  const int steps = (ldb + kRowBytes - 1) / kRowBytes;
+
+  Opnd B;
+  B.base = a.Xc + (int64_t)tau * kTile * ldb;
+  B.bytes = (int64_t)(a.rows_pad - tau * kTile) * ldb;
+  B.ldb = ldb;
+  B.kbytes = ldb;
+
+  float m[4], s[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    m[j] = -INFINITY;
+    s[j] = 0.f;
+  }
+  f32x16 acc[4][4];
+  for (int vt = vt0; vt < vt1; ++vt) {
+    Opnd A;
+    A.base = a.W + (int64_t)vt * kTile * ldb;
+    A.bytes = (int64_t)(a.V - vt * kTile) * ldb;
+    A.ldb = ldb;
+    A.kbytes = ldb;
+    zero_acc(acc);
+    gemm_tile<E, LoadDirect, LoadDirect>(A, B, steps, ldb % kRowBytes != 0, smem, fo, acc);
+    // rows at or past V (last tile only) take no part in the reduction
+    const int vlim = a.V - vt * kTile;
+    if (vlim >= kTile) lse_update<false>(acc, m, s, 0);
+    else lse_update<true>(acc, m, s, vlim - wm * 128 - 4 * (lane >> 5));
+  }
+  // combine the two lane halves and the two waves that share tokens
+  typedef __attribute__((address_space(3))) float lf;
+  lf* st = (lf*)smem;  // [wm][h][256 tokens][m, s]
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = ((wm * 2 + (lane >> 5)) * kTile + acc_col(wn, j, lane)) * 2;
+    st[e] = m[j];
+    st[e + 1] = s[j];
+  }
+  __syncthreads();
+  const int t = threadIdx.x;
+  float M = -INFINITY, S = 0.f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) lse_merge(M, S, st[(q * kTile + t) * 2], st[(q * kTile + t) * 2 + 1]);
+  a.part[(int64_t)p * a.rows_pad + tau * kTile + t] = make_float2(M, S);
+}
+
+// ---------------------------------------------------------------------------
+// k_merge: one thread per original row.  Valid rows merge the P partials into
+// lse and form loss_i = lse_i - zt_i; ignored rows get lse = 0.  Each block
+// writes the fixed-order sum of its 256 row losses.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_merge(
+    const float2* __restrict__ part, int P, int rows_pad,
+    const int* __restrict__ rowpos, const float* __restrict__ zt, int N,
+    float* __restrict__ lse_out, float* __restrict__ blocksum) {
+  __shared__ float red[256];
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  float li = 0.f;
+  if (i < N) {
+    const int k = rowpos[i];
+    float lse = 0.f;
+    if (k >= 0) {
+      float M = -INFINITY, S = 0.f;
+      for (int p = 0; p < P; ++p) {
+        const float2 v = part[(int64_t)p * rows_pad + k];
+        const float Mn = fmaxf(M, v.x);
+        if (Mn == -INFINITY) continue;
+        S = S * exp2f(M - Mn) + v.y * exp2f(v.x - Mn);
+        M = Mn;
+      }
+      lse = (M + log2f(S)) * kLn2;
+      li = lse - zt[k];
+    }
+    lse_out[i] = lse;
+  }
+  red[threadIdx.x] = li;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) blocksum[blockIdx.x] = red[0];
+}
+
+// k_loss: fixed-order sum of the block sums -> loss (mean or sum).
+__global__ __launch_bounds__(256) void k_loss(
+    const float* __restrict__ blocksum, int nb, const Counters* __restrict__ ctr,
+    int reduction, float* __restrict__ loss, int64_t* __restrict__ n_valid) {
+  __shared__ float red[256];
+  float acc = 0.f;
+  for (int b = threadIdx.x; b < nb; b += 256) acc += blocksum[b];
+  red[threadIdx.x] = acc;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    const int n = ctr->n;
+    float L = red[0];
+    if (reduction == 0) L = n > 0 ? L / (float)n : 0.f;
+    if (ctr->status != 0) L = __builtin_nanf("");
+    *loss = L;
+    if (n_valid) *n_valid = n;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Backward GEMM kernels
+// ---------------------------------------------------------------------------
+struct BwdArgs {
+  const char* W;       // [V, H]
+  const char* Xc;      // [rows_pad, H] compacted valid rows
+  char* G;             // [rows_pad, Vb] softmax-gradient slab
+  const float* lse2;   // [rows_pad] lse * log2(e)
+  const int* tgt;      // [n]
+  float* dx32;         // [rows_pad, H]
+  char* dW;            // [V, H] output (grad dtype)
+  const Counters* ctr;
+  int H, V, rows_pad, Vb;
+  int v0, vb;          // block start and width
+  int TT, HT, VTb, nblocks;
+  int splits;          // dX: K-splits of the block
+  int dw_f32;          // dW written as fp32 (else bf16)
+};
+
+// G = c * 2^(z*log2e - lse2) for one tile, stored as G[token][vocab].
+// kMasked: tile rows with (32i + 8g + q) >= vlim_lane lie past the vocabulary
+// end and token columns >= nlim are padding; both become 0.
+template <class E, bool kMasked>
+__device__ __forceinline__ void g_store(const BwdArgs& a, const f32x16 (&acc)[4][4],
+                                        float c, int vt, int tau, int wm, int wn,
+                                        int lane, int vlim_lane, int nlim) {
+  const rsrc_t gr = make_rsrc(a.G, (int64_t)a.rows_pad * a.Vb * E::kBytes);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int tcol = acc_col(wn, j, lane);
+    const int tok = tau * kTile + tcol;
+    const float l2 = a.lse2[tok];
+    const bool tok_ok = !kMasked || tcol < nlim;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int row0 = acc_row(wm, i, 4 * g, lane);   // 4 consecutive rows
+        float v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          v[q] = c * __builtin_amdgcn_exp2f(fmaf(acc[i][j][4 * g + q], kLog2e, -l2));
+          if (kMasked && !(tok_ok && 32 * i + 8 * g + q < vlim_lane)) v[q] = 0.f;
+        }
+        const int off = (tok * a.Vb + vt * kTile + row0) * E::kBytes;
+        if constexpr (E::kBytes == 2) {
+          i32x2 pk;
+          pk[0] = (int)(f2bf(v[0]) | (f2bf(v[1]) << 16));
+          pk[1] = (int)(f2bf(v[2]) | (f2bf(v[3]) << 16));
+          __builtin_amdgcn_raw_buffer_store_b64(pk, gr, off, 0, 0);
+        } else {
+          i32x4 pk = {__builtin_bit_cast(int, v[0]), __builtin_bit_cast(int, v[1]),
+                      __builtin_bit_cast(int, v[2]), __builtin_bit_cast(int, v[3])};
+          __builtin_amdgcn_raw_buffer_store_b128(pk, gr, off, 0, 0);
+        }
+      }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// G = c * 2^(z*log2e - lse2) on the tile (vocab rows x token columns); zero
+// outside the vocabulary and for padding rows.  Stored as G[token][vocab].
+template <class E>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_bwd_g(BwdArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem_[];
+  lds_t* smem = (lds_t*)smem_;
+  const int item = xcd_item(blockIdx.x, a.nblocks);
+  if (item >= a.VTb * a.TT) return;
+  const int vt = item / a.TT, tau = item - vt * a.TT;
+  const int n = a.ctr->n;
+  if (tau * kTile >= n) return;
+  const float c = a.ctr->c;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const FragOffsets fo(wm, wn);
+  const int ldb = a.H * E::kBytes;
+  const int steps = (ldb + kRowBytes - 1) / kRowBytes;
+  const int vbase = a.v0 + vt * kTile;
+
+  Opnd A, B;
+  A.base = a.W + (int64_t)vbase * ldb;
+  A.bytes = (int64_t)(a.V - vbase) * ldb;
+  A.ldb = ldb;
+  A.kbytes = ldb;
+  B.base = a.Xc + (int64_t)tau * kTile * ldb;
+  B.bytes = (int64_t)(a.rows_pad - tau * kTile) * ldb;
+  B.ldb = ldb;
+  B.kbytes = ldb;
+  f32x16 acc[4][4];
+  zero_acc(acc);
+  gemm_tile<E, LoadDirect, LoadDirect>(A, B, steps, ldb % kRowBytes != 0, smem, fo, acc);
+
+  const int vlim = a.V - vbase;
+  if (vlim >= kTile && (tau + 1) * kTile <= n)
+    g_store<E, false>(a, acc, c, vt, tau, wm, wn, lane, 0, 0);
+  else
+    g_store<E, true>(a, acc, c, vt, tau, wm, wn, lane, vlim - wm * 128 - 4 * (lane >> 5),
+                     n - tau * kTile);
+}
+
+// G[k, y_k - v0] -= c for the valid rows whose target lies in the block.
+template <class E>
+__global__ __launch_bounds__(256) void k_fixup(BwdArgs a) {
+  const int k = blockIdx.x * 256 + threadIdx.x;
+  if (k >= a.ctr->n) return;
+  const int y = a.tgt[k] - a.v0;
+  if (y < 0 || y >= a.vb) return;
+  const float c = a.ctr->c;
+  const int64_t off = (int64_t)k * a.Vb + y;
+  if constexpr (E::kBytes == 2) {
+    uint16_t* g = (uint16_t*)a.G + off;
+    *g = (uint16_t)f2bf(bf2f(*g) - c);
+  } else {
+    float* g = (float*)a.G + off;
+    *g = *g - c;
+  }
+}
+
+// dW rows of one tile in the output dtype.  kMasked: rows with
+// (32i + 8(r/4) + r%4) >= mlim_lane lie past the block, columns >= hlim past H.
+template <bool kMasked>
+__device__ __forceinline__ void dw_store(const BwdArgs& a, const f32x16 (&acc)[4][4],
+                                         int vt, int ht, int wm, int wn, int lane,
+                                         int mlim_lane, int hlim) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int hc = acc_col(wn, j, lane);
+    if (kMasked && hc >= hlim) continue;
+    const int h = ht * kTile + hc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        if (kMasked && 32 * i + 8 * (r >> 2) + (r & 3) >= mlim_lane) continue;
+        const int m = vt * kTile + acc_row(wm, i, r, lane);
+        const int64_t e = (int64_t)(a.v0 + m) * a.H + h;
+        if (a.dw_f32) ((float*)a.dW)[e] = acc[i][j][r];
+        else ((uint16_t*)a.dW)[e] = (uint16_t)f2bf(acc[i][j][r]);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// dW[v0 + m, h] = sum_k G[k, m] Xc[k, h]: A = G (K = rows outer), B = Xc
+// (K = rows outer); K runs over the valid rows rounded up to one step.
+template <class E>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_bwd_dw(BwdArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem_[];
+  lds_t* smem = (lds_t*)smem_;
+  const int item = xcd_item(blockIdx.x, a.nblocks);
+  if (item >= a.HT * a.VTb) return;
+  const int ht = item / a.VTb, vt = item - ht * a.VTb;
+  const int n = a.ctr->n;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const FragOffsets fo(wm, wn);
+  const int es = E::kBytes;
+  const int steps = (n + E::kKStep - 1) / E::kKStep;
+
+  Opnd A, B;
+  A.base = a.G + (int64_t)vt * kTile * es;
+  A.bytes = (int64_t)a.rows_pad * a.Vb * es - (int64_t)vt * kTile * es;
+  A.ldb = a.Vb * es;
+  A.kbytes = 0;
+  B.base = a.Xc + (int64_t)ht * kTile * es;
+  B.bytes = (int64_t)a.rows_pad * a.H * es - (int64_t)ht * kTile * es;
+  B.ldb = a.H * es;
+  B.kbytes = 0;
+  f32x16 acc[4][4];
+  zero_acc(acc);
+  using LT = typename TransLoader<E>::type;
+  gemm_tile<E, LT, LT>(A, B, steps, false, smem, fo, acc);
+
+  const int mlim = a.vb - vt * kTile, hlim = a.H - ht * kTile;
+  if (mlim >= kTile && hlim >= kTile)
+    dw_store<false>(a, acc, vt, ht, wm, wn, lane, 0, 0);
+  else
+    dw_store<true>(a, acc, vt, ht, wm, wn, lane, mlim - wm * 128 - 4 * (lane >> 5),
+                   hlim);
+}
+
+template <bool kMasked>
+__device__ __forceinline__ void dx_add(const BwdArgs& a, const f32x16 (&acc)[4][4],
+                                       int tau, int ht, int wm, int wn, int lane,
+                                       int hlim) {
+  const rsrc_t xr = make_rsrc(a.dx32, (int64_t)a.rows_pad * a.H * 4);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int hc = acc_col(wn, j, lane);
+    if (kMasked && hc >= hlim) continue;
+    const int h = ht * kTile + hc;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int k = tau * kTile + acc_row(wm, i, r, lane);
+        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[i][j][r], xr,
+                                                        (k * a.H + h) * 4, 0, 0);
+      }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// dX32[k, h] += sum_m G[k, m] W[v0 + m, h] over one K-split of the block.
+template <class E>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_bwd_dx(BwdArgs a) {
+  extern __shared__ __attribute__((aligned(16))) char smem_[];
+  lds_t* smem = (lds_t*)smem_;
+  const int item = xcd_item(blockIdx.x, a.nblocks);
+  if (item >= a.splits * a.HT * a.TT) return;
+  const int sp = item / (a.HT * a.TT);
+  const int rem = item - sp * a.HT * a.TT;
+  const int ht = rem / a.TT, tau = rem - ht * a.TT;
+  const int n = a.ctr->n;
+  if (tau * kTile >= n) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const FragOffsets fo(wm, wn);
+  const int es = E::kBytes;
+  // the block's K range [0, vb_pad) split into `splits` whole steps
+  const int ksteps_total = (a.vb + E::kKStep - 1) / E::kKStep;
+  const int s0 = (int)((int64_t)sp * ksteps_total / a.splits);
+  const int s1 = (int)((int64_t)(sp + 1) * ksteps_total / a.splits);
+  const int k0 = s0 * E::kKStep;
+
+  Opnd A, B;
+  A.base = a.G + ((int64_t)tau * kTile * a.Vb + k0) * es;
+  A.bytes = (int64_t)a.rows_pad * a.Vb * es - ((int64_t)tau * kTile * a.Vb + k0) * es;
+  A.ldb = a.Vb * es;
+  A.kbytes = (a.Vb - k0) * es;
+  B.base = a.W + ((int64_t)(a.v0 + k0) * a.H + (int64_t)ht * kTile) * es;
+  B.bytes = (int64_t)a.V * a.H * es - ((int64_t)(a.v0 + k0) * a.H + (int64_t)ht * kTile) * es;
+  B.ldb = a.H * es;
+  B.kbytes = 0;
+  f32x16 acc[4][4];
+  zero_acc(acc);
+  gemm_tile<E, LoadDirect, typename TransLoader<E>::type>(A, B, s1 - s0, false, smem, fo,
+                                                          acc);
+
+  // rows >= n hold zeros (G is 0 there) and stay inside the accumulator;
+  // columns past H would land in the next row and are skipped
+  const int hlim = a.H - ht * kTile;
+  if (hlim >= kTile) dx_add<false>(a, acc, tau, ht, wm, wn, lane, 0);
+  else dx_add<true>(a, acc, tau, ht, wm, wn, lane, hlim);
+}
+
+// dX[i] = round(dX32[rowpos[i]]) for valid rows, 0 for the others.
+__global__ __launch_bounds__(256) void k_dx_final(
+    const float* __restrict__ dx32, const int* __restrict__ rowpos, int N, int H,
+    char* __restrict__ dX, int out_f32) {
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (i >= N) return;
+  const int k = rowpos[i];
+  const int groups = H >> 2;  // 4 values per lane step
+  for (int g = lane; g < groups; g += 64) {
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    if (k >= 0) v = *(const f32x4*)(dx32 + (int64_t)k * H + 4 * g);
+    if (out_f32) {
+      *(f32x4*)((float*)dX + (int64_t)i * H + 4 * g) = v;
+    } else {
+      i32x2 pk;
+      pk[0] = (int)(f2bf(v[0]) | (f2bf(v[1]) << 16));
+      pk[1] = (int)(f2bf(v[2]) | (f2bf(v[3]) << 16));
+      *(i32x2*)((uint16_t*)dX + (int64_t)i * H + 4 * g) = pk;
+    }
+  }
+}
+
+// n == 0 rows (N == 0): loss = 0, n_valid = 0.
+__global__ void k_empty(float* loss, int64_t* n_valid, int32_t* status) {
+  *loss = 0.f;
+  if (n_valid) *n_valid = 0;
+  if (status) *status = 0;
+}
+
+}  // namespace flce

@@ -1,0 +1,64 @@
+"""Shared helpers of the GPU tests: run the HIP path through the binding on a
+synthetic workload and compare with the float64 oracle."""
+import numpy as np
+import torch
+
+import lm_head_linear_flce_amd as F
+import oracle
+
+DEV = "cuda:0"
+
+# the tolerances of the build's contract, per input dtype
+TOL = {
+    "f32": dict(loss_rel=1e-5, cos=0.999999, maxabs=None),
+    "bf16": dict(loss_rel=2e-3, cos=0.9999, maxabs=1e-2),
+}
+LSE_ABS = 1e-4     # per valid row, both dtypes
+
+
+def to_device(w):
+    dt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    X = torch.from_numpy(w.X).to(DEV).to(dt).reshape(w.B, w.T, w.H)
+    W = torch.from_numpy(w.W).to(DEV).to(dt)
+    lab = torch.from_numpy(np.ascontiguousarray(w.labels)).to(DEV)
+    return X, W, lab
+
+
+def run(w, grad_dtype=None, grad_scale=None, X=None, W=None, lab=None):
+    if X is None:
+        X, W, lab = to_device(w)
+    loss, lse, n_valid, status = F.forward(X, W, lab, w.ignore_index, w.shift, w.reduction)
+    gs = None if grad_scale is None else torch.tensor(grad_scale, dtype=torch.float32,
+                                                        device=DEV)
+    dX, dW, bstatus = F.backward(X, W, lab, lse, grad_scale=gs,
+                                 ignore_index=w.ignore_index, shift=w.shift,
+                                 reduction=w.reduction, grad_dtype=grad_dtype)
+    torch.cuda.synchronize()
+    return dict(loss=float(loss), lse=lse.double().cpu().numpy(),
+                n_valid=int(n_valid), status=int(status), bstatus=int(bstatus),
+                dX=dX.reshape(w.N, w.H).double().cpu().numpy(),
+                dW=dW.double().cpu().numpy())
+
+
+def check(w, got, ref, dx_rows=None, dw_rows=None, what=""):
+    """Contract tolerances plus the per-row lse diagnostic."""
+    tol = TOL[w.dtype]
+    assert got["status"] == 0 and got["bstatus"] == 0, what
+    assert got["n_valid"] == ref["n_valid"], what
+    rl = abs(got["loss"] - ref["loss"]) / max(abs(ref["loss"]), 1e-30)
+    assert rl <= tol["loss_rel"], f"{what} loss {got['loss']} vs {ref['loss']} rel {rl}"
+    _, valid = oracle.targets(w.labels, w.shift, w.ignore_index)
+    lerr = np.abs(got["lse"][valid] - ref["lse"][valid]).max() if valid.any() else 0.0
+    assert lerr <= LSE_ABS, f"{what} lse max abs err {lerr}"
+    assert np.all(got["lse"][~valid] == 0.0), what
+    gx = got["dX"] if dx_rows is None else got["dX"][dx_rows]
+    gw = got["dW"] if dw_rows is None else got["dW"][dw_rows]
+    out = {}
+    for name, g, r in (("dX", gx, ref["dX"]), ("dW", gw, ref["dW"])):
+        cos = oracle.cosine(g, r)
+        assert cos >= tol["cos"], f"{what} {name} cosine {cos}"
+        if tol["maxabs"] is not None:
+            m = np.abs(g - r).max()
+            assert m <= tol["maxabs"] * np.abs(r).max(), f"{what} {name} max abs {m}"
+        out[name] = cos
+    return out

@@ -1,0 +1,127 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every function include/flce.h declares, sizes its workspace linearly in N (never
+with N*V), and rejects bad arguments before launching anything."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import lm_head_linear_flce_amd as F
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "flce.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(flce_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_abi():
+    assert declared_functions() == sorted(F.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(F.library_path())
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_header_constants_match_binding():
+    text = open(HEADER).read()
+    for name, value in re.findall(r"#define (FLCE_[A-Z0-9_]+) (\d+)", text):
+        assert getattr(F, name) == int(value), name
+
+
+def test_status_strings():
+    for code in range(0, 10):
+        s = F.flce_status_string(code)
+        assert s and s != "unknown status code"
+    assert F.flce_status_string(1234) == "unknown status code"
+
+
+@pytest.mark.parametrize("B,T,H,V", [(1, 8192, 3584, 152064), (2, 8192, 4096, 151936),
+                                     (1, 32768, 2048, 152064), (1, 4099, 1024, 262147)])
+def test_workspace_is_far_below_the_logits(B, T, H, V):
+    ws = F.flce_workspace_size(B, T, H, V, F.FLCE_DTYPE_BF16)
+    logits = B * T * V * 2
+    assert 0 < ws < logits / 2
+    # the vocabulary only enters through a bounded block: quadrupling V adds
+    # at most the forward's per-range partials
+    ws4 = F.flce_workspace_size(B, T, H, 4 * V, F.FLCE_DTYPE_BF16)
+    assert ws4 <= ws + 64 * B * T * 8 + (1 << 20)
+
+
+def test_workspace_grows_linearly_in_rows():
+    w1 = F.flce_workspace_size(1, 4096, 2048, 152064, F.FLCE_DTYPE_BF16)
+    w2 = F.flce_workspace_size(1, 8192, 2048, 152064, F.FLCE_DTYPE_BF16)
+    w4 = F.flce_workspace_size(1, 16384, 2048, 152064, F.FLCE_DTYPE_BF16)
+    assert w2 <= 2.2 * w1 and w4 <= 2.2 * w2
+
+
+@pytest.mark.parametrize("args,code", [
+    ((1, 16, 100, 50, F.FLCE_DTYPE_BF16), F.FLCE_ERR_ALIGN),      # H % 8
+    ((1, 16, 128, 50, 7), F.FLCE_ERR_DTYPE),
+    ((-1, 16, 128, 50, F.FLCE_DTYPE_BF16), F.FLCE_ERR_SHAPE),
+    ((1, 16, 128, 0, F.FLCE_DTYPE_BF16), F.FLCE_ERR_SHAPE),
+    ((1, 16, 0, 50, F.FLCE_DTYPE_BF16), F.FLCE_ERR_SHAPE),
+])
+def test_workspace_size_rejects(args, code):
+    with pytest.raises(F.FlceError) as e:
+        F.flce_workspace_size(*args)
+    assert e.value.code == code
+
+
+def test_workspace_size_null_out_pointer():
+    lib = ctypes.CDLL(F.library_path())
+    lib.flce_workspace_size.argtypes = [ctypes.c_int64] * 4 + [ctypes.c_int, ctypes.c_void_p]
+    assert lib.flce_workspace_size(1, 8, 8, 8, 1, None) == F.FLCE_ERR_NULL
+
+
+# Fake, aligned, never dereferenced device addresses: every call below must be
+# rejected by the host checks, which run before any HIP call.
+P = 1 << 20
+
+
+def fwd(**kw):
+    a = dict(X=P, W=2 * P, labels=3 * P, B=1, T=16, H=128, V=50, dtype=F.FLCE_DTYPE_BF16,
+             ignore_index=-100, reduction=F.FLCE_REDUCTION_MEAN, shift=0, loss=4 * P,
+             lse=5 * P, n_valid=0, status=0, workspace=6 * P, workspace_bytes=1 << 30,
+             stream=0)
+    a.update(kw)
+    return F.flce_forward(*a.values())
+
+
+def bwd(**kw):
+    a = dict(X=P, W=2 * P, labels=3 * P, B=1, T=16, H=128, V=50, dtype=F.FLCE_DTYPE_BF16,
+             ignore_index=-100, reduction=F.FLCE_REDUCTION_MEAN, shift=0, lse=5 * P,
+             grad_scale=0, dX=7 * P, dW=8 * P, grad_dtype=F.FLCE_DTYPE_BF16, status=0,
+             workspace=6 * P, workspace_bytes=1 << 30, stream=0)
+    a.update(kw)
+    return F.flce_backward(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(X=0), F.FLCE_ERR_NULL), (dict(W=0), F.FLCE_ERR_NULL),
+    (dict(labels=0), F.FLCE_ERR_NULL), (dict(loss=0), F.FLCE_ERR_NULL),
+    (dict(lse=0), F.FLCE_ERR_NULL), (dict(H=100), F.FLCE_ERR_ALIGN),
+    (dict(X=P + 8), F.FLCE_ERR_ALIGN), (dict(dtype=3), F.FLCE_ERR_DTYPE),
+    (dict(reduction=2), F.FLCE_ERR_REDUCTION), (dict(workspace=0), F.FLCE_ERR_WORKSPACE),
+    (dict(workspace_bytes=64), F.FLCE_ERR_WORKSPACE), (dict(V=-5), F.FLCE_ERR_SHAPE),
+])
+def test_forward_host_checks(kw, code):
+    assert fwd(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dX=0), F.FLCE_ERR_NULL), (dict(dW=0), F.FLCE_ERR_NULL),
+    (dict(lse=0), F.FLCE_ERR_NULL), (dict(grad_dtype=5), F.FLCE_ERR_DTYPE),
+    (dict(dtype=F.FLCE_DTYPE_F32, grad_dtype=F.FLCE_DTYPE_BF16), F.FLCE_ERR_DTYPE),
+    (dict(dX=P), F.FLCE_ERR_ALIAS), (dict(dW=2 * P + 64), F.FLCE_ERR_ALIAS),
+    (dict(workspace_bytes=10), F.FLCE_ERR_WORKSPACE), (dict(reduction=9), F.FLCE_ERR_REDUCTION),
+    (dict(dW=8 * P + 4), F.FLCE_ERR_ALIGN),
+])
+def test_backward_host_checks(kw, code):
+    assert bwd(**kw) == code

@@ -1,0 +1,206 @@
+"""Parity of the HIP path (through the C ABI) with the float64 oracle.
+
+Oracle-sized cases keep each workload's recipe (distributions, masks, shift,
+reduction, dtype) at sizes that span several 256-wide tiles in both N and V and
+end in ragged tails; the full-size workloads are checked on the oracle's stored
+values (tests/golden/full_*.npz: loss, every row's lse, sampled dX and dW rows)
+and on invariants that hold at any size."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import lm_head_linear_flce_amd as F
+import oracle
+import synth
+from gpu_util import DEV, check, run, to_device
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+# (workload recipe, overrides): several tiles in N and V, ragged tails
+SMALL = [
+    ("tiny_f32", {}),
+    ("tiny_f32", dict(B=3, T=211, H=104, V=1000, seed=11)),
+    ("qwen2_7b_head", dict(T=777, H=512, V=3001, seed=21)),
+    ("qwen3_sft_batch", dict(T=613, H=392, V=5003, seed=31)),
+    ("long_context", dict(T=2049, H=256, V=2051, seed=41)),
+    ("ragged_vocab", dict(T=1031, H=128, V=4099, seed=51)),
+    # N large enough that the backward splits the vocabulary into blocks
+    ("qwen2_7b_head", dict(T=8193, H=64, V=40013, seed=61)),
+]
+
+
+def _ids(p):
+    name, ov = p
+    return name + ("" if not ov else "-" + "-".join(f"{k}{v}" for k, v in ov.items()
+                                                    if k != "seed"))
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[_ids(p) for p in SMALL])
+def test_small_parity(case):
+    name, ov = case
+    w = synth.workload(name, **ov)
+    print(f"[parity] {name} {ov} N={w.N} H={w.H} V={w.V}", flush=True)
+    ref = oracle.flce(w.X, w.W, w.labels, ignore_index=w.ignore_index,
+                      reduction=w.reduction, shift=w.shift, mode="rows", chunk=1024)
+    got = run(w)
+    check(w, got, ref, what=name)
+    # ignored rows of dX are exactly zero
+    _, valid = oracle.targets(w.labels, w.shift, w.ignore_index)
+    assert np.all(got["dX"][~valid] == 0.0)
+
+
+@pytest.mark.parametrize("case", SMALL[2:4], ids=[_ids(p) for p in SMALL[2:4]])
+def test_fp32_gradient_outputs(case):
+    """grad_dtype=float32 returns the FP32 accumulators unrounded."""
+    name, ov = case
+    w = synth.workload(name, **ov)
+    ref = oracle.flce(w.X, w.W, w.labels, ignore_index=w.ignore_index,
+                      reduction=w.reduction, shift=w.shift, mode="rows", chunk=1024)
+    got = run(w, grad_dtype=torch.float32)
+    cos = check(w, got, ref, what=name)
+    assert cos["dX"] > 0.99999 and cos["dW"] > 0.99999
+
+
+def test_grad_scale_and_autograd():
+    w = synth.workload("qwen2_7b_head", T=300, H=128, V=700, seed=71)
+    X, W, lab = to_device(w)
+    Xr = X.detach().clone().requires_grad_(True)
+    Wr = W.detach().clone().requires_grad_(True)
+    loss = F.linear_cross_entropy(Xr, Wr, lab, ignore_index=-100, shift=True,
+                                  reduction="mean")
+    (2.5 * loss).backward()
+    ref = oracle.flce(w.X, w.W, w.labels, shift=True, grad_scale=2.5)
+    assert abs(float(loss) - ref["loss"]) <= 2e-3 * abs(ref["loss"])
+    gx = Xr.grad.reshape(w.N, w.H).double().cpu().numpy()
+    gw = Wr.grad.double().cpu().numpy()
+    assert oracle.cosine(gx, ref["dX"]) >= 0.9999
+    assert oracle.cosine(gw, ref["dW"]) >= 0.9999
+    assert np.abs(gx - ref["dX"]).max() <= 1e-2 * np.abs(ref["dX"]).max()
+    assert np.abs(gw - ref["dW"]).max() <= 1e-2 * np.abs(ref["dW"]).max()
+
+
+def test_loss_is_bitwise_deterministic():
+    w = synth.workload("ragged_vocab", T=900, H=256, V=3001, seed=81)
+    X, W, lab = to_device(w)
+    outs = [F.forward(X, W, lab, -100, w.shift, w.reduction) for _ in range(3)]
+    torch.cuda.synchronize()
+    assert len({float(o[0]) for o in outs}) == 1
+    for o in outs[1:]:
+        assert torch.equal(o[1], outs[0][1])
+
+
+def test_ignored_rows_are_never_read():
+    w = synth.workload("qwen3_sft_batch", T=300, H=128, V=1000, seed=91)
+    _, valid = oracle.targets(w.labels, w.shift, w.ignore_index)
+    a = run(w)
+    w2 = synth.workload("qwen3_sft_batch", T=300, H=128, V=1000, seed=91)
+    ign = np.flatnonzero(~valid)
+    noise = np.random.default_rng(0).standard_normal((len(ign), w.H)) * 1e4
+    w2.X[ign] = synth.round_to_bf16(noise.astype(np.float32))
+    w2.X[ign[:3]] = np.nan
+    b = run(w2)
+    assert a["loss"] == b["loss"]
+    assert np.array_equal(a["lse"], b["lse"])
+    assert np.array_equal(a["dW"], b["dW"])
+    assert np.all(b["dX"][~valid] == 0.0)
+    # dX sums FP32 partials with atomics: equal up to the order of additions
+    np.testing.assert_allclose(b["dX"][valid], a["dX"][valid], rtol=1e-2,
+                               atol=1e-6 * np.abs(a["dX"]).max())
+
+
+def test_no_valid_rows():
+    w = synth.workload("long_context", T=500, H=64, V=300, seed=101)
+    w.labels[:] = -100
+    got = run(w)
+    assert got["n_valid"] == 0 and got["loss"] == 0.0
+    assert not got["dX"].any() and not got["dW"].any() and not got["lse"].any()
+
+
+def test_single_token_sequences_with_shift():
+    w = synth.workload("qwen2_7b_head", B=5, T=1, H=64, V=300, seed=111)
+    got = run(w)
+    assert got["n_valid"] == 0 and got["loss"] == 0.0
+
+
+def test_empty_batch():
+    X = torch.zeros((0, 64), dtype=torch.bfloat16, device=DEV)
+    W = torch.randn((300, 64), device=DEV).to(torch.bfloat16)
+    lab = torch.zeros((0, 0), dtype=torch.int64, device=DEV).reshape(1, 0)
+    loss, lse, n, st = F.forward(X, W, lab)
+    torch.cuda.synchronize()
+    assert float(loss) == 0.0 and int(n) == 0 and int(st) == 0
+
+
+def test_label_out_of_range_sets_status_and_nan():
+    w = synth.workload("ragged_vocab", T=300, H=64, V=500, seed=121)
+    w.labels[0, 5] = w.V + 3
+    got = run(w)
+    assert got["status"] == F.FLCE_ERR_LABEL_RANGE
+    assert got["bstatus"] == F.FLCE_ERR_LABEL_RANGE
+    assert np.isnan(got["loss"])
+    assert np.isnan(got["dW"]).any()
+
+
+def test_ignore_index_inside_vocabulary():
+    w = synth.workload("ragged_vocab", T=400, H=64, V=600, seed=131)
+    w.labels[w.labels < 50] = 7
+    w.ignore_index = 7
+    ref = oracle.flce(w.X, w.W, w.labels, ignore_index=7, reduction=w.reduction)
+    got = run(w)
+    check(w, got, ref, what="ignore=7")
+
+
+def test_zero_weight_gives_log_vocab():
+    w = synth.workload("qwen2_7b_head", T=500, H=128, V=1500, seed=141)
+    w.W[:] = 0.0
+    got = run(w)
+    assert abs(got["loss"] - np.log(w.V)) <= 1e-5 * np.log(w.V)
+    _, valid = oracle.targets(w.labels, w.shift)
+    assert np.abs(got["lse"][valid] - np.log(w.V)).max() < 1e-5
+    assert not got["dX"].any()
+
+
+def test_peak_memory_never_holds_logits():
+    w = synth.workload("long_context", T=8192, H=256, V=32768, seed=151)
+    X, W, lab = to_device(w)
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    loss, lse, _, _ = F.forward(X, W, lab, -100, w.shift, w.reduction)
+    dX, dW, _ = F.backward(X, W, lab, lse, shift=w.shift, reduction=w.reduction)
+    torch.cuda.synchronize()
+    peak = torch.cuda.max_memory_allocated() - base
+    ws = F.flce_workspace_size(w.B, w.T, w.H, w.V, F.FLCE_DTYPE_BF16)
+    outs = (w.N * w.H + w.V * w.H) * 2 + w.N * 4 + 4096
+    assert peak <= ws + outs + (2 << 20), (peak, ws, outs)
+    assert peak < w.N * w.V * 2
+
+
+# ---------------------------------------------------------------------------
+# full sizes
+# ---------------------------------------------------------------------------
+FULL = ["tiny_f32", "qwen2_7b_head", "qwen3_sft_batch", "long_context", "ragged_vocab"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_against_stored_oracle(name):
+    path = os.path.join(GOLDEN, f"full_{name}.npz")
+    if not os.path.exists(path):
+        pytest.skip(f"{path} not generated (tests/golden/make_full_expected.py)")
+    e = np.load(path)
+    print(f"[full] {name}", flush=True)
+    w = synth.workload(name)
+    got = run(w)
+    ref = dict(n_valid=int(e["n_valid"]), loss=float(e["loss"]), lse=e["lse"],
+               dX=e["dx"], dW=e["dw"])
+    check(w, got, ref, dx_rows=e["dx_rows"], dw_rows=e["dw_rows"], what=name)
+    # invariants on the whole outputs
+    _, valid = oracle.targets(w.labels, w.shift, w.ignore_index)
+    assert np.all(got["dX"][~valid] == 0.0)
+    # rows of G sum to zero, so every column of dW sums to ~0
+    colsum = np.abs(got["dW"].sum(axis=0)).max()
+    colnorm = np.sqrt((got["dW"] ** 2).sum(axis=0)).max()
+    assert colsum <= 1e-2 * colnorm, (colsum, colnorm)

@@ -14,7 +14,7 @@ namespace flce {
 namespace {
 
 constexpr int64_t kAlign = 256;
-constexpr int64_t kGSlabBudget = 512ll << 20;   // bytes of the G slab (target)
+constexpr int64_t kVocabBlock = 16384;          // backward vocabulary block
 constexpr int64_t kMaxI32 = 0x7FFFFFFFll;
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -52,8 +52,10 @@ int make_plan(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, Plan* p) {
   int64_t P = 8 * std::max<int64_t>(1, cdiv(1024, 8 * q.TT));
   P = std::min<int64_t>(P, round_up(q.VT, 8));
   q.P = std::max<int64_t>(8, P);
-  // backward: vocabulary block so that the G slab stays near the budget
-  int64_t vb = kGSlabBudget / (q.rows_pad * q.es);
+  // backward: a fixed vocabulary block, so the softmax-gradient slab holds
+  // kVocabBlock values per row whatever V is (smaller only for very many rows,
+  // to keep 32-bit offsets)
+  int64_t vb = std::min<int64_t>(kVocabBlock, kMaxI32 / (q.rows_pad * q.es));
   vb = std::max<int64_t>(kTile, vb / kTile * kTile);
   vb = std::min<int64_t>(vb, round_up(V, kTile));
   q.Vb = vb;

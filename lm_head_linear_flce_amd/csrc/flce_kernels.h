@@ -153,15 +153,18 @@ __global__ __launch_bounds__(256) void k_target(
   float acc = 0.f;
   for (int c = lane; c < (row_bytes >> 4); c += 64) {
     const i32x4 a = x[c], b = w[c];
+    if constexpr (E::kBytes == 2) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if constexpr (E::kBytes == 2) {
+      for (int q = 0; q < 4; ++q) {
         const uint32_t ua = (uint32_t)a[q], ub = (uint32_t)b[q];
         acc = fmaf(bf2f(ua & 0xFFFFu), bf2f(ub & 0xFFFFu), acc);
         acc = fmaf(bf2f(ua >> 16), bf2f(ub >> 16), acc);
-      } else {
-        acc = fmaf(__builtin_bit_cast(float, a[q]), __builtin_bit_cast(float, b[q]), acc);
       }
+    } else {
+      // bit-cast whole vectors: casting single vector elements miscompiles
+      const f32x4 af = __builtin_bit_cast(f32x4, a), bf = __builtin_bit_cast(f32x4, b);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc = fmaf(af[q], bf[q], acc);
     }
   }
 #pragma unroll
@@ -399,9 +402,9 @@ __device__ __forceinline__ void g_store(const BwdArgs& a, const f32x16 (&acc)[4]
           pk[1] = (int)(f2bf(v[2]) | (f2bf(v[3]) << 16));
           __builtin_amdgcn_raw_buffer_store_b64(pk, gr, off, 0, 0);
         } else {
-          i32x4 pk = {__builtin_bit_cast(int, v[0]), __builtin_bit_cast(int, v[1]),
-                      __builtin_bit_cast(int, v[2]), __builtin_bit_cast(int, v[3])};
-          __builtin_amdgcn_raw_buffer_store_b128(pk, gr, off, 0, 0);
+          const f32x4 fv = {v[0], v[1], v[2], v[3]};
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, fv), gr, off, 0,
+                                                 0);
         }
       }
     __builtin_amdgcn_sched_barrier(0);

@@ -164,7 +164,7 @@ def test_zero_weight_gives_log_vocab():
 
 
 def test_peak_memory_never_holds_logits():
-    w = synth.workload("long_context", T=8192, H=256, V=32768, seed=151)
+    w = synth.workload("long_context", T=4096, H=128, V=131072, seed=151)
     X, W, lab = to_device(w)
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
@@ -176,7 +176,7 @@ def test_peak_memory_never_holds_logits():
     ws = F.flce_workspace_size(w.B, w.T, w.H, w.V, F.FLCE_DTYPE_BF16)
     outs = (w.N * w.H + w.V * w.H) * 2 + w.N * 4 + 4096
     assert peak <= ws + outs + (2 << 20), (peak, ws, outs)
-    assert peak < w.N * w.V * 2
+    assert peak < w.N * w.V * 2 / 4
 
 
 # ---------------------------------------------------------------------------
@@ -200,7 +200,12 @@ def test_full_size_against_stored_oracle(name):
     # invariants on the whole outputs
     _, valid = oracle.targets(w.labels, w.shift, w.ignore_index)
     assert np.all(got["dX"][~valid] == 0.0)
-    # rows of G sum to zero, so every column of dW sums to ~0
-    colsum = np.abs(got["dW"].sum(axis=0)).max()
-    colnorm = np.sqrt((got["dW"] ** 2).sum(axis=0)).max()
-    assert colsum <= 1e-2 * colnorm, (colsum, colnorm)
+    # Rows of G sum to zero, so every column of dW sums to zero up to rounding:
+    # G is stored with relative error u_g per entry and sum_v |G_iv| <= 2c, so
+    # |sum_v dW[v, h]| <= 2 u_g c sum_i |X_ih| + u_out sum_v |dW[v, h]| (+ FP32).
+    u = 2.0 ** -8 if w.dtype == "bf16" else 2.0 ** -23
+    c = 1.0 / got["n_valid"] if w.reduction == "mean" else 1.0
+    Xv = w.X[valid].astype(np.float64)
+    bound = 2 * u * c * np.abs(Xv).sum(axis=0) + u * np.abs(got["dW"]).sum(axis=0)
+    colsum = np.abs(got["dW"].sum(axis=0))
+    assert np.all(colsum <= 1.01 * bound + 1e-12), (colsum / bound).max()

@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--workload", default="qwen2_7b_head")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one plain 1 GiB device copy first (reference for "
+                         "the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
 
 
@@ -149,6 +152,14 @@ def main():
     peak_extra = torch.cuda.max_memory_allocated() - base
     out_bytes = dX.numel() * dX.element_size() + dW.numel() * dW.element_size() + 4 * w.N
     del loss, dX, dW
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for _ in range(args.warmup):

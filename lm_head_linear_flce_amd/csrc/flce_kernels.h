@@ -236,7 +236,8 @@ void k_fwd_lse(FwdArgs a) {
   lds_t* smem = (lds_t*)smem_;
   const int item = xcd_item(blockIdx.x, a.nblocks);
   if (item >= a.P * a.TT) return;
-  const int p = item / a.TT, tau = item - p * a.TT;
+  int p, tau;
+  grouped(item, a.P, a.TT, p, tau);
   const int n = a.ctr->n;
   if (tau * kTile >= n) return;
   const int vt0 = (int)((int64_t)p * a.VT / a.P), vt1 = (int)((int64_t)(p + 1) * a.VT / a.P);
@@ -420,7 +421,8 @@ void k_bwd_g(BwdArgs a) {
   lds_t* smem = (lds_t*)smem_;
   const int item = xcd_item(blockIdx.x, a.nblocks);
   if (item >= a.VTb * a.TT) return;
-  const int vt = item / a.TT, tau = item - vt * a.TT;
+  int vt, tau;
+  grouped(item, a.VTb, a.TT, vt, tau);
   const int n = a.ctr->n;
   if (tau * kTile >= n) return;
   const float c = a.ctr->c;
@@ -504,7 +506,8 @@ void k_bwd_dw(BwdArgs a) {
   lds_t* smem = (lds_t*)smem_;
   const int item = xcd_item(blockIdx.x, a.nblocks);
   if (item >= a.HT * a.VTb) return;
-  const int ht = item / a.VTb, vt = item - ht * a.VTb;
+  int ht, vt;
+  grouped(item, a.HT, a.VTb, ht, vt);
   const int n = a.ctr->n;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -564,9 +567,9 @@ void k_bwd_dx(BwdArgs a) {
   lds_t* smem = (lds_t*)smem_;
   const int item = xcd_item(blockIdx.x, a.nblocks);
   if (item >= a.splits * a.HT * a.TT) return;
-  const int sp = item / (a.HT * a.TT);
-  const int rem = item - sp * a.HT * a.TT;
-  const int ht = rem / a.TT, tau = rem - ht * a.TT;
+  int sh, tau;   // sh = split * HT + ht
+  grouped(item, a.splits * a.HT, a.TT, sh, tau);
+  const int sp = sh / a.HT, ht = sh - sp * a.HT;
   const int n = a.ctr->n;
   if (tau * kTile >= n) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;

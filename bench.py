@@ -28,6 +28,22 @@ BF16_PEAK = 2.5e15        # MI355X dense bf16 MFMA, FLOP/s
 F32_PEAK = 157.3e12       # MI355X dense fp32 MFMA, FLOP/s
 HBM_PEAK = 8.0e12         # MI355X HBM3E, B/s
 KERNELS = ("k_fwd_lse", "k_bwd_g", "k_bwd_dw", "k_bwd_dx")
+KERNEL_SOURCES = ("lm_head_linear_flce_amd/csrc/flce_tile.h",
+                  "lm_head_linear_flce_amd/csrc/flce_kernels.h",
+                  "lm_head_linear_flce_amd/csrc/flce_api.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+# the rocprofv3 runs the committed summaries come from ($R = repository root,
+# run from /tmp with TMPDIR=/tmp)
+PROFILE_COMMANDS = (
+    "rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof_trace -o flce "
+    "-- python $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+    "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/prof_fetch -o flce "
+    "-- python $R/bench.py --steps 1 --warmup 0 --no-cpu-baseline --copy-calibration",
+    "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof_write -o flce "
+    "-- python $R/bench.py --steps 1 --warmup 0 --no-cpu-baseline --copy-calibration",
+    "python $R/bench.py --summarize $R/gpurun_out",
+)
+TRAFFIC = os.path.join(PROFILES, "traffic_qwen2_7b_head.json")
 METRIC = "fused linear-CE fwd+bwd tokens/sec and % bf16 MFMA peak; peak extra HBM bytes"
 
 
@@ -39,6 +55,10 @@ def parse():
     ap.add_argument("--workload", default="qwen2_7b_head")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--summarize", metavar="DIR",
+                    help="summarise the rocprofv3 output of PROFILE_COMMANDS under DIR "
+                         "(DIR/prof_trace, DIR/prof_fetch, DIR/prof_write) into "
+                         "profiles/ and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one plain 1 GiB device copy first (reference for "
                          "the FETCH_SIZE / WRITE_SIZE counters)")
@@ -79,6 +99,18 @@ class HipEvents:
             self.hip.hipEventDestroy(self.arr[i])
 
 
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or
+    None when there is none for this workload or the kernels changed since."""
+    if workload != "qwen2_7b_head" or not os.path.exists(TRAFFIC):
+        return None
+    with open(TRAFFIC) as f:
+        t = json.load(f)
+    if t.get("source_hash") != source_hash():
+        return None
+    return t["bytes_per_launch"].get(kernel)
+
+
 def oracle_baseline(w, rows_wanted):
     """The float64 oracle on a bounded sample of valid rows (full per-row work:
     logits rows, softmax, dX rows and their dW contribution), extrapolated to
@@ -110,8 +142,94 @@ def oracle_baseline(w, rows_wanted):
     }
 
 
+def source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _short(name):
+    import re
+    name = re.sub(r"\(.*", "", name).replace("void ", "")
+    return name.replace("flce::", "")
+
+
+def summarize(prof_dir, command):
+    """Kernel-trace statistics and calibrated HBM traffic -> profiles/."""
+    import csv
+    import glob
+    stats = glob.glob(os.path.join(prof_dir, "prof_trace", "**", "*kernel_stats.csv"),
+                      recursive=True)
+    pmcs = [p for sub in ("prof_fetch", "prof_write") for p in glob.glob(
+        os.path.join(prof_dir, sub, "**", "*counter_collection.csv"), recursive=True)]
+    lines = ["# Kernel time and HBM traffic: Qwen2-7B-like LM head, N=8192 H=3584 "
+             "V=152064 bf16", "", f"kernel source hash: `{source_hash()}`", "",
+             "Commands (run from /tmp with TMPDIR=/tmp; $R = repository root):", "",
+             "```", *command, "```", ""]
+    rows = []
+    for path in stats:
+        for r in csv.DictReader(open(path)):
+            rows.append((_short(r["Name"]), int(r["Calls"]), float(r["TotalDurationNs"]),
+                         float(r["AverageNs"]), float(r["Percentage"])))
+    rows.sort(key=lambda x: -x[2])
+    lines += ["## rocprofv3 --kernel-trace --stats", "",
+              "| kernel | calls | total ms | avg us | % |", "|---|---|---|---|---|"]
+    for n, c, tot, avg, pct in rows:
+        if pct < 0.01:
+            continue
+        lines.append(f"| {n} | {c} | {tot / 1e6:.3f} | {avg / 1e3:.1f} | {pct:.2f} |")
+    # counters: per kernel, per dispatch averages; the 1 GiB copy calibrates
+    per = {}
+    calib = {}
+    for path in pmcs:
+        for r in csv.DictReader(open(path)):
+            n = _short(r["Kernel_Name"])
+            cn = r["Counter_Name"]
+            v = float(r["Counter_Value"])
+            if "copyBuffer" in n and int(r["Grid_Size"]) == 131072:
+                calib[cn] = v
+                continue
+            d = per.setdefault(n, {}).setdefault(cn, [0.0, 0])
+            d[0] += v
+            d[1] += 1
+    gib_kib = float(1 << 20)
+    f_fetch = gib_kib / calib["FETCH_SIZE"] if calib.get("FETCH_SIZE") else None
+    f_write = gib_kib / calib["WRITE_SIZE"] if calib.get("WRITE_SIZE") else None
+    lines += ["", "## HBM traffic (rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE)", "",
+              f"Calibration: a plain 1 GiB device copy reads FETCH_SIZE = "
+              f"{calib.get('FETCH_SIZE', float('nan')):.0f} KiB and WRITE_SIZE = "
+              f"{calib.get('WRITE_SIZE', float('nan')):.0f} KiB; scale factors "
+              f"{f_fetch} and {f_write}.", "",
+              "| kernel | dispatches | fetch MB / launch | write MB / launch | traffic MB / launch |",
+              "|---|---|---|---|---|"]
+    traffic = {}
+    for n, d in sorted(per.items()):
+        if not any(k in n for k in KERNELS) or "FETCH_SIZE" not in d or "WRITE_SIZE" not in d:
+            continue
+        fe = d["FETCH_SIZE"][0] / d["FETCH_SIZE"][1] * 1024 * (f_fetch or 1.0)
+        wr = d["WRITE_SIZE"][0] / d["WRITE_SIZE"][1] * 1024 * (f_write or 1.0)
+        key = n.split("<")[0]
+        traffic[key] = fe + wr
+        lines.append(f"| {n} | {d['FETCH_SIZE'][1]} | {fe / 1e6:.1f} | {wr / 1e6:.1f} | "
+                     f"{(fe + wr) / 1e6:.1f} |")
+    os.makedirs(PROFILES, exist_ok=True)
+    md = os.path.join(PROFILES, "flce_qwen2_7b_head_kernels.md")
+    with open(md, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    with open(TRAFFIC, "w") as f:
+        json.dump({"source_hash": source_hash(), "bytes_per_launch": traffic,
+                   "calibration": {"fetch": f_fetch, "write": f_write}}, f, indent=1)
+    print(md)
+
+
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args.summarize, PROFILE_COMMANDS)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path "
               "has no multi-GPU mode", file=sys.stderr)
@@ -239,7 +357,7 @@ def main():
                         for kk, vv in v.items()} for k, v in per_kernel.items()},
         "roofline": {"bound": "mfma", "kernel": dom, "achieved": ach / 1e12,
                      "peak": peak / 1e12, "unit": "TFLOP/s", "frac": ach / peak,
-                     "traffic": None},
+                     "traffic": measured_traffic(dom, w.name)},
     }
     if not args.no_cpu_baseline:
         print("[bench] oracle on the host", file=sys.stderr, flush=True)

@@ -244,7 +244,6 @@ void k_fwd_lse(FwdArgs a) {
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const FragOffsets fo(wm, wn);
   const int ldb = a.H * E::kBytes;
   const int steps = (ldb + kRowBytes - 1) / kRowBytes;
 
@@ -268,7 +267,8 @@ void k_fwd_lse(FwdArgs a) {
     A.ldb = ldb;
     A.kbytes = ldb;
     zero_acc(acc);
-    gemm_tile<E, LoadDirect, LoadDirect>(A, B, steps, ldb % kRowBytes != 0, smem, fo, acc);
+    gemm_tile<E, LoadDirect, LoadDirect>(A, B, steps, smem, wm, wn,
+                                         acc);
     // rows at or past V (last tile only) take no part in the reduction
     const int vlim = a.V - vt * kTile;
     if (vlim >= kTile) lse_update<false>(acc, m, s, 0);
@@ -428,7 +428,6 @@ void k_bwd_g(BwdArgs a) {
   const float c = a.ctr->c;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const FragOffsets fo(wm, wn);
   const int ldb = a.H * E::kBytes;
   const int steps = (ldb + kRowBytes - 1) / kRowBytes;
   const int vbase = a.v0 + vt * kTile;
@@ -444,7 +443,8 @@ void k_bwd_g(BwdArgs a) {
   B.kbytes = ldb;
   f32x16 acc[4][4];
   zero_acc(acc);
-  gemm_tile<E, LoadDirect, LoadDirect>(A, B, steps, ldb % kRowBytes != 0, smem, fo, acc);
+  gemm_tile<E, LoadDirect, LoadDirect>(A, B, steps, smem, wm, wn,
+                                         acc);
 
   const int vlim = a.V - vbase;
   if (vlim >= kTile && (tau + 1) * kTile <= n)
@@ -511,7 +511,6 @@ void k_bwd_dw(BwdArgs a) {
   const int n = a.ctr->n;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const FragOffsets fo(wm, wn);
   const int es = E::kBytes;
   const int steps = (n + E::kKStep - 1) / E::kKStep;
 
@@ -526,8 +525,7 @@ void k_bwd_dw(BwdArgs a) {
   B.kbytes = 0;
   f32x16 acc[4][4];
   zero_acc(acc);
-  using LT = typename TransLoader<E>::type;
-  gemm_tile<E, LT, LT>(A, B, steps, false, smem, fo, acc);
+  gemm_tile<E, LoadMN<E>, LoadMN<E>>(A, B, steps, smem, wm, wn, acc);
 
   const int mlim = a.vb - vt * kTile, hlim = a.H - ht * kTile;
   if (mlim >= kTile && hlim >= kTile)
@@ -574,7 +572,6 @@ void k_bwd_dx(BwdArgs a) {
   if (tau * kTile >= n) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const FragOffsets fo(wm, wn);
   const int es = E::kBytes;
   // the block's K range [0, vb_pad) split into `splits` whole steps
   const int ksteps_total = (a.vb + E::kKStep - 1) / E::kKStep;
@@ -593,8 +590,7 @@ void k_bwd_dx(BwdArgs a) {
   B.kbytes = 0;
   f32x16 acc[4][4];
   zero_acc(acc);
-  gemm_tile<E, LoadDirect, typename TransLoader<E>::type>(A, B, s1 - s0, false, smem, fo,
-                                                          acc);
+  gemm_tile<E, LoadDirect, LoadMN<E>>(A, B, s1 - s0, smem, wm, wn, acc);
 
   // rows >= n hold zeros (G is 0 there) and stay inside the accumulator;
   // columns past H would land in the next row and are skipped

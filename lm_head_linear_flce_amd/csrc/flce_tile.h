@@ -9,8 +9,8 @@
 //
 //   LDS = A[2 stages][256 rows][128 B] + B[2 stages][256 rows][128 B] = 128 KiB
 //
-// Inside LDS every operand row is K-contiguous, so one ds_read_b128 hands a
-// lane the 8 bf16 (or 4 fp32) K-values an MFMA lane expects.  The 16-byte chunk
+// A K-major LDS row is K-contiguous, so one ds_read_b128 hands a lane the 8
+// bf16 (or 4 fp32) K values an MFMA lane expects.  The 16-byte chunk
 // c of row r is stored at a row-dependent XOR-permuted chunk position so that
 // the lanes one LDS cycle serves touch distinct bank groups for fragment
 // reads and for stores; see swz() for the exact pattern.
@@ -20,12 +20,10 @@
 // vocabulary / row tails need no branch and can never fault.  Two loaders:
 //   * LoadDirect  -- the operand is stored with K contiguous (row-major
 //                    [rows][K]), e.g. W [V, H] or X [N, H] contracted over H;
-//   * LoadTrans*  -- the operand is stored with K as the outer index
+//   * LoadMN      -- the operand is stored with K as the outer index
 //                    ([K][rows]), e.g. X [N, H] or W [V, H] contracted over N
-//                    or V.  Each thread reads an E x E block (E = 16 / bytes
-//                    per element) with E row loads of 16 B, transposes it in
-//                    registers (v_perm_b32 for bf16, plain moves for fp32) and
-//                    writes E K-contiguous chunks.
+//                    or V.  It keeps that layout in LDS and the fragment read
+//                    transposes (ds_read_b64_tr_b16 on gfx950).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -98,29 +96,28 @@ struct Opnd {
 // ---------------------------------------------------------------------------
 struct LoadDirect {
   static constexpr bool kTransposed = false;
+  struct Frag;
   i32x4 v[8];
-  // kTail: the step may run past the end of the rows' K extent; chunks beyond
-  // it are replaced by zeros (they would hold the next row's values).
-  // quarter `part` (0..3) of the loads: register rows 2*part, 2*part+1
-  template <class E, bool kTail>
-  __device__ __forceinline__ void issue_part(const Opnd& o, int s, int part) {
+  // Quarter `part` (0..3) of the loads of step s: register rows 2*part and
+  // 2*part+1.  A chunk at or past the rows' K extent (it would hold the next
+  // row's values) and every chunk of a step that is not `live` read zeros:
+  // the descriptor covers at most the tile's 256 rows (< 2^31 bytes, as H is
+  // bounded), so the offset 2^31 is always out of range.
+  template <class E>
+  __device__ __forceinline__ void issue_part(const Opnd& o, int s, int part, bool live) {
     const int c = threadIdx.x & 7, rr = threadIdx.x >> 3;
-    const rsrc_t r = make_rsrc(o.base, o.bytes);
+    const int64_t span = (int64_t)kTile * o.ldb;
+    const rsrc_t r = make_rsrc(o.base, live ? (o.bytes < span ? o.bytes : span) : 0);
     const int kb = s * kRowBytes + c * 16;
+    const bool ok = kb < o.kbytes;
 #pragma unroll
-    for (int i = 2 * part; i < 2 * part + 2; ++i) {
-      v[i] = bload128(r, (rr + 32 * i) * o.ldb + kb);
-      if constexpr (kTail) {
-        const bool ok = kb < o.kbytes;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) v[i][q] = ok ? v[i][q] : 0;
-      }
-    }
+    for (int i = 2 * part; i < 2 * part + 2; ++i)
+      v[i] = bload128(r, ok ? (rr + 32 * i) * o.ldb + kb : (int)0x80000000u);
   }
-  template <class E, bool kTail>
-  __device__ __forceinline__ void issue(const Opnd& o, int s) {
+  template <class E>
+  __device__ __forceinline__ void issue(const Opnd& o, int s, bool live) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) issue_part<E, kTail>(o, s, q);
+    for (int q = 0; q < 4; ++q) issue_part<E>(o, s, q, live);
   }
   // quarter `part` (0..3) of the stores: register rows 2*part, 2*part+1
   __device__ __forceinline__ void commit_part(lds_t* slab, int part) const {
@@ -135,86 +132,133 @@ struct LoadDirect {
   }
 };
 
-// bf16, K-outer storage: thread (kb = t % 8, mb = t / 8) reads K rows
-// 8kb..8kb+7 of columns 8mb..8mb+7 and writes rows 8mb+i, chunk kb.
-struct LoadTransBF16 {
-  static constexpr bool kTransposed = true;
-  i32x4 v[8];
-  template <class E, bool kTail>
-  __device__ __forceinline__ void issue_part(const Opnd& o, int s, int part) {
-    const int kb = threadIdx.x & 7, mb = threadIdx.x >> 3;
-    const int64_t k0 = (int64_t)s * BF16::kKStep;
-    const rsrc_t r = make_rsrc(o.base + k0 * o.ldb, o.bytes - k0 * o.ldb);
+typedef const __attribute__((address_space(3))) i32x4 lds_ci32x4;
+typedef const __attribute__((address_space(3))) int lds_cint;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+
+// Fragment reader of a K-major slab: one ds_read_b128 per 32-row block.
+struct LoadDirect::Frag {
+  int off[4];   // per chunk pair p
+  __device__ __forceinline__ explicit Frag(int row_base) {
+    const int lane = threadIdx.x & 63, r32 = lane & 31, h = lane >> 5;
 #pragma unroll
-    for (int j = 2 * part; j < 2 * part + 2; ++j)
-      v[j] = bload128(r, (kb * 8 + j) * o.ldb + mb * 16);
+    for (int p = 0; p < 4; ++p) off[p] = swz(row_base + r32, 2 * p + h);
   }
-  template <class E, bool kTail>
-  __device__ __forceinline__ void issue(const Opnd& o, int s) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) issue_part<E, kTail>(o, s, q);
+  __device__ __forceinline__ i32x4 read(const lds_t* slab, int p, int i) const {
+    return *(lds_ci32x4*)(slab + off[p] + i * 4096);
   }
-  __device__ __forceinline__ void commit(lds_t* slab) const {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) commit_part(slab, q);
-  }
-  __device__ __forceinline__ void commit_part(lds_t* slab, int part) const {
-    const int kb = threadIdx.x & 7, mb = threadIdx.x >> 3;
-#pragma unroll
-    for (int i = 2 * part; i < 2 * part + 2; ++i) {
-      const unsigned sel = (i & 1) ? 0x07060302u : 0x05040100u;
-      i32x4 o;
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        o[q] = (int)__builtin_amdgcn_perm((unsigned)v[2 * q + 1][i >> 1],
-                                          (unsigned)v[2 * q][i >> 1], sel);
-      *(__attribute__((address_space(3))) i32x4*)(slab + swz(mb * 8 + i, kb)) = o;
-    }
-  }
+  static constexpr int kReads = 1;
 };
 
-// fp32, K-outer storage: two 4 x 4 blocks per thread.
-struct LoadTransF32 {
+// K-outer storage, kept K-outer in LDS ("MN-major"): LDS row = one K index
+// with the tile's 256 columns contiguous.  The loads are plain 16-byte copies;
+// the transpose happens in the fragment read.
+//   bf16: 64 K rows of 512 B; chunk c of K row k at chunk c ^ 4(k&3), which
+//         keeps the transposing reads below free of bank conflicts.  Thread t
+//         copies chunk t % 32 of K rows t / 32 + 8 i.
+//   fp32: 32 K rows of 1 KiB, no permutation; thread t copies chunk t % 64 of
+//         K rows t / 64 + 4 i.
+template <class E> struct LoadMN;
+
+template <>
+struct LoadMN<BF16> {
   static constexpr bool kTransposed = true;
   i32x4 v[8];
-  template <class E, bool kTail>
-  __device__ __forceinline__ void issue_part(const Opnd& o, int s, int part) {
-    const int64_t k0 = (int64_t)s * F32::kKStep;
-    const rsrc_t r = make_rsrc(o.base + k0 * o.ldb, o.bytes - k0 * o.ldb);
-    const int blk = part >> 1;
-    const int b = threadIdx.x + kThreads * blk;
-    const int kb = b & 7, mb = b >> 3;
+  template <class E>
+  __device__ __forceinline__ void issue_part(const Opnd& o, int s, int part, bool live) {
+    const int c = threadIdx.x & 31, kr = threadIdx.x >> 5;
+    const int64_t k0 = (int64_t)s * BF16::kKStep;
+    const rsrc_t r = make_rsrc(o.base + k0 * o.ldb, live ? o.bytes - k0 * o.ldb : 0);
 #pragma unroll
-    for (int j = 2 * (part & 1); j < 2 * (part & 1) + 2; ++j)
-      v[blk * 4 + j] = bload128(r, (kb * 4 + j) * o.ldb + mb * 16);
+    for (int i = 2 * part; i < 2 * part + 2; ++i) v[i] = bload128(r, (kr + 8 * i) * o.ldb + c * 16);
   }
-  template <class E, bool kTail>
-  __device__ __forceinline__ void issue(const Opnd& o, int s) {
+  template <class E>
+  __device__ __forceinline__ void issue(const Opnd& o, int s, bool live) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) issue_part<E, kTail>(o, s, q);
+    for (int q = 0; q < 4; ++q) issue_part<E>(o, s, q, live);
+  }
+  __device__ __forceinline__ void commit_part(lds_t* slab, int part) const {
+    const int c = threadIdx.x & 31, kr = threadIdx.x >> 5;
+    const int base = kr * 512 + ((c ^ (4 * (kr & 3))) << 4);
+#pragma unroll
+    for (int i = 2 * part; i < 2 * part + 2; ++i)
+      *(__attribute__((address_space(3))) i32x4*)(slab + base + i * 4096) = v[i];
   }
   __device__ __forceinline__ void commit(lds_t* slab) const {
 #pragma unroll
     for (int q = 0; q < 4; ++q) commit_part(slab, q);
   }
-  __device__ __forceinline__ void commit_part(lds_t* slab, int part) const {
-    const int blk = part >> 1;
-    {
-      const int b = threadIdx.x + kThreads * blk;
-      const int kb = b & 7, mb = b >> 3;
+  // Lane l = 16 G + j of a wave: the group of 16 reads K rows 8(G/2) + j/4
+  // (+ 16 p + 4 r), columns cb + 16 (G&1) + 4 (j&3) .. +3; ds_read_b64_tr_b16
+  // then gives lane j the 4 K values of column cb + 16 (G&1) + j, r = 0 the
+  // first four of its eight, r = 1 the last four.
+  struct Frag {
+    int off[4];   // per 32-column block i
+    __device__ __forceinline__ explicit Frag(int col_base) {
+      const int lane = threadIdx.x & 63, G = lane >> 4, j = lane & 15;
+      const int k = 8 * (G >> 1) + (j >> 2);
 #pragma unroll
-      for (int i = 2 * (part & 1); i < 2 * (part & 1) + 2; ++i) {
-        i32x4 o = {v[blk * 4 + 0][i], v[blk * 4 + 1][i], v[blk * 4 + 2][i],
-                   v[blk * 4 + 3][i]};
-        *(__attribute__((address_space(3))) i32x4*)(slab + swz(mb * 4 + i, kb)) = o;
+      for (int i = 0; i < 4; ++i) {
+        const int col = col_base + 32 * i + 16 * (G & 1) + 4 * (j & 3);
+        off[i] = k * 512 + (((col >> 3) ^ (4 * (k & 3))) << 4) + (col & 7) * 2;
       }
     }
-  }
+    __device__ __forceinline__ i32x4 read(const lds_t* slab, int p, int i) const {
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(slab + off[i] + (16 * p) * 512));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (lds_i16x4*)(slab + off[i] + (16 * p + 4) * 512));
+      const i32x2 l2 = __builtin_bit_cast(i32x2, lo), h2 = __builtin_bit_cast(i32x2, hi);
+      return i32x4{l2[0], l2[1], h2[0], h2[1]};
+    }
+    static constexpr int kReads = 2;
+  };
 };
 
-template <class E> struct TransLoader;
-template <> struct TransLoader<BF16> { using type = LoadTransBF16; };
-template <> struct TransLoader<F32> { using type = LoadTransF32; };
+template <>
+struct LoadMN<F32> {
+  static constexpr bool kTransposed = true;
+  i32x4 v[8];
+  template <class E>
+  __device__ __forceinline__ void issue_part(const Opnd& o, int s, int part, bool live) {
+    const int c = threadIdx.x & 63, kr = threadIdx.x >> 6;
+    const int64_t k0 = (int64_t)s * F32::kKStep;
+    const rsrc_t r = make_rsrc(o.base + k0 * o.ldb, live ? o.bytes - k0 * o.ldb : 0);
+#pragma unroll
+    for (int i = 2 * part; i < 2 * part + 2; ++i) v[i] = bload128(r, (kr + 4 * i) * o.ldb + c * 16);
+  }
+  template <class E>
+  __device__ __forceinline__ void issue(const Opnd& o, int s, bool live) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) issue_part<E>(o, s, q, live);
+  }
+  __device__ __forceinline__ void commit_part(lds_t* slab, int part) const {
+    const int c = threadIdx.x & 63, kr = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 2 * part; i < 2 * part + 2; ++i)
+      *(__attribute__((address_space(3))) i32x4*)(slab + (kr + 4 * i) * 1024 + c * 16) = v[i];
+  }
+  __device__ __forceinline__ void commit(lds_t* slab) const {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) commit_part(slab, q);
+  }
+  // lane (column l%32, half h) takes k = 8p + 4h + e, e = 0..3
+  struct Frag {
+    int off;
+    __device__ __forceinline__ explicit Frag(int col_base) {
+      const int lane = threadIdx.x & 63;
+      off = 4 * (lane >> 5) * 1024 + (col_base + (lane & 31)) * 4;
+    }
+    __device__ __forceinline__ i32x4 read(const lds_t* slab, int p, int i) const {
+      i32x4 v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[e] = *(lds_cint*)(slab + off + (8 * p + e) * 1024 + i * 128);
+      return v;
+    }
+    static constexpr int kReads = 4;
+  };
+};
 
 // ---------------------------------------------------------------------------
 // MFMA on one LDS slab pair.  For chunk pair p (K bytes 32p..32p+31) lane
@@ -242,73 +286,55 @@ __device__ __forceinline__ void mma<F32>(const i32x4& a, const i32x4& b, f32x16&
     c = __builtin_amdgcn_mfma_f32_32x32x2f32(af[j], bf[j], c, 0, 0, 0);
 }
 
-// Per-lane LDS byte offsets of the fragment rows for chunk pair p, relative to
-// an operand slab.  Block mb (or nb) adds mb * 32 rows = mb * 4096 bytes.
-struct FragOffsets {
-  int a[4], b[4];
-  __device__ __forceinline__ FragOffsets(int wm, int wn) {
-    const int lane = threadIdx.x & 63, r32 = lane & 31, h = lane >> 5;
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      a[p] = swz(wm * 128 + r32, 2 * p + h);
-      b[p] = swz(wn * 128 + r32, 2 * p + h);
-    }
-  }
-};
-
 // Fragments of one chunk pair: 4 A blocks and 4 B blocks, 16 B each.
 struct Frags {
   i32x4 a[4], b[4];
-  __device__ __forceinline__ void load(const lds_t* sa, const lds_t* sb,
-                                       const FragOffsets& fo, int p) {
-    typedef const __attribute__((address_space(3))) i32x4 lv;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = *(lv*)(sa + fo.a[p] + i * 4096);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) b[j] = *(lv*)(sb + fo.b[p] + j * 4096);
-  }
 };
 
-// The reads of chunk pair p+1 are issued before the 16 MFMAs of pair p; a
-// scheduling barrier after each pair keeps the compiler from hoisting every
-// read of the slab up front (which would need 128 fragment registers).
-// `mid(p)` runs after the MFMAs of pair p are issued: the main loop stores a
-// quarter of the next step's operands to LDS there while those MFMAs execute.
 // Scheduling-group masks of __builtin_amdgcn_sched_group_barrier.
 constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100,
               kSchedDsWrite = 0x200;
 
-template <class E, bool kInterleave, class Mid>
-__device__ __forceinline__ void mma_slab(const lds_t* sa, const lds_t* sb,
-                                         const FragOffsets& fo,
-                                         f32x16 (&acc)[4][4], Mid&& mid) {
+// The fragment reads of chunk pair p+1 are issued before the 16 MFMAs of pair
+// p.  `mid(p)` then adds a quarter of the next step's LDS stores and of the
+// step after's global loads; the scheduling groups put one or two memory
+// instructions between consecutive MFMAs, fragment reads first.
+template <class E, class FA, class FB, class Mid>
+__device__ __forceinline__ void mma_slab(const lds_t* sa, const lds_t* sb, const FA& fa,
+                                         const FB& fb, f32x16 (&acc)[4][4], Mid&& mid) {
+  constexpr int kDsr = 4 * (FA::kReads + FB::kReads);
   Frags f[2];
-  f[0].load(sa, sb, fo, 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) f[0].a[i] = fa.read(sa, 0, i);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) f[0].b[j] = fb.read(sb, 0, j);
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    if (p + 1 < 4) f[(p + 1) & 1].load(sa, sb, fo, p + 1);
+    if (p + 1 < 4) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f[(p + 1) & 1].a[i] = fa.read(sa, p + 1, i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) f[(p + 1) & 1].b[j] = fb.read(sb, p + 1, j);
+    }
     const Frags& c = f[p & 1];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int j = 0; j < 4; ++j) mma<E>(c.a[i], c.b[j], acc[i][j]);
     mid(p);
-    // one memory instruction between consecutive MFMAs: the 8 fragment reads
-    // of the next pair, then the pair's share of LDS stores and global loads
-    // (not when both operands are transposed: their stores wait on VALU
-    // permutes and are better left in a cluster)
-    if constexpr (E::kBytes == 2 && kInterleave) {
+    if constexpr (E::kBytes == 2) {
 #pragma unroll
-      for (int q = 0; q < 8; ++q) {
+      for (int q = 0; q < 16; ++q) {
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-      }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+        if (p + 1 < 4 && q < kDsr) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        if (kDsr <= 8) {
+          // fragment reads in the first half, stores and loads in the second
+          if (q >= 8 && (q & 1) == 0) __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 1, 0);
+          if (q >= 8 && (q & 1) == 1) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+        } else {
+          if ((q & 3) == 1) __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 1, 0);
+          if ((q & 3) == 3) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -328,18 +354,16 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][4]) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 }
 
-// Full K loop of one tile: acc += A . B^T over `steps` steps; `tail` says the
-// last step may cross the end of the K extent (direct operands only).
+// Full K loop of one tile: acc += A . B^T over `steps` steps.
 //
 // Software pipeline: global loads run two steps ahead of the MFMAs, into two
 // alternating register sets, and land in one of two LDS stages:
-//   step s:  issue loads of step s+2 -> regs[s%2]   (their old content, step s,
-//                                                    is already in LDS)
-//            MFMAs on LDS stage s%2, with the stores of regs[(s+1)%2]
-//            (step s+1) -> LDS stage (s+1)%2 interleaved between them
+//   step s:  MFMAs on LDS stage s%2; between them, quarter by quarter, the
+//            stores of regs[(s+1)%2] (step s+1) -> LDS stage (s+1)%2 and the
+//            loads of step s+2 -> regs[s%2] (whose step s is already in LDS)
 //            barrier
-// so every load has about two steps of MFMA time to arrive.  The steady-state
-// loop runs step pairs with no branch inside; the last 1-3 steps are peeled.
+// so a quarter of the loads has one step of MFMA time to arrive before its
+// registers are stored.  The loop runs step pairs with one branch-free body.
 // Ends with a barrier, so the caller may reuse LDS right after.
 template <class E, class LA, class LB>
 struct TilePipe {
@@ -348,87 +372,52 @@ struct TilePipe {
   const Opnd& A;
   const Opnd& B;
   int steps;
-  bool tail;
   lds_t* sa;
   lds_t* sb;
-  const FragOffsets& fo;
+  typename LA::Frag fa;
+  typename LB::Frag fb;
 
-  __device__ __forceinline__ TilePipe(const Opnd& a, const Opnd& b, int n, bool t,
-                                      lds_t* smem, const FragOffsets& f)
-      : A(a), B(b), steps(n), tail(t), sa(smem), sb(smem + 2 * kSlab), fo(f) {}
+  __device__ __forceinline__ TilePipe(const Opnd& a, const Opnd& b, int n, lds_t* smem,
+                                      int wm, int wn)
+      : A(a), B(b), steps(n), sa(smem), sb(smem + 2 * kSlab), fa(wm * 128),
+        fb(wn * 128) {}
 
+  // one step s with s % 2 == k: MFMAs on slab k, the loads of step s + 1 go to
+  // slab k ^ 1, the loads of step s + 2 are issued into registers k.  Steps
+  // at or past `steps` load zeros, so the loop needs no peeled tail (an odd
+  // count runs one all-zero step).
   template <int k>
-  __device__ __forceinline__ void issue(int s) {
-    if (tail && s == steps - 1) {
-      la[k].template issue<E, true>(A, s);
-      lb[k].template issue<E, true>(B, s);
-    } else {
-      la[k].template issue<E, false>(A, s);
-      lb[k].template issue<E, false>(B, s);
-    }
-  }
-  template <int k>
-  __device__ __forceinline__ void commit() {
-    la[k].commit(sa + k * kSlab);
-    lb[k].commit(sb + k * kSlab);
-  }
-  // one step s with s % 2 == k
-  template <int k>
-  __device__ __forceinline__ void issue_part(int s, int part) {
-    if (tail && s == steps - 1) {
-      la[k].template issue_part<E, true>(A, s, part);
-      lb[k].template issue_part<E, true>(B, s, part);
-    } else {
-      la[k].template issue_part<E, false>(A, s, part);
-      lb[k].template issue_part<E, false>(B, s, part);
-    }
-  }
-  static constexpr bool kInterleave = !(LA::kTransposed && LB::kTransposed);
-  template <int k, bool kIssue, bool kCommit>
   __device__ __forceinline__ void step(int s, f32x16 (&acc)[4][4]) {
-    if constexpr (kIssue && !kInterleave) {
-      issue<k>(s + 2);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    mma_slab<E, kInterleave>(sa + k * kSlab, sb + k * kSlab, fo, acc, [&](int part) {
-      if constexpr (kCommit) {
-        la[k ^ 1].commit_part(sa + (k ^ 1) * kSlab, part);
-        lb[k ^ 1].commit_part(sb + (k ^ 1) * kSlab, part);
-      }
-      if constexpr (kIssue && kInterleave) issue_part<k>(s + 2, part);
+    const bool live = s + 2 < steps;
+    mma_slab<E>(sa + k * kSlab, sb + k * kSlab, fa, fb, acc, [&](int part) {
+      la[k ^ 1].commit_part(sa + (k ^ 1) * kSlab, part);
+      lb[k ^ 1].commit_part(sb + (k ^ 1) * kSlab, part);
+      la[k].template issue_part<E>(A, s + 2, part, live);
+      lb[k].template issue_part<E>(B, s + 2, part, live);
     });
     __syncthreads();
   }
   __device__ __forceinline__ void run(f32x16 (&acc)[4][4]) {
     if (steps <= 0) return;
-    issue<0>(0);
-    if (steps > 1) issue<1>(1);
-    commit<0>();
+    la[0].template issue<E>(A, 0, true);
+    lb[0].template issue<E>(B, 0, true);
+    la[1].template issue<E>(A, 1, steps > 1);
+    lb[1].template issue<E>(B, 1, steps > 1);
+    la[0].commit(sa);
+    lb[0].commit(sb);
     __syncthreads();
-    int s = 0;
-    for (; s + 3 < steps; s += 2) {
-      step<0, true, true>(s, acc);
-      step<1, true, true>(s + 1, acc);
-    }
-    const int rem = steps - s;   // 1, 2 or 3, s even
-    if (rem == 3) {
-      step<0, true, true>(s, acc);
-      step<1, false, true>(s + 1, acc);
-      step<0, false, false>(s + 2, acc);
-    } else if (rem == 2) {
-      step<0, false, true>(s, acc);
-      step<1, false, false>(s + 1, acc);
-    } else {
-      step<0, false, false>(s, acc);
+    for (int s = 0; s < steps; s += 2) {
+      step<0>(s, acc);
+      step<1>(s + 1, acc);
     }
   }
 };
 
 template <class E, class LA, class LB>
 __device__ __forceinline__ void gemm_tile(const Opnd& A, const Opnd& B, int steps,
-                                          bool tail, lds_t* smem, const FragOffsets& fo,
+                                          lds_t* smem, int wm, int wn,
                                           f32x16 (&acc)[4][4]) {
-  TilePipe<E, LA, LB> pipe(A, B, steps, tail, smem, fo);
+  TilePipe<E, LA, LB> pipe(A, B, steps, smem, wm, wn);
   pipe.run(acc);
 }
 

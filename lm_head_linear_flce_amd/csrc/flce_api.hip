@@ -24,7 +24,7 @@ int64_t cdiv(int64_t x, int64_t m) { return (x + m - 1) / m; }
 struct Plan {
   int64_t N, rows_pad, H, V, es;
   int64_t TT, VT;           // token tiles (upper bound), vocabulary tiles
-  int64_t P;                // forward vocabulary ranges (multiple of 8)
+  int64_t fwd_items;        // forward work items (range x token tile), at most
   int64_t Vb;               // backward vocabulary block (multiple of 256)
   // workspace offsets (bytes)
   int64_t o_ctr, o_idx, o_tgt, o_rowpos, o_xc;
@@ -48,10 +48,9 @@ int make_plan(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, Plan* p) {
   q.rows_pad = round_up(N > 0 ? N : 1, kTile);
   q.TT = q.rows_pad / kTile;
   q.VT = cdiv(V, kTile);
-  // forward: about four launch waves of 256 CUs in (range x token tile) items
-  int64_t P = 8 * std::max<int64_t>(1, cdiv(1024, 8 * q.TT));
-  P = std::min<int64_t>(P, round_up(q.VT, 8));
-  q.P = std::max<int64_t>(8, P);
+  // forward: the split itself is chosen on the device (k_prep), once the
+  // number of valid rows is known; this bounds its item count and partials
+  q.fwd_items = std::max<int64_t>(2048, q.TT);
   // backward: a fixed vocabulary block, so the softmax-gradient slab holds
   // kVocabBlock values per row whatever V is (smaller only for very many rows,
   // to keep 32-bit offsets)
@@ -76,7 +75,7 @@ int make_plan(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, Plan* p) {
   q.o_rowpos = take(4 * q.rows_pad);
   q.o_xc = take(q.rows_pad * H * q.es);
   const int64_t common = off;
-  q.o_part = take(8 * q.P * q.rows_pad);
+  q.o_part = take(8 * kTile * q.fwd_items);
   q.o_zt = take(4 * q.rows_pad);
   q.o_bsum = take(4 * cdiv(q.rows_pad, 256));
   const int64_t fwd_end = off;
@@ -113,6 +112,17 @@ struct Launch {
 };
 
 int64_t pad8(int64_t n) { return round_up(n, 8); }
+
+// Compute units of the current device (the forward split prices launch waves
+// of this many workgroups); 256 if the query fails.
+int cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0)
+    return 256;
+  return n;
+}
 
 // Measurement hook (flce_set_timing): events recorded around the launches of
 // one named kernel.
@@ -158,8 +168,8 @@ int forward_impl(const Plan& pl, const void* X, const void* W, const int64_t* la
   const int row_bytes = (int)(pl.H * E::kBytes);
 
   hipLaunchKernelGGL(k_prep, dim3(1), dim3(1024), 0, stream, labels, (int)B, (int)T,
-                     ignore_index, pl.V, shift, reduction, (const float*)nullptr, idx,
-                     tgt, rowpos, ctr, status);
+                     ignore_index, pl.V, shift, reduction, (const float*)nullptr,
+                     cu_count(), (int)pl.fwd_items, idx, tgt, rowpos, ctr, status);
   L.check();
   hipLaunchKernelGGL(k_gather, dim3((unsigned)cdiv(rows_pad, 4)), dim3(256), 0, stream,
                      (const char*)X, row_bytes, (const int*)idx, (const Counters*)ctr,
@@ -176,21 +186,19 @@ int forward_impl(const Plan& pl, const void* X, const void* W, const int64_t* la
   fa.H = (int)pl.H;
   fa.V = (int)pl.V;
   fa.rows_pad = rows_pad;
-  fa.P = (int)pl.P;
-  fa.TT = (int)pl.TT;
   fa.VT = (int)pl.VT;
-  fa.nblocks = (int)pad8(pl.P * pl.TT);
   fa.ctr = ctr;
   fa.part = part;
   if (L.err == hipSuccess) L.err = allow_big_lds(k_fwd_lse<E>);
   {
     Timed t("k_fwd_lse", stream);
-    hipLaunchKernelGGL(k_fwd_lse<E>, dim3(fa.nblocks), dim3(kThreads), kLdsBytes, stream, fa);
+    hipLaunchKernelGGL(k_fwd_lse<E>, dim3((unsigned)pl.fwd_items), dim3(kThreads), kLdsBytes,
+                       stream, fa);
     L.check();
   }
   const int nb = (int)cdiv(pl.N, 256);
   hipLaunchKernelGGL(k_merge, dim3(nb), dim3(256), 0, stream, (const float2*)part,
-                     (int)pl.P, rows_pad, (const int*)rowpos, (const float*)zt,
+                     (const Counters*)ctr, (const int*)rowpos, (const float*)zt,
                      (int)pl.N, lse, bsum);
   L.check();
   hipLaunchKernelGGL(k_loss, dim3(1), dim3(256), 0, stream, (const float*)bsum, nb,
@@ -217,8 +225,8 @@ int backward_impl(const Plan& pl, const void* X, const void* W, const int64_t* l
   const int row_bytes = (int)(pl.H * E::kBytes);
 
   hipLaunchKernelGGL(k_prep, dim3(1), dim3(1024), 0, stream, labels, (int)B, (int)T,
-                     ignore_index, pl.V, shift, reduction, grad_scale, idx, tgt, rowpos,
-                     ctr, status);
+                     ignore_index, pl.V, shift, reduction, grad_scale, cu_count(),
+                     (int)pl.fwd_items, idx, tgt, rowpos, ctr, status);
   L.check();
   hipLaunchKernelGGL(k_gather, dim3((unsigned)cdiv(rows_pad, 4)), dim3(256), 0, stream,
                      (const char*)X, row_bytes, (const int*)idx, (const Counters*)ctr,

@@ -33,8 +33,9 @@ struct Counters {
   int n;         // valid rows
   int status;    // 0 or FLCE_ERR_LABEL_RANGE
   float c;       // gradient scale (backward)
-  int pad;
+  int fwd_p;     // forward: vocabulary ranges per token tile
 };
+
 
 constexpr int kStatusLabelRange = 8;
 
@@ -45,11 +46,12 @@ constexpr int kStatusLabelRange = 8;
 __global__ __launch_bounds__(1024) void k_prep(
     const int64_t* __restrict__ labels, int B, int T, int64_t ignore,
     int64_t V, int shift, int reduction, const float* __restrict__ grad_scale,
-    int* __restrict__ idx, int* __restrict__ tgt, int* __restrict__ rowpos,
+    int ncu, int max_items, int* __restrict__ idx, int* __restrict__ tgt, int* __restrict__ rowpos,
     Counters* __restrict__ ctr, int32_t* __restrict__ status_out) {
   __shared__ int wsum[16];
   __shared__ int base_s;
   __shared__ int bad_s;
+  __shared__ unsigned long long best_s;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int N = B * T;
   if (tid == 0) {
@@ -94,8 +96,26 @@ __global__ __launch_bounds__(1024) void k_prep(
     }
     __syncthreads();
   }
+  // Forward split: P vocabulary ranges per token tile, P * TTn items of
+  // about VT / P tiles each, at most max_items of them (P = 1 always fits).
+  // With the items running in waves of `ncu` workgroups the time is about
+  // waves(P) * ceil(VT / P) tiles; thread t prices P = t + 1 and the
+  // cheapest (then the smallest) P wins.
+  const int n = base_s;
+  const int64_t VT = (V + kTile - 1) / kTile;
+  const int64_t TTn = n > 0 ? (n + kTile - 1) / kTile : 1;
+  if (tid == 0) best_s = ~0ull;
+  __syncthreads();
+  {
+    const int64_t P = tid + 1;
+    if (P == 1 || (P <= VT && P * TTn <= max_items)) {
+      const int64_t waves = (P * TTn + ncu - 1) / ncu;
+      const int64_t per = (VT + P - 1) / P;
+      atomicMin(&best_s, (unsigned long long)(waves * per) * 2048ull + (unsigned long long)P);
+    }
+  }
+  __syncthreads();
   if (tid == 0) {
-    const int n = base_s;
     const int st = bad_s ? kStatusLabelRange : 0;
     const float gs = grad_scale ? *grad_scale : 1.0f;
     float c = reduction == 0 ? (n > 0 ? gs / (float)n : 0.0f) : gs;
@@ -103,6 +123,7 @@ __global__ __launch_bounds__(1024) void k_prep(
     ctr->n = n;
     ctr->status = st;
     ctr->c = c;
+    ctr->fwd_p = (int)(best_s & 2047ull);
     if (status_out) *status_out = st;
   }
 }
@@ -224,9 +245,9 @@ struct FwdArgs {
   const char* W;
   const char* Xc;
   int H, V, rows_pad;
-  int P, TT, VT, nblocks;
+  int VT;
   const Counters* ctr;
-  float2* part;      // [P][rows_pad] (m in log2 units, s)
+  float2* part;      // [item = p * TTn + tau][256 rows] (m in log2 units, s)
 };
 
 template <class E>
@@ -234,13 +255,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_fwd_lse(FwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem_[];
   lds_t* smem = (lds_t*)smem_;
-  const int item = xcd_item(blockIdx.x, a.nblocks);
-  if (item >= a.P * a.TT) return;
+  // the split k_prep chose: P ranges x TTn token tiles, handed out XCD by XCD
+  const int n = a.ctr->n, P = a.ctr->fwd_p;
+  const int TTn = (n + kTile - 1) / kTile;
+  const int nact = P * TTn, nact8 = (nact + 7) & ~7;
+  if ((int)blockIdx.x >= nact8) return;
+  const int item = xcd_item(blockIdx.x, nact8);
+  if (item >= nact) return;
   int p, tau;
-  grouped(item, a.P, a.TT, p, tau);
-  const int n = a.ctr->n;
-  if (tau * kTile >= n) return;
-  const int vt0 = (int)((int64_t)p * a.VT / a.P), vt1 = (int)((int64_t)(p + 1) * a.VT / a.P);
+  grouped(item, P, TTn, p, tau);
+  const int vt0 = (int)((int64_t)p * a.VT / P), vt1 = (int)((int64_t)(p + 1) * a.VT / P);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -288,7 +312,7 @@ void k_fwd_lse(FwdArgs a) {
   float M = -INFINITY, S = 0.f;
 #pragma unroll
   for (int q = 0; q < 4; ++q) lse_merge(M, S, st[(q * kTile + t) * 2], st[(q * kTile + t) * 2 + 1]);
-  a.part[(int64_t)p * a.rows_pad + tau * kTile + t] = make_float2(M, S);
+  a.part[((int64_t)p * TTn + tau) * kTile + t] = make_float2(M, S);
 }
 
 // ---------------------------------------------------------------------------
@@ -297,19 +321,21 @@ void k_fwd_lse(FwdArgs a) {
 // writes the fixed-order sum of its 256 row losses.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_merge(
-    const float2* __restrict__ part, int P, int rows_pad,
+    const float2* __restrict__ part, const Counters* __restrict__ ctr,
     const int* __restrict__ rowpos, const float* __restrict__ zt, int N,
     float* __restrict__ lse_out, float* __restrict__ blocksum) {
   __shared__ float red[256];
   const int i = blockIdx.x * 256 + threadIdx.x;
+  const int P = ctr->fwd_p, TTn = (ctr->n + kTile - 1) / kTile;
   float li = 0.f;
   if (i < N) {
     const int k = rowpos[i];
     float lse = 0.f;
     if (k >= 0) {
+      const float2* pk = part + (int64_t)(k / kTile) * kTile + k % kTile;
       float M = -INFINITY, S = 0.f;
       for (int p = 0; p < P; ++p) {
-        const float2 v = part[(int64_t)p * rows_pad + k];
+        const float2 v = pk[(int64_t)p * TTn * kTile];
         const float Mn = fmaxf(M, v.x);
         if (Mn == -INFINITY) continue;
         S = S * exp2f(M - Mn) + v.y * exp2f(v.x - Mn);

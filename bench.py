@@ -27,7 +27,10 @@ sys.path.insert(0, ROOT)
 BF16_PEAK = 2.5e15        # MI355X dense bf16 MFMA, FLOP/s
 F32_PEAK = 157.3e12       # MI355X dense fp32 MFMA, FLOP/s
 HBM_PEAK = 8.0e12         # MI355X HBM3E, B/s
-KERNELS = ("k_fwd_lse", "k_bwd_g", "k_bwd_dw", "k_bwd_dx")
+KERNELS = ("k_fwd_lse", "k_bwd")
+# MFMA contractions per step of each kernel, in units of 2 n H V flops: the
+# forward logits; the backward's recomputed logits, dX and dW
+GEMMS_PER_STEP = {"k_fwd_lse": 1, "k_bwd": 3}
 KERNEL_SOURCES = ("lm_head_linear_flce_amd/csrc/flce_tile.h",
                   "lm_head_linear_flce_amd/csrc/flce_kernels.h",
                   "lm_head_linear_flce_amd/csrc/flce_api.hip")
@@ -326,9 +329,10 @@ def main():
     t = step_ms / 1e3
     peak = BF16_PEAK if w.dtype == "bf16" else F32_PEAK
     pk = per_kernel[dom]
-    # algorithmic flops of one launch of the dominant kernel: 2 n H (vocab it covers)
-    vocab_per_launch = V / max(launches_per_step[dom], 1)
-    ach = 2.0 * n * H * vocab_per_launch / (pk["avg_launch_ms"] / 1e3)
+    # algorithmic flops of the dominant kernel per launch: its contractions'
+    # 2 n H V each per step, over its launches per step
+    flops_per_launch = GEMMS_PER_STEP[dom] * 2.0 * n * H * V / max(launches_per_step[dom], 1)
+    ach = flops_per_launch / (pk["avg_launch_ms"] / 1e3)
     result = {
         "metric": METRIC,
         "value": N / t,

@@ -79,8 +79,8 @@ extern "C" {
  * flce_backward need for this shape and dtype (one buffer serves both).
  * Host-only arithmetic, no HIP call.  The figure is the engine's whole extra
  * device memory: it grows linearly in N (per-row indices, a compacted copy of
- * the valid rows of X, an FP32 dX accumulator and a bounded slab of softmax
- * gradients covering a fixed vocabulary block), never with N*V.
+ * the valid rows of X, an FP32 dX accumulator and two bounded slabs of
+ * softmax gradients, each covering a fixed vocabulary block), never with N*V.
  *   B, T, H, V : problem sizes (B*T = N rows)
  *   dtype      : FLCE_DTYPE_*
  *   bytes      : out, host pointer
@@ -134,8 +134,8 @@ int flce_backward(const void* X, const void* W, const int64_t* labels,
 
 /*
  * flce_set_timing -- measurement hook for benchmarks and profilers.  While set,
- * every launch of the kernel named `kernel` ("k_fwd_lse", "k_bwd_g",
- * "k_bwd_dw" or "k_bwd_dx") made by flce_forward / flce_backward records
+ * every launch of the kernel named `kernel` ("k_fwd_lse", the forward GEMM,
+ * or "k_bwd", the backward GEMM launches) made by flce_forward / flce_backward records
  * events[2*i] on its stream right before the launch and events[2*i+1] right
  * after it, where i = *count, and then increments *count (a host int), until
  * *count reaches `capacity`.  `events` holds 2*capacity hipEvent_t handles

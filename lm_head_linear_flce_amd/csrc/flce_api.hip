@@ -14,7 +14,12 @@ namespace flce {
 namespace {
 
 constexpr int64_t kAlign = 256;
-constexpr int64_t kVocabBlock = 16384;          // backward vocabulary block
+#ifndef FLCE_SLAB_MIB
+#define FLCE_SLAB_MIB 256
+#endif
+// backward: both softmax-gradient slabs together hold at most this many bytes
+// (unless a single 256-wide vocabulary tile per row already needs more)
+constexpr int64_t kSlabBudget = (int64_t)FLCE_SLAB_MIB << 20;
 constexpr int64_t kMaxI32 = 0x7FFFFFFFll;
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -51,10 +56,10 @@ int make_plan(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, Plan* p) {
   // forward: the split itself is chosen on the device (k_prep), once the
   // number of valid rows is known; this bounds its item count and partials
   q.fwd_items = std::max<int64_t>(2048, q.TT);
-  // backward: a fixed vocabulary block, so the softmax-gradient slab holds
-  // kVocabBlock values per row whatever V is (smaller only for very many rows,
-  // to keep 32-bit offsets)
-  int64_t vb = std::min<int64_t>(kVocabBlock, kMaxI32 / (q.rows_pad * q.es));
+  // backward: the vocabulary block is as wide as the slab budget allows for
+  // this many rows, whatever V is (and narrow enough for 32-bit offsets)
+  int64_t vb = std::min<int64_t>(kSlabBudget / (2 * q.rows_pad * q.es),
+                                 kMaxI32 / (q.rows_pad * q.es));
   vb = std::max<int64_t>(kTile, vb / kTile * kTile);
   vb = std::min<int64_t>(vb, round_up(V, kTile));
   q.Vb = vb;
@@ -81,7 +86,7 @@ int make_plan(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, Plan* p) {
   const int64_t fwd_end = off;
   off = common;
   q.o_lse2 = take(4 * q.rows_pad);
-  q.o_g = take(q.rows_pad * q.Vb * q.es);
+  q.o_g = take(2 * q.rows_pad * q.Vb * q.es);   // two slabs, alternating blocks
   q.o_dx32 = take(4 * q.rows_pad * H);
   const int64_t bwd_end = off;
   q.total = std::max(fwd_end, bwd_end);
@@ -249,42 +254,35 @@ int backward_impl(const Plan& pl, const void* X, const void* W, const int64_t* l
   a.TT = (int)pl.TT;
   a.HT = (int)cdiv(pl.H, kTile);
   a.dw_f32 = grad_f32;
-  if (L.err == hipSuccess) L.err = allow_big_lds(k_bwd_g<E>);
-  if (L.err == hipSuccess) L.err = allow_big_lds(k_bwd_dw<E>);
-  if (L.err == hipSuccess) L.err = allow_big_lds(k_bwd_dx<E>);
-  for (int64_t v0 = 0; v0 < pl.V && L.err == hipSuccess; v0 += pl.Vb) {
-    a.v0 = (int)v0;
-    a.vb = (int)std::min<int64_t>(pl.Vb, pl.V - v0);
-    a.VTb = (int)cdiv(a.vb, kTile);
-    // G slab
-    a.nblocks = (int)pad8((int64_t)a.VTb * a.TT);
-    a.splits = 1;
+  a.v0 = a.vb = a.VTb = 0;
+  const int64_t slab = pl.rows_pad * pl.Vb * pl.es;
+  auto block = [&](int64_t b) {
+    BwdArgs r = a;
+    r.v0 = (int)(b * pl.Vb);
+    r.vb = (int)std::min<int64_t>(pl.Vb, pl.V - r.v0);
+    r.VTb = (int)cdiv(r.vb, kTile);
+    r.G = g + (b & 1) * slab;
+    return r;
+  };
+  if (L.err == hipSuccess) L.err = allow_big_lds(k_bwd<E>);
+  // launch b + 1 runs the dX / dW tiles of block b and the G tiles of block
+  // b + 1 (dX first: its tiles are the longest)
+  const int64_t nblk = cdiv(pl.V, pl.Vb);
+  for (int64_t b = -1; b < nblk && L.err == hipSuccess; ++b) {
+    const BwdArgs cur = b >= 0 ? block(b) : a;
+    const BwdArgs nxt = b + 1 < nblk ? block(b + 1) : a;
+    const int nb_dx = b >= 0 ? (int)pad8((int64_t)a.HT * a.TT) : 0;
+    const int nb_dw = b >= 0 ? (int)pad8((int64_t)a.HT * cur.VTb) : 0;
+    const int nb_g = b + 1 < nblk ? (int)pad8((int64_t)nxt.VTb * a.TT) : 0;
     {
-      Timed t("k_bwd_g", stream);
-      hipLaunchKernelGGL(k_bwd_g<E>, dim3(a.nblocks), dim3(kThreads), kLdsBytes, stream, a);
+      Timed t("k_bwd", stream);
+      hipLaunchKernelGGL(k_bwd<E>, dim3((unsigned)(nb_dx + nb_dw + nb_g)), dim3(kThreads),
+                         kLdsBytes, stream, cur, nxt, nb_dx, nb_dw, nb_g);
       L.check();
     }
-    hipLaunchKernelGGL(k_fixup<E>, dim3((unsigned)cdiv(rows_pad, 256)), dim3(256), 0,
-                       stream, a);
-    L.check();
-    // dW rows of the block
-    a.nblocks = (int)pad8((int64_t)a.HT * a.VTb);
-    {
-      Timed t("k_bwd_dw", stream);
-      hipLaunchKernelGGL(k_bwd_dw<E>, dim3(a.nblocks), dim3(kThreads), kLdsBytes, stream, a);
-      L.check();
-    }
-    // dX accumulation, split over the block's vocabulary so the launch fills
-    // the machine (about 2 waves of 256 workgroups at least)
-    const int64_t tiles = (int64_t)a.HT * a.TT;
-    const int64_t ksteps = cdiv(a.vb, E::kKStep);
-    int64_t sp = std::max<int64_t>(1, cdiv(512, tiles));
-    sp = std::min<int64_t>(sp, std::max<int64_t>(1, ksteps / 16));
-    a.splits = (int)sp;
-    a.nblocks = (int)pad8(sp * tiles);
-    {
-      Timed t("k_bwd_dx", stream);
-      hipLaunchKernelGGL(k_bwd_dx<E>, dim3(a.nblocks), dim3(kThreads), kLdsBytes, stream, a);
+    if (b + 1 < nblk) {
+      hipLaunchKernelGGL(k_fixup<E>, dim3((unsigned)cdiv(rows_pad, 256)), dim3(256), 0,
+                         stream, nxt);
       L.check();
     }
   }

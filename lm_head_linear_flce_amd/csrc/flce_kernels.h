@@ -13,13 +13,14 @@
 //               over a range of vocabulary tiles -> (m, s) partials
 //   k_merge     lse = merge of the partials, loss_i = lse_i - zt_i, block sums
 //   k_loss      fixed-order sum of the block sums -> loss
-// Backward (dX, dW), per vocabulary block [v0, v0 + vb):
-//   k_bwd_g     logits recomputed on MFMA, G = c * exp(z - lse) stored (bf16 or
-//               fp32) into a bounded [rows x block] slab
+// Backward (dX, dW), over vocabulary blocks [v0, v0 + vb), as tiles of k_bwd:
+//   G tiles     logits recomputed on MFMA, G = c * exp(z - lse) stored (bf16 or
+//               fp32) into a bounded [rows x block] slab (two, alternating)
 //   k_fixup     G[k, y_k - v0] -= c for targets inside the block
-//   k_bwd_dw    dW[v0 + m, :] = sum_k G[k, m] Xc[k, :]   (complete, stored once)
-//   k_bwd_dx    dX32[k, :] += sum_m G[k, m] W[v0 + m, :] (FP32, split over m)
-// then k_dx_final rounds dX32 once and scatters it to the original rows.
+//   dW tiles    dW[v0 + m, :] = sum_k G[k, m] Xc[k, :]   (complete, stored once)
+//   dX tiles    dX32[k, :] += sum_m G[k, m] W[v0 + m, :] (FP32)
+// one launch runs the dX and dW tiles of block b with the G tiles of block
+// b + 1; k_dx_final rounds dX32 once and scatters it to the original rows.
 #pragma once
 
 #include "flce_tile.h"
@@ -379,12 +380,18 @@ __global__ __launch_bounds__(256) void k_loss(
 }
 
 // ---------------------------------------------------------------------------
-// Backward GEMM kernels
+// Backward GEMM tiles.  One launch of k_bwd runs three kinds of 256 x 256
+// MFMA tiles, one per workgroup, longest first, so that the last wave of one
+// kind is filled by the next instead of leaving compute units idle:
+//   dX tiles of vocabulary block b     dX32[k, :] += G_b[k, :] W_b     (K = block)
+//   dW tiles of block b                dW_b = G_b^T Xc                 (K = rows)
+//   G tiles of block b + 1             G_{b+1} = c exp(Z - lse)        (K = H)
+// Blocks b and b + 1 use the two halves of the softmax-gradient slab.
 // ---------------------------------------------------------------------------
 struct BwdArgs {
   const char* W;       // [V, H]
   const char* Xc;      // [rows_pad, H] compacted valid rows
-  char* G;             // [rows_pad, Vb] softmax-gradient slab
+  char* G;             // [rows_pad, Vb] this block's softmax-gradient slab
   const float* lse2;   // [rows_pad] lse * log2(e)
   const int* tgt;      // [n]
   float* dx32;         // [rows_pad, H]
@@ -392,8 +399,7 @@ struct BwdArgs {
   const Counters* ctr;
   int H, V, rows_pad, Vb;
   int v0, vb;          // block start and width
-  int TT, HT, VTb, nblocks;
-  int splits;          // dX: K-splits of the block
+  int TT, HT, VTb;     // token tiles (bound), hidden tiles, block vocab tiles
   int dw_f32;          // dW written as fp32 (else bf16)
 };
 
@@ -438,14 +444,11 @@ __device__ __forceinline__ void g_store(const BwdArgs& a, const f32x16 (&acc)[4]
   }
 }
 
-// G = c * 2^(z*log2e - lse2) on the tile (vocab rows x token columns); zero
-// outside the vocabulary and for padding rows.  Stored as G[token][vocab].
+// G tile (vocabulary tile vt of the block x token tile tau): the logits are
+// recomputed (A = W rows, B = Xc rows, K = H) and turned into G on the way
+// out; zero outside the vocabulary and on padding rows.
 template <class E>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void k_bwd_g(BwdArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char smem_[];
-  lds_t* smem = (lds_t*)smem_;
-  const int item = xcd_item(blockIdx.x, a.nblocks);
+__device__ __forceinline__ void g_tile(const BwdArgs& a, int item, lds_t* smem) {
   if (item >= a.VTb * a.TT) return;
   int vt, tau;
   grouped(item, a.VTb, a.TT, vt, tau);
@@ -469,8 +472,7 @@ void k_bwd_g(BwdArgs a) {
   B.kbytes = ldb;
   f32x16 acc[4][4];
   zero_acc(acc);
-  gemm_tile<E, LoadDirect, LoadDirect>(A, B, steps, smem, wm, wn,
-                                         acc);
+  gemm_tile<E, LoadDirect, LoadDirect>(A, B, steps, smem, wm, wn, acc);
 
   const int vlim = a.V - vbase;
   if (vlim >= kTile && (tau + 1) * kTile <= n)
@@ -480,7 +482,7 @@ void k_bwd_g(BwdArgs a) {
                      n - tau * kTile);
 }
 
-// G[k, y_k - v0] -= c for the valid rows whose target lies in the block.
+// The one-hot part of G: G[k, y_k - v0] -= c for targets inside the block.
 template <class E>
 __global__ __launch_bounds__(256) void k_fixup(BwdArgs a) {
   const int k = blockIdx.x * 256 + threadIdx.x;
@@ -498,39 +500,45 @@ __global__ __launch_bounds__(256) void k_fixup(BwdArgs a) {
   }
 }
 
-// dW rows of one tile in the output dtype.  kMasked: rows with
-// (32i + 8(r/4) + r%4) >= mlim_lane lie past the block, columns >= hlim past H.
+// dW tile in the output dtype: accumulator rows are hidden indices (4
+// consecutive per lane and register group), columns vocabulary entries of the
+// block.  kMasked: columns >= mlim lie past the block, rows >= hlim past H
+// (H % 8 == 0, so a group of 4 is either inside or outside).
 template <bool kMasked>
 __device__ __forceinline__ void dw_store(const BwdArgs& a, const f32x16 (&acc)[4][4],
                                          int vt, int ht, int wm, int wn, int lane,
-                                         int mlim_lane, int hlim) {
+                                         int mlim, int hlim) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int hc = acc_col(wn, j, lane);
-    if (kMasked && hc >= hlim) continue;
-    const int h = ht * kTile + hc;
+    const int mc = acc_col(wn, j, lane);
+    if (kMasked && mc >= mlim) continue;
+    const int64_t row = (int64_t)(a.v0 + vt * kTile + mc) * a.H + ht * kTile;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        if (kMasked && 32 * i + 8 * (r >> 2) + (r & 3) >= mlim_lane) continue;
-        const int m = vt * kTile + acc_row(wm, i, r, lane);
-        const int64_t e = (int64_t)(a.v0 + m) * a.H + h;
-        if (a.dw_f32) ((float*)a.dW)[e] = acc[i][j][r];
-        else ((uint16_t*)a.dW)[e] = (uint16_t)f2bf(acc[i][j][r]);
+      for (int g = 0; g < 4; ++g) {
+        const int hc = acc_row(wm, i, 4 * g, lane);
+        if (kMasked && hc >= hlim) continue;
+        const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                         acc[i][j][4 * g + 3]};
+        if (a.dw_f32) {
+          *(f32x4*)((float*)a.dW + row + hc) = v;
+        } else {
+          i32x2 pk;
+          pk[0] = (int)(f2bf(v[0]) | (f2bf(v[1]) << 16));
+          pk[1] = (int)(f2bf(v[2]) | (f2bf(v[3]) << 16));
+          *(i32x2*)((uint16_t*)a.dW + row + hc) = pk;
+        }
       }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// dW[v0 + m, h] = sum_k G[k, m] Xc[k, h]: A = G (K = rows outer), B = Xc
-// (K = rows outer); K runs over the valid rows rounded up to one step.
+// dW[v0 + m, h] = sum_k Xc[k, h] G[k, m] for one (hidden tile, vocabulary
+// tile) of the block: A = Xc, B = G, both stored with K (rows) outer; K runs
+// over the valid rows rounded up to one step (G and Xc are zero past n).
 template <class E>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void k_bwd_dw(BwdArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char smem_[];
-  lds_t* smem = (lds_t*)smem_;
-  const int item = xcd_item(blockIdx.x, a.nblocks);
+__device__ __forceinline__ void dw_tile(const BwdArgs& a, int item, lds_t* smem) {
   if (item >= a.HT * a.VTb) return;
   int ht, vt;
   grouped(item, a.HT, a.VTb, ht, vt);
@@ -541,91 +549,119 @@ void k_bwd_dw(BwdArgs a) {
   const int steps = (n + E::kKStep - 1) / E::kKStep;
 
   Opnd A, B;
-  A.base = a.G + (int64_t)vt * kTile * es;
-  A.bytes = (int64_t)a.rows_pad * a.Vb * es - (int64_t)vt * kTile * es;
-  A.ldb = a.Vb * es;
+  A.base = a.Xc + (int64_t)ht * kTile * es;
+  A.bytes = (int64_t)a.rows_pad * a.H * es - (int64_t)ht * kTile * es;
+  A.ldb = a.H * es;
   A.kbytes = 0;
-  B.base = a.Xc + (int64_t)ht * kTile * es;
-  B.bytes = (int64_t)a.rows_pad * a.H * es - (int64_t)ht * kTile * es;
-  B.ldb = a.H * es;
+  B.base = a.G + (int64_t)vt * kTile * es;
+  B.bytes = (int64_t)a.rows_pad * a.Vb * es - (int64_t)vt * kTile * es;
+  B.ldb = a.Vb * es;
   B.kbytes = 0;
   f32x16 acc[4][4];
   zero_acc(acc);
   gemm_tile<E, LoadMN<E>, LoadMN<E>>(A, B, steps, smem, wm, wn, acc);
 
   const int mlim = a.vb - vt * kTile, hlim = a.H - ht * kTile;
-  if (mlim >= kTile && hlim >= kTile)
-    dw_store<false>(a, acc, vt, ht, wm, wn, lane, 0, 0);
-  else
-    dw_store<true>(a, acc, vt, ht, wm, wn, lane, mlim - wm * 128 - 4 * (lane >> 5),
-                   hlim);
+  if (mlim >= kTile && hlim >= kTile) dw_store<false>(a, acc, vt, ht, wm, wn, lane, 0, 0);
+  else dw_store<true>(a, acc, vt, ht, wm, wn, lane, mlim, hlim);
 }
 
+// dX32 += tile, read-modify-write: each (token tile, hidden tile) belongs to
+// one workgroup of a launch, and launches are ordered on the stream.
+// Accumulator rows are hidden indices, columns tokens; token columns >= nlim
+// (padding) and hidden rows >= hlim are skipped.
 template <bool kMasked>
 __device__ __forceinline__ void dx_add(const BwdArgs& a, const f32x16 (&acc)[4][4],
                                        int tau, int ht, int wm, int wn, int lane,
-                                       int hlim) {
+                                       int nlim, int hlim) {
   const rsrc_t xr = make_rsrc(a.dx32, (int64_t)a.rows_pad * a.H * 4);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int hc = acc_col(wn, j, lane);
-    if (kMasked && hc >= hlim) continue;
-    const int h = ht * kTile + hc;
+    const int tcol = acc_col(wn, j, lane);
+    if (kMasked && tcol >= nlim) continue;
+    const int row = ((tau * kTile + tcol) * a.H + ht * kTile) * 4;
+    f32x4 old[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int k = tau * kTile + acc_row(wm, i, r, lane);
-        __builtin_amdgcn_raw_ptr_buffer_atomic_fadd_f32(acc[i][j][r], xr,
-                                                        (k * a.H + h) * 4, 0, 0);
+      for (int g = 0; g < 4; ++g) {
+        const int hc = acc_row(wm, i, 4 * g, lane);
+        old[i][g] = (kMasked && hc >= hlim)
+                        ? f32x4{0.f, 0.f, 0.f, 0.f}
+                        : __builtin_bit_cast(f32x4, bload128(xr, row + hc * 4));
+      }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int hc = acc_row(wm, i, 4 * g, lane);
+        if (kMasked && hc >= hlim) continue;
+        const f32x4 v = {old[i][g][0] + acc[i][j][4 * g], old[i][g][1] + acc[i][j][4 * g + 1],
+                         old[i][g][2] + acc[i][j][4 * g + 2],
+                         old[i][g][3] + acc[i][j][4 * g + 3]};
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), xr, row + hc * 4,
+                                               0, 0);
       }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// dX32[k, h] += sum_m G[k, m] W[v0 + m, h] over one K-split of the block.
+// dX32[k, h] += sum_m W[v0 + m, h] G[k, m] over the whole block for one
+// (hidden tile, token tile): A = W (K = vocabulary rows outer), B = G rows
+// (K contiguous).  Past the block's end G is zero (last block) or the step
+// count stops at the block (others).
 template <class E>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void k_bwd_dx(BwdArgs a) {
-  extern __shared__ __attribute__((aligned(16))) char smem_[];
-  lds_t* smem = (lds_t*)smem_;
-  const int item = xcd_item(blockIdx.x, a.nblocks);
-  if (item >= a.splits * a.HT * a.TT) return;
-  int sh, tau;   // sh = split * HT + ht
-  grouped(item, a.splits * a.HT, a.TT, sh, tau);
-  const int sp = sh / a.HT, ht = sh - sp * a.HT;
+__device__ __forceinline__ void dx_tile(const BwdArgs& a, int item, lds_t* smem) {
+  if (item >= a.HT * a.TT) return;
+  int ht, tau;
+  grouped(item, a.HT, a.TT, ht, tau);
   const int n = a.ctr->n;
   if (tau * kTile >= n) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int es = E::kBytes;
-  // the block's K range [0, vb_pad) split into `splits` whole steps
-  const int ksteps_total = (a.vb + E::kKStep - 1) / E::kKStep;
-  const int s0 = (int)((int64_t)sp * ksteps_total / a.splits);
-  const int s1 = (int)((int64_t)(sp + 1) * ksteps_total / a.splits);
-  const int k0 = s0 * E::kKStep;
+  const int steps = (a.vb + E::kKStep - 1) / E::kKStep;
 
   Opnd A, B;
-  A.base = a.G + ((int64_t)tau * kTile * a.Vb + k0) * es;
-  A.bytes = (int64_t)a.rows_pad * a.Vb * es - ((int64_t)tau * kTile * a.Vb + k0) * es;
-  A.ldb = a.Vb * es;
-  A.kbytes = (a.Vb - k0) * es;
-  B.base = a.W + ((int64_t)(a.v0 + k0) * a.H + (int64_t)ht * kTile) * es;
-  B.bytes = (int64_t)a.V * a.H * es - ((int64_t)(a.v0 + k0) * a.H + (int64_t)ht * kTile) * es;
-  B.ldb = a.H * es;
-  B.kbytes = 0;
+  A.base = a.W + ((int64_t)a.v0 * a.H + (int64_t)ht * kTile) * es;
+  A.bytes = (int64_t)a.V * a.H * es - ((int64_t)a.v0 * a.H + (int64_t)ht * kTile) * es;
+  A.ldb = a.H * es;
+  A.kbytes = 0;
+  B.base = a.G + (int64_t)tau * kTile * a.Vb * es;
+  B.bytes = (int64_t)a.rows_pad * a.Vb * es - (int64_t)tau * kTile * a.Vb * es;
+  B.ldb = a.Vb * es;
+  B.kbytes = a.Vb * es;
   f32x16 acc[4][4];
   zero_acc(acc);
-  gemm_tile<E, LoadDirect, LoadMN<E>>(A, B, s1 - s0, smem, wm, wn, acc);
+  gemm_tile<E, LoadMN<E>, LoadDirect>(A, B, steps, smem, wm, wn, acc);
 
-  // rows >= n hold zeros (G is 0 there) and stay inside the accumulator;
-  // columns past H would land in the next row and are skipped
-  const int hlim = a.H - ht * kTile;
-  if (hlim >= kTile) dx_add<false>(a, acc, tau, ht, wm, wn, lane, 0);
-  else dx_add<true>(a, acc, tau, ht, wm, wn, lane, hlim);
+  const int nlim = n - tau * kTile, hlim = a.H - ht * kTile;
+  if (nlim >= kTile && hlim >= kTile) dx_add<false>(a, acc, tau, ht, wm, wn, lane, 0, 0);
+  else dx_add<true>(a, acc, tau, ht, wm, wn, lane, nlim, hlim);
 }
 
-// dX[i] = round(dX32[rowpos[i]]) for valid rows, 0 for the others.
+// One backward launch: nb_dx dX tiles and nb_dw dW tiles of block `cur`,
+// then nb_g G tiles of block `nxt` (each count a multiple of 8, so every
+// kind is spread over the XCDs on its own).
+template <class E>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_bwd(BwdArgs cur, BwdArgs nxt, int nb_dx, int nb_dw, int nb_g) {
+  extern __shared__ __attribute__((aligned(16))) char smem_[];
+  lds_t* smem = (lds_t*)smem_;
+  int b = blockIdx.x;
+  if (b < nb_dx) {
+    dx_tile<E>(cur, xcd_item(b, nb_dx), smem);
+    return;
+  }
+  b -= nb_dx;
+  if (b < nb_dw) {
+    dw_tile<E>(cur, xcd_item(b, nb_dw), smem);
+    return;
+  }
+  b -= nb_dw;
+  if (b < nb_g) g_tile<E>(nxt, xcd_item(b, nb_g), smem);
+}
+
 __global__ __launch_bounds__(256) void k_dx_final(
     const float* __restrict__ dx32, const int* __restrict__ rowpos, int N, int H,
     char* __restrict__ dX, int out_f32) {

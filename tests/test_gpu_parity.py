@@ -164,7 +164,7 @@ def test_zero_weight_gives_log_vocab():
 
 
 def test_peak_memory_never_holds_logits():
-    w = synth.workload("long_context", T=4096, H=128, V=131072, seed=151)
+    w = synth.workload("long_context", T=4096, H=128, V=262144, seed=151)
     X, W, lab = to_device(w)
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()

@@ -503,31 +503,37 @@ __global__ __launch_bounds__(256) void k_fixup(BwdArgs a) {
 // dW tile in the output dtype: accumulator rows are hidden indices (4
 // consecutive per lane and register group), columns vocabulary entries of the
 // block.  kMasked: columns >= mlim lie past the block, rows >= hlim past H
-// (H % 8 == 0, so a group of 4 is either inside or outside).
+// (H % 8 == 0, so a group of 4 is either inside or outside).  Branch-free:
+// a masked lane stores to an offset past the descriptor's range, which the
+// hardware drops (the descriptor covers the tile's 256 rows, < 2^31 bytes).
 template <bool kMasked>
 __device__ __forceinline__ void dw_store(const BwdArgs& a, const f32x16 (&acc)[4][4],
                                          int vt, int ht, int wm, int wn, int lane,
                                          int mlim, int hlim) {
+  const int es = a.dw_f32 ? 4 : 2;
+  const int64_t row0 = (int64_t)(a.v0 + vt * kTile) * a.H + (int64_t)ht * kTile;
+  const int64_t left = ((int64_t)a.V * a.H - row0) * es;
+  const int64_t span = (int64_t)kTile * a.H * es;
+  const rsrc_t wr = make_rsrc((char*)a.dW + row0 * es, left < span ? left : span);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int mc = acc_col(wn, j, lane);
-    if (kMasked && mc >= mlim) continue;
-    const int64_t row = (int64_t)(a.v0 + vt * kTile + mc) * a.H + ht * kTile;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int hc = acc_row(wm, i, 4 * g, lane);
-        if (kMasked && hc >= hlim) continue;
+        const bool ok = !kMasked || (mc < mlim && hc < hlim);
+        const int off = ok ? (mc * a.H + hc) * es : (int)0x80000000u;
         const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
                          acc[i][j][4 * g + 3]};
         if (a.dw_f32) {
-          *(f32x4*)((float*)a.dW + row + hc) = v;
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), wr, off, 0, 0);
         } else {
           i32x2 pk;
           pk[0] = (int)(f2bf(v[0]) | (f2bf(v[1]) << 16));
           pk[1] = (int)(f2bf(v[2]) | (f2bf(v[3]) << 16));
-          *(i32x2*)((uint16_t*)a.dW + row + hc) = pk;
+          __builtin_amdgcn_raw_buffer_store_b64(pk, wr, off, 0, 0);
         }
       }
     __builtin_amdgcn_sched_barrier(0);
@@ -569,7 +575,9 @@ __device__ __forceinline__ void dw_tile(const BwdArgs& a, int item, lds_t* smem)
 // dX32 += tile, read-modify-write: each (token tile, hidden tile) belongs to
 // one workgroup of a launch, and launches are ordered on the stream.
 // Accumulator rows are hidden indices, columns tokens; token columns >= nlim
-// (padding) and hidden rows >= hlim are skipped.
+// (padding) and hidden rows >= hlim are skipped.  Branch-free: masked lanes
+// load and store at an offset past the buffer (rows_pad * H * 4 < 2^31), so
+// the load returns zeros and the store is dropped.
 template <bool kMasked>
 __device__ __forceinline__ void dx_add(const BwdArgs& a, const f32x16 (&acc)[4][4],
                                        int tau, int ht, int wm, int wn, int lane,
@@ -578,29 +586,27 @@ __device__ __forceinline__ void dx_add(const BwdArgs& a, const f32x16 (&acc)[4][
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int tcol = acc_col(wn, j, lane);
-    if (kMasked && tcol >= nlim) continue;
     const int row = ((tau * kTile + tcol) * a.H + ht * kTile) * 4;
+    int off[4][4];
     f32x4 old[4][4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int hc = acc_row(wm, i, 4 * g, lane);
-        old[i][g] = (kMasked && hc >= hlim)
-                        ? f32x4{0.f, 0.f, 0.f, 0.f}
-                        : __builtin_bit_cast(f32x4, bload128(xr, row + hc * 4));
+        const bool ok = !kMasked || (tcol < nlim && hc < hlim);
+        off[i][g] = ok ? row + hc * 4 : (int)0x80000000u;
+        old[i][g] = __builtin_bit_cast(f32x4, bload128(xr, off[i][g]));
       }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int hc = acc_row(wm, i, 4 * g, lane);
-        if (kMasked && hc >= hlim) continue;
         const f32x4 v = {old[i][g][0] + acc[i][j][4 * g], old[i][g][1] + acc[i][j][4 * g + 1],
                          old[i][g][2] + acc[i][j][4 * g + 2],
                          old[i][g][3] + acc[i][j][4 * g + 3]};
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), xr, row + hc * 4,
-                                               0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), xr, off[i][g], 0,
+                                               0);
       }
     __builtin_amdgcn_sched_barrier(0);
   }

@@ -219,19 +219,19 @@ __device__ __forceinline__ void lse_update(const f32x16 (&acc)[4][4], float (&m)
       for (int r = 0; r < 16; ++r)
         if (!kMasked || 32 * i + 8 * (r >> 2) + (r & 3) < lim)
           tmax = fmaxf(tmax, acc[i][j][r]);
-    if (tmax != -INFINITY) {
-      const float M = fmaxf(m[j], tmax * kLog2e);
-      float sum = 0.f;
+    // branch-free: with nothing seen yet (M = -inf) the sums stay 0
+    const float M = fmaxf(m[j], tmax * kLog2e);
+    const float Ms = M == -INFINITY ? 0.f : M;
+    float sum = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = __builtin_amdgcn_exp2f(fmaf(acc[i][j][r], kLog2e, -M));
-          if (!kMasked || 32 * i + 8 * (r >> 2) + (r & 3) < lim) sum += e;
-        }
-      s[j] = s[j] * __builtin_amdgcn_exp2f(m[j] - M) + sum;
-      m[j] = M;
-    }
+      for (int r = 0; r < 16; ++r) {
+        const float e = __builtin_amdgcn_exp2f(fmaf(acc[i][j][r], kLog2e, -Ms));
+        sum += (!kMasked || 32 * i + 8 * (r >> 2) + (r & 3) < lim) ? e : 0.f;
+      }
+    s[j] = s[j] * __builtin_amdgcn_exp2f(m[j] - Ms) + sum;
+    m[j] = M;
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -406,16 +406,16 @@ struct BwdArgs {
 // G = c * 2^(z*log2e - lse2) for one tile, stored as G[token][vocab].
 // kMasked: tile rows with (32i + 8g + q) >= vlim_lane lie past the vocabulary
 // end and token columns >= nlim are padding; both become 0.
+// l2[j]: lse2 of the lane's token column j, loaded before the tile's K loop.
 template <class E, bool kMasked>
 __device__ __forceinline__ void g_store(const BwdArgs& a, const f32x16 (&acc)[4][4],
-                                        float c, int vt, int tau, int wm, int wn,
-                                        int lane, int vlim_lane, int nlim) {
+                                        const float (&l2)[4], float c, int vt, int tau,
+                                        int wm, int wn, int lane, int vlim_lane, int nlim) {
   const rsrc_t gr = make_rsrc(a.G, (int64_t)a.rows_pad * a.Vb * E::kBytes);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int tcol = acc_col(wn, j, lane);
     const int tok = tau * kTile + tcol;
-    const float l2 = a.lse2[tok];
     const bool tok_ok = !kMasked || tcol < nlim;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -425,14 +425,14 @@ __device__ __forceinline__ void g_store(const BwdArgs& a, const f32x16 (&acc)[4]
         float v[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          v[q] = c * __builtin_amdgcn_exp2f(fmaf(acc[i][j][4 * g + q], kLog2e, -l2));
+          v[q] = c * __builtin_amdgcn_exp2f(fmaf(acc[i][j][4 * g + q], kLog2e, -l2[j]));
           if (kMasked && !(tok_ok && 32 * i + 8 * g + q < vlim_lane)) v[q] = 0.f;
         }
         const int off = (tok * a.Vb + vt * kTile + row0) * E::kBytes;
         if constexpr (E::kBytes == 2) {
           i32x2 pk;
-          pk[0] = (int)(f2bf(v[0]) | (f2bf(v[1]) << 16));
-          pk[1] = (int)(f2bf(v[2]) | (f2bf(v[3]) << 16));
+          pk[0] = pack_bf16(v[0], v[1]);
+          pk[1] = pack_bf16(v[2], v[3]);
           __builtin_amdgcn_raw_buffer_store_b64(pk, gr, off, 0, 0);
         } else {
           const f32x4 fv = {v[0], v[1], v[2], v[3]};
@@ -470,16 +470,20 @@ __device__ __forceinline__ void g_tile(const BwdArgs& a, int item, lds_t* smem) 
   B.bytes = (int64_t)(a.rows_pad - tau * kTile) * ldb;
   B.ldb = ldb;
   B.kbytes = ldb;
+  // the rows' lse, fetched now so the epilogue does not wait on it
+  float l2[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) l2[j] = a.lse2[tau * kTile + acc_col(wn, j, lane)];
   f32x16 acc[4][4];
   zero_acc(acc);
   gemm_tile<E, LoadDirect, LoadDirect>(A, B, steps, smem, wm, wn, acc);
 
   const int vlim = a.V - vbase;
   if (vlim >= kTile && (tau + 1) * kTile <= n)
-    g_store<E, false>(a, acc, c, vt, tau, wm, wn, lane, 0, 0);
+    g_store<E, false>(a, acc, l2, c, vt, tau, wm, wn, lane, 0, 0);
   else
-    g_store<E, true>(a, acc, c, vt, tau, wm, wn, lane, vlim - wm * 128 - 4 * (lane >> 5),
-                     n - tau * kTile);
+    g_store<E, true>(a, acc, l2, c, vt, tau, wm, wn, lane,
+                     vlim - wm * 128 - 4 * (lane >> 5), n - tau * kTile);
 }
 
 // The one-hot part of G: G[k, y_k - v0] -= c for targets inside the block.
@@ -531,8 +535,8 @@ __device__ __forceinline__ void dw_store(const BwdArgs& a, const f32x16 (&acc)[4
           __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), wr, off, 0, 0);
         } else {
           i32x2 pk;
-          pk[0] = (int)(f2bf(v[0]) | (f2bf(v[1]) << 16));
-          pk[1] = (int)(f2bf(v[2]) | (f2bf(v[3]) << 16));
+          pk[0] = pack_bf16(v[0], v[1]);
+          pk[1] = pack_bf16(v[2], v[3]);
           __builtin_amdgcn_raw_buffer_store_b64(pk, wr, off, 0, 0);
         }
       }
@@ -583,30 +587,35 @@ __device__ __forceinline__ void dx_add(const BwdArgs& a, const f32x16 (&acc)[4][
                                        int tau, int ht, int wm, int wn, int lane,
                                        int nlim, int hlim) {
   const rsrc_t xr = make_rsrc(a.dx32, (int64_t)a.rows_pad * a.H * 4);
+  auto offset = [&](int j, int i, int g) {
+    const int tcol = acc_col(wn, j, lane), hc = acc_row(wm, i, 4 * g, lane);
+    const bool ok = !kMasked || (tcol < nlim && hc < hlim);
+    return ok ? ((tau * kTile + tcol) * a.H + ht * kTile + hc) * 4 : (int)0x80000000u;
+  };
+  // the loads of column j + 1 are in flight while column j is added and stored
+  f32x4 old[2][4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) old[0][i][g] = __builtin_bit_cast(f32x4, bload128(xr, offset(0, i, g)));
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int tcol = acc_col(wn, j, lane);
-    const int row = ((tau * kTile + tcol) * a.H + ht * kTile) * 4;
-    int off[4][4];
-    f32x4 old[4][4];
+    if (j + 1 < 4) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          old[(j + 1) & 1][i][g] = __builtin_bit_cast(f32x4, bload128(xr, offset(j + 1, i, g)));
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        const int hc = acc_row(wm, i, 4 * g, lane);
-        const bool ok = !kMasked || (tcol < nlim && hc < hlim);
-        off[i][g] = ok ? row + hc * 4 : (int)0x80000000u;
-        old[i][g] = __builtin_bit_cast(f32x4, bload128(xr, off[i][g]));
-      }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4 v = {old[i][g][0] + acc[i][j][4 * g], old[i][g][1] + acc[i][j][4 * g + 1],
-                         old[i][g][2] + acc[i][j][4 * g + 2],
-                         old[i][g][3] + acc[i][j][4 * g + 3]};
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), xr, off[i][g], 0,
-                                               0);
+        const f32x4& o = old[j & 1][i][g];
+        const f32x4 v = {o[0] + acc[i][j][4 * g], o[1] + acc[i][j][4 * g + 1],
+                         o[2] + acc[i][j][4 * g + 2], o[3] + acc[i][j][4 * g + 3]};
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), xr, offset(j, i, g),
+                                               0, 0);
       }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -683,8 +692,8 @@ __global__ __launch_bounds__(256) void k_dx_final(
       *(f32x4*)((float*)dX + (int64_t)i * H + 4 * g) = v;
     } else {
       i32x2 pk;
-      pk[0] = (int)(f2bf(v[0]) | (f2bf(v[1]) << 16));
-      pk[1] = (int)(f2bf(v[2]) | (f2bf(v[3]) << 16));
+      pk[0] = pack_bf16(v[0], v[1]);
+      pk[1] = pack_bf16(v[2], v[3]);
       *(i32x2*)((uint16_t*)dX + (int64_t)i * H + 4 * g) = pk;
     }
   }

@@ -58,10 +58,18 @@ struct F32 {
   static constexpr int kKStep = 32;
 };
 
+// Buffer descriptor over [base, base + bytes) (clamped to 32 bits).  Every
+// caller passes workgroup-uniform values; saying so with readfirstlane keeps
+// the descriptor in scalar registers even where the compiler cannot prove
+// uniformity (it would otherwise wrap each load in a per-lane loop).
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
   uint32_t n = bytes <= 0 ? 0u
              : (bytes > 0xFFFFFFFFll ? 0xFFFFFFFFu : (uint32_t)bytes);
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+  const uint64_t p = (uint64_t)base;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  n = __builtin_amdgcn_readfirstlane(n);
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(((uint64_t)hi << 32) | lo), (short)0,
                                            (int)n, kRsrcWord3);
 }
 
@@ -455,11 +463,15 @@ __device__ __forceinline__ void grouped(int item, int R, int C, int& r, int& c) 
 }
 
 // float -> bfloat16 bits, round to nearest even, NaN kept quiet.
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// fp32 -> bf16 with round-to-nearest-even (NaN stays NaN): gfx950 converts a
+// pair in one v_cvt_pk_bf16_f32; `a` lands in the low half.
+__device__ __forceinline__ int pack_bf16(float a, float b) {
+  return __builtin_bit_cast(int, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
 __device__ __forceinline__ uint32_t f2bf(float f) {
-  uint32_t u = __builtin_bit_cast(uint32_t, f);
-  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return u >> 16;
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 __device__ __forceinline__ float bf2f(uint32_t b) {
   return __builtin_bit_cast(float, b << 16);

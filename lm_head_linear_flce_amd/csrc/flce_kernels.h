@@ -407,40 +407,41 @@ struct BwdArgs {
 // kMasked: tile rows with (32i + 8g + q) >= vlim_lane lie past the vocabulary
 // end and token columns >= nlim are padding; both become 0.
 // l2[j]: lse2 of the lane's token column j, loaded before the tile's K loop.
+// bf16: through LDS (store_quarter_bf16); fp32: direct 16-byte stores.
 template <class E, bool kMasked>
 __device__ __forceinline__ void g_store(const BwdArgs& a, const f32x16 (&acc)[4][4],
                                         const float (&l2)[4], float c, int vt, int tau,
-                                        int wm, int wn, int lane, int vlim_lane, int nlim) {
+                                        int wm, int wn, int lane, int vlim_lane, int nlim,
+                                        lds_t* smem) {
   const rsrc_t gr = make_rsrc(a.G, (int64_t)a.rows_pad * a.Vb * E::kBytes);
+  auto val = [&](int i, int j, int r) {
+    const float v = c * __builtin_amdgcn_exp2f(fmaf(acc[i][j][r], kLog2e, -l2[j]));
+    const bool ok = !kMasked || (acc_col(wn, j, lane) < nlim &&
+                                 32 * i + 8 * (r >> 2) + (r & 3) < vlim_lane);
+    return ok ? v : 0.f;
+  };
+  if constexpr (E::kBytes == 2) {
+    const int wave = threadIdx.x >> 6;
+    const int tok0 = tau * kTile + wn * 128, voc0 = vt * kTile + wm * 128;
+    store_quarter_bf16(smem + wave * 32768, lane, val, [&](int o, int x0, i32x4 v) {
+      __builtin_amdgcn_raw_buffer_store_b128(v, gr, ((tok0 + o) * a.Vb + voc0 + x0) * 2, 0, 0);
+    });
+  } else {
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int tcol = acc_col(wn, j, lane);
-    const int tok = tau * kTile + tcol;
-    const bool tok_ok = !kMasked || tcol < nlim;
+    for (int j = 0; j < 4; ++j) {
+      const int tok = tau * kTile + acc_col(wn, j, lane);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int row0 = acc_row(wm, i, 4 * g, lane);   // 4 consecutive rows
-        float v[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          v[q] = c * __builtin_amdgcn_exp2f(fmaf(acc[i][j][4 * g + q], kLog2e, -l2[j]));
-          if (kMasked && !(tok_ok && 32 * i + 8 * g + q < vlim_lane)) v[q] = 0.f;
+        for (int g = 0; g < 4; ++g) {
+          const int row0 = acc_row(wm, i, 4 * g, lane);   // 4 consecutive rows
+          const f32x4 fv = {val(i, j, 4 * g), val(i, j, 4 * g + 1), val(i, j, 4 * g + 2),
+                            val(i, j, 4 * g + 3)};
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, fv), gr,
+                                                 (tok * a.Vb + vt * kTile + row0) * 4, 0, 0);
         }
-        const int off = (tok * a.Vb + vt * kTile + row0) * E::kBytes;
-        if constexpr (E::kBytes == 2) {
-          i32x2 pk;
-          pk[0] = pack_bf16(v[0], v[1]);
-          pk[1] = pack_bf16(v[2], v[3]);
-          __builtin_amdgcn_raw_buffer_store_b64(pk, gr, off, 0, 0);
-        } else {
-          const f32x4 fv = {v[0], v[1], v[2], v[3]};
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, fv), gr, off, 0,
-                                                 0);
-        }
-      }
-    __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   }
 }
 
@@ -480,10 +481,10 @@ __device__ __forceinline__ void g_tile(const BwdArgs& a, int item, lds_t* smem) 
 
   const int vlim = a.V - vbase;
   if (vlim >= kTile && (tau + 1) * kTile <= n)
-    g_store<E, false>(a, acc, l2, c, vt, tau, wm, wn, lane, 0, 0);
+    g_store<E, false>(a, acc, l2, c, vt, tau, wm, wn, lane, 0, 0, smem);
   else
     g_store<E, true>(a, acc, l2, c, vt, tau, wm, wn, lane,
-                     vlim - wm * 128 - 4 * (lane >> 5), n - tau * kTile);
+                     vlim - wm * 128 - 4 * (lane >> 5), n - tau * kTile, smem);
 }
 
 // The one-hot part of G: G[k, y_k - v0] -= c for targets inside the block.
@@ -513,12 +514,26 @@ __global__ __launch_bounds__(256) void k_fixup(BwdArgs a) {
 template <bool kMasked>
 __device__ __forceinline__ void dw_store(const BwdArgs& a, const f32x16 (&acc)[4][4],
                                          int vt, int ht, int wm, int wn, int lane,
-                                         int mlim, int hlim) {
+                                         int mlim, int hlim, lds_t* smem) {
   const int es = a.dw_f32 ? 4 : 2;
   const int64_t row0 = (int64_t)(a.v0 + vt * kTile) * a.H + (int64_t)ht * kTile;
   const int64_t left = ((int64_t)a.V * a.H - row0) * es;
   const int64_t span = (int64_t)kTile * a.H * es;
   const rsrc_t wr = make_rsrc((char*)a.dW + row0 * es, left < span ? left : span);
+  if (!a.dw_f32) {
+    // bf16 rows through LDS: row o of the quarter is vocabulary entry
+    // wn * 128 + o of the tile, inner x its hidden index wm * 128 + x
+    const int wave = threadIdx.x >> 6;
+    store_quarter_bf16(
+        smem + wave * 32768, lane, [&](int i, int j, int r) { return acc[i][j][r]; },
+        [&](int o, int x0, i32x4 v) {
+          const int m = wn * 128 + o, h = wm * 128 + x0;
+          const bool ok = !kMasked || (m < mlim && h < hlim);
+          __builtin_amdgcn_raw_buffer_store_b128(v, wr, ok ? (m * a.H + h) * 2 : (int)0x80000000u,
+                                                 0, 0);
+        });
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int mc = acc_col(wn, j, lane);
@@ -528,17 +543,10 @@ __device__ __forceinline__ void dw_store(const BwdArgs& a, const f32x16 (&acc)[4
       for (int g = 0; g < 4; ++g) {
         const int hc = acc_row(wm, i, 4 * g, lane);
         const bool ok = !kMasked || (mc < mlim && hc < hlim);
-        const int off = ok ? (mc * a.H + hc) * es : (int)0x80000000u;
+        const int off = ok ? (mc * a.H + hc) * 4 : (int)0x80000000u;
         const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
                          acc[i][j][4 * g + 3]};
-        if (a.dw_f32) {
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), wr, off, 0, 0);
-        } else {
-          i32x2 pk;
-          pk[0] = pack_bf16(v[0], v[1]);
-          pk[1] = pack_bf16(v[2], v[3]);
-          __builtin_amdgcn_raw_buffer_store_b64(pk, wr, off, 0, 0);
-        }
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), wr, off, 0, 0);
       }
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -572,53 +580,35 @@ __device__ __forceinline__ void dw_tile(const BwdArgs& a, int item, lds_t* smem)
   gemm_tile<E, LoadMN<E>, LoadMN<E>>(A, B, steps, smem, wm, wn, acc);
 
   const int mlim = a.vb - vt * kTile, hlim = a.H - ht * kTile;
-  if (mlim >= kTile && hlim >= kTile) dw_store<false>(a, acc, vt, ht, wm, wn, lane, 0, 0);
-  else dw_store<true>(a, acc, vt, ht, wm, wn, lane, mlim, hlim);
+  if (mlim >= kTile && hlim >= kTile) dw_store<false>(a, acc, vt, ht, wm, wn, lane, 0, 0, smem);
+  else dw_store<true>(a, acc, vt, ht, wm, wn, lane, mlim, hlim, smem);
 }
 
 // dX32 += tile, read-modify-write: each (token tile, hidden tile) belongs to
 // one workgroup of a launch, and launches are ordered on the stream.
-// Accumulator rows are hidden indices, columns tokens; token columns >= nlim
-// (padding) and hidden rows >= hlim are skipped.  Branch-free: masked lanes
-// load and store at an offset past the buffer (rows_pad * H * 4 < 2^31), so
+// Accumulator rows are hidden indices, columns tokens; the quarter goes
+// through LDS (rmw_quarter_f32) so that each token row is read and written in
+// 512-byte runs.  Token columns >= nlim (padding) and hidden rows >= hlim are
+// skipped: their offset lies past the buffer (rows_pad * H * 4 < 2^31), so
 // the load returns zeros and the store is dropped.
 template <bool kMasked>
 __device__ __forceinline__ void dx_add(const BwdArgs& a, const f32x16 (&acc)[4][4],
                                        int tau, int ht, int wm, int wn, int lane,
-                                       int nlim, int hlim) {
+                                       int nlim, int hlim, lds_t* smem) {
   const rsrc_t xr = make_rsrc(a.dx32, (int64_t)a.rows_pad * a.H * 4);
-  auto offset = [&](int j, int i, int g) {
-    const int tcol = acc_col(wn, j, lane), hc = acc_row(wm, i, 4 * g, lane);
+  const int wave = threadIdx.x >> 6;
+  auto offset = [&](int o, int x0) {
+    const int tcol = wn * 128 + o, hc = wm * 128 + x0;
     const bool ok = !kMasked || (tcol < nlim && hc < hlim);
     return ok ? ((tau * kTile + tcol) * a.H + ht * kTile + hc) * 4 : (int)0x80000000u;
   };
-  // the loads of column j + 1 are in flight while column j is added and stored
-  f32x4 old[2][4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) old[0][i][g] = __builtin_bit_cast(f32x4, bload128(xr, offset(0, i, g)));
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if (j + 1 < 4) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int g = 0; g < 4; ++g)
-          old[(j + 1) & 1][i][g] = __builtin_bit_cast(f32x4, bload128(xr, offset(j + 1, i, g)));
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4& o = old[j & 1][i][g];
-        const f32x4 v = {o[0] + acc[i][j][4 * g], o[1] + acc[i][j][4 * g + 1],
-                         o[2] + acc[i][j][4 * g + 2], o[3] + acc[i][j][4 * g + 3]};
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), xr, offset(j, i, g),
+  rmw_quarter_f32(
+      smem + wave * 32768, lane, acc,
+      [&](int o, int x0) { return __builtin_bit_cast(f32x4, bload128(xr, offset(o, x0))); },
+      [&](int o, int x0, f32x4 v) {
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), xr, offset(o, x0),
                                                0, 0);
-      }
-    __builtin_amdgcn_sched_barrier(0);
-  }
+      });
 }
 
 // dX32[k, h] += sum_m W[v0 + m, h] G[k, m] over the whole block for one
@@ -651,8 +641,8 @@ __device__ __forceinline__ void dx_tile(const BwdArgs& a, int item, lds_t* smem)
   gemm_tile<E, LoadMN<E>, LoadDirect>(A, B, steps, smem, wm, wn, acc);
 
   const int nlim = n - tau * kTile, hlim = a.H - ht * kTile;
-  if (nlim >= kTile && hlim >= kTile) dx_add<false>(a, acc, tau, ht, wm, wn, lane, 0, 0);
-  else dx_add<true>(a, acc, tau, ht, wm, wn, lane, nlim, hlim);
+  if (nlim >= kTile && hlim >= kTile) dx_add<false>(a, acc, tau, ht, wm, wn, lane, 0, 0, smem);
+  else dx_add<true>(a, acc, tau, ht, wm, wn, lane, nlim, hlim, smem);
 }
 
 // One backward launch: nb_dx dX tiles and nb_dw dW tiles of block `cur`,

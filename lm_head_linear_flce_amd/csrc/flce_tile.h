@@ -73,6 +73,20 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
                                            (int)n, kRsrcWord3);
 }
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+// fp32 -> bf16 with round-to-nearest-even (NaN stays NaN): gfx950 converts a
+// pair in one v_cvt_pk_bf16_f32; `a` lands in the low half.
+__device__ __forceinline__ int pack_bf16(float a, float b) {
+  return __builtin_bit_cast(int, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+__device__ __forceinline__ uint32_t f2bf(float f) {
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+__device__ __forceinline__ float bf2f(uint32_t b) {
+  return __builtin_bit_cast(float, b << 16);
+}
+
 __device__ __forceinline__ i32x4 bload128(rsrc_t r, int off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 }
@@ -439,6 +453,87 @@ __device__ __forceinline__ int acc_col(int wn, int j, int lane) {
   return wn * 128 + 32 * j + (lane & 31);
 }
 
+// Epilogue store of one wave's 128 x 128 quarter of a tile as bf16 rows.
+// The accumulator layout gives each lane 4 consecutive values of a row's
+// contiguous dimension ("inner" x = 32 i + 8 g + 4 (lane / 32) + q, the tile
+// row index) for one row ("outer" o = 32 j + lane % 32, the tile column
+// index), so direct stores would scatter 8-byte pieces over 32 rows.  The
+// quarter goes through the wave's own 32 KiB of LDS instead ([128 rows][256
+// B], 8-byte unit u of row o kept at u ^ (o % 32), conflict-free both ways)
+// and leaves as 16-byte chunks, 16 lanes per 256-byte row segment.
+//   val(i, j, r) -> float   value of accumulator register (i, j, r)
+//   emit(o, x0, v)          store chunk v (8 bf16, inner x0 .. x0 + 7) of row o
+// The region must be free (after the K loop's last barrier) and only this
+// wave touches it, so no barrier is needed between the two phases.
+template <class Val, class Emit>
+__device__ __forceinline__ void store_quarter_bf16(lds_t* region, int lane, Val&& val,
+                                                   Emit&& emit) {
+  typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
+  typedef __attribute__((address_space(3))) i32x4 lds_i32x4;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int o = 32 * j + (lane & 31);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int u = 8 * i + 2 * g + (lane >> 5);
+        i32x2 pk;
+        pk[0] = pack_bf16(val(i, j, 4 * g), val(i, j, 4 * g + 1));
+        pk[1] = pack_bf16(val(i, j, 4 * g + 2), val(i, j, 4 * g + 3));
+        *(lds_i32x2*)(region + o * 256 + ((u ^ (o & 31)) << 3)) = pk;
+      }
+  }
+  const int c = lane & 15;
+#pragma unroll
+  for (int t = 0; t < 32; ++t) {
+    const int o = 4 * t + (lane >> 4), x = o & 31;
+    i32x4 v = *(const lds_i32x4*)(region + o * 256 + ((c ^ (x >> 1)) << 4));
+    if (x & 1) v = i32x4{v[2], v[3], v[0], v[1]};
+    emit(o, 8 * c, v);
+  }
+}
+
+// fp32 counterpart for read-modify-write epilogues: the same quarter, in two
+// halves of 64 rows (j = 0, 1 then j = 2, 3) of 512 B each, 16-byte unit u of
+// row o kept at u ^ (o % 32).  For every 16-byte chunk (4 fp32, inner x0 ..
+// x0 + 3) of row o, `load(o, x0)` fetches the old value (all of a half's
+// loads are issued before its LDS traffic) and `store(o, x0, v)` writes v.
+template <class Load, class Store>
+__device__ __forceinline__ void rmw_quarter_f32(lds_t* region, int lane,
+                                                const f32x16 (&acc)[4][4], Load&& load,
+                                                Store&& store) {
+  typedef __attribute__((address_space(3))) i32x4 lds_i32x4;
+  const int c = lane & 31;
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    f32x4 old[32];
+#pragma unroll
+    for (int t = 0; t < 32; ++t) old[t] = load(64 * hf + 2 * t + (lane >> 5), 4 * c);
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+      const int j = 2 * hf + jj, o = 32 * jj + (lane & 31);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int u = 8 * i + 2 * g + (lane >> 5);
+          const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                           acc[i][j][4 * g + 3]};
+          *(lds_i32x4*)(region + o * 512 + ((u ^ (o & 31)) << 4)) = __builtin_bit_cast(i32x4, v);
+        }
+    }
+#pragma unroll
+    for (int t = 0; t < 32; ++t) {
+      const int o = 2 * t + (lane >> 5);
+      const f32x4 v = __builtin_bit_cast(
+          f32x4, *(const lds_i32x4*)(region + o * 512 + ((c ^ (o & 31)) << 4)));
+      store(64 * hf + o, 4 * c, f32x4{old[t][0] + v[0], old[t][1] + v[1], old[t][2] + v[2],
+                                      old[t][3] + v[3]});
+    }
+  }
+}
+
 // Maps a launch index to a work item so that items i, i+1, ... run on the same
 // XCD: workgroups are handed to the 8 XCDs round-robin, so block b lands on XCD
 // b % 8; grouping by b % 8 keeps neighbouring items (which share an operand
@@ -460,21 +555,6 @@ __device__ __forceinline__ void grouped(int item, int R, int C, int& r, int& c) 
   const int local = item - group * kGroup * C;
   r = r0 + local % gsz;
   c = local / gsz;
-}
-
-// float -> bfloat16 bits, round to nearest even, NaN kept quiet.
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-// fp32 -> bf16 with round-to-nearest-even (NaN stays NaN): gfx950 converts a
-// pair in one v_cvt_pk_bf16_f32; `a` lands in the low half.
-__device__ __forceinline__ int pack_bf16(float a, float b) {
-  return __builtin_bit_cast(int, __builtin_convertvector(f32x2{a, b}, bf16x2));
-}
-__device__ __forceinline__ uint32_t f2bf(float f) {
-  return __builtin_bit_cast(uint16_t, (__bf16)f);
-}
-__device__ __forceinline__ float bf2f(uint32_t b) {
-  return __builtin_bit_cast(float, b << 16);
 }
 
 }  // namespace flce

@@ -133,9 +133,57 @@ int flce_backward(const void* X, const void* W, const int64_t* labels,
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Chunked mode: the row-chunk recipe of the ms-swift PR "feat(sft): Add
+ * optional fused linear ce for qwen2/qwen3 on npu" ("What this PR does": the
+ * sequence cut into chunks, each chunk's logits, loss and both gradients
+ * computed at once; "Mathematical Equivalence": grad_weight summed over the
+ * chunks).  One call returns loss, lse, dX and dW.  A chunk of C valid rows
+ * keeps its softmax gradient over the whole vocabulary in a [C, V] slab of
+ * the workspace (C chosen from a 1 GiB budget), so the logits are computed
+ * once (three contractions, 6 n H V flop, instead of the forward + backward
+ * pair's four) at the price of memory proportional to the chunk.
+ *
+ * flce_chunked_workspace_size -- bytes of device scratch flce_chunked needs
+ * (host-only arithmetic).  Arguments as flce_workspace_size.
+ */
+int flce_chunked_workspace_size(int64_t B, int64_t T, int64_t H, int64_t V, int dtype,
+                                size_t* bytes);
+
+/*
+ * flce_chunked -- loss, per-row lse and the gradients of grad_scale * loss.
+ *   X, W, labels, sizes, dtype, ignore_index, reduction, shift : as forward
+ *   grad_scale    : float32 scalar, device; NULL = 1
+ *   loss, lse, n_valid : as flce_forward's outputs
+ *   dX, dW, grad_dtype : as flce_backward's outputs
+ *   status        : as forward (a bad label also makes the gradients NaN)
+ *   workspace, workspace_bytes : device scratch of flce_chunked_workspace_size
+ *   stream        : hipStream_t
+ * dW is summed over the row chunks: with grad_dtype = FLCE_DTYPE_F32 in FP32;
+ * with bf16 it is rounded once per chunk (ceil(n / C) roundings; one when all
+ * valid rows fit one chunk).  dX is accumulated in FP32 and rounded once.
+ */
+int flce_chunked(const void* X, const void* W, const int64_t* labels,
+                 int64_t B, int64_t T, int64_t H, int64_t V, int dtype,
+                 int64_t ignore_index, int reduction, int shift, const float* grad_scale,
+                 float* loss, float* lse, int64_t* n_valid, void* dX, void* dW,
+                 int grad_dtype, int32_t* status, void* workspace, size_t workspace_bytes,
+                 void* stream);
+
+/*
+ * flce_scale_grads -- dX[0:nx] *= *scale and dW[0:nw] *= *scale in place (the
+ * upstream gradient applied to gradients computed with grad_scale = 1, e.g.
+ * by flce_chunked during an autograd forward).  nx, nw: element counts,
+ * multiples of 8 (bf16) or 4 (fp32); grad_dtype FLCE_DTYPE_BF16 or _F32;
+ * scale: float32 scalar, device.  Buffers 16-byte aligned.
+ */
+int flce_scale_grads(void* dX, int64_t nx, void* dW, int64_t nw, int grad_dtype,
+                     const float* scale, void* stream);
+
+/*
  * flce_set_timing -- measurement hook for benchmarks and profilers.  While set,
- * every launch of the kernel named `kernel` ("k_fwd_lse", the forward GEMM,
- * or "k_bwd", the backward GEMM launches) made by flce_forward / flce_backward records
+ * every launch of the kernel named `kernel` ("k_fwd_lse", the forward GEMM;
+ * "k_bwd", the backward GEMM launches; "k_chunk_z" and "k_chunk_dxdw", the
+ * chunked mode's logits and gradient launches) made by the library records
  * events[2*i] on its stream right before the launch and events[2*i+1] right
  * after it, where i = *count, and then increments *count (a host int), until
  * *count reaches `capacity`.  `events` holds 2*capacity hipEvent_t handles

@@ -3,13 +3,16 @@
 Two layers, both argument marshalling only -- every step of the computation runs
 in the HIP kernels of ``libflce.so``:
 
-* ``flce_workspace_size``, ``flce_forward``, ``flce_backward`` and
+* ``flce_workspace_size``, ``flce_forward``, ``flce_backward``,
+  ``flce_chunked_workspace_size``, ``flce_chunked``, ``flce_scale_grads`` and
   ``flce_status_string`` mirror the C ABI of ``include/flce.h`` one to one and
   take raw device addresses (Python ints) and sizes;
 * ``linear_cross_entropy(hidden, weight, labels, ignore_index=-100,
-  shift=False, reduction="mean")`` is the tensor-level call with autograd, the
-  argument set of the ``linear_cross_entropy`` call in the LoRA-SFT blog post's
-  CCE patch.  PyTorch only provides device memory and the current stream.
+  shift=False, reduction="mean", mode="recompute")`` is the tensor-level call
+  with autograd, the argument set of the ``linear_cross_entropy`` call in the
+  LoRA-SFT blog post's CCE patch; ``mode="chunked"`` computes the gradients
+  during the forward with the row-chunk schedule.  PyTorch only provides device
+  memory and the current stream.
 
 Importing the package loads ``libflce.so`` and fails loudly if it is missing;
 there is no fallback implementation.
@@ -22,8 +25,8 @@ import os
 __all__ = [
     "FLCE_OK", "FLCE_DTYPE_F32", "FLCE_DTYPE_BF16", "FLCE_REDUCTION_MEAN",
     "FLCE_REDUCTION_SUM", "FlceError", "flce_workspace_size", "flce_forward",
-    "flce_backward", "flce_set_timing", "flce_status_string", "linear_cross_entropy",
-    "library_path",
+    "flce_backward", "flce_chunked_workspace_size", "flce_chunked", "flce_scale_grads",
+    "flce_set_timing", "flce_status_string", "linear_cross_entropy", "library_path",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflce.so")
@@ -44,8 +47,9 @@ FLCE_DTYPE_BF16 = 1
 FLCE_REDUCTION_MEAN = 0
 FLCE_REDUCTION_SUM = 1
 
-EXPORTS = ("flce_workspace_size", "flce_forward", "flce_backward", "flce_set_timing",
-           "flce_status_string")
+EXPORTS = ("flce_workspace_size", "flce_forward", "flce_backward",
+           "flce_chunked_workspace_size", "flce_chunked", "flce_scale_grads",
+           "flce_set_timing", "flce_status_string")
 
 
 class FlceError(RuntimeError):
@@ -75,6 +79,13 @@ def _load() -> ctypes.CDLL:
     lib.flce_backward.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, i64, i32, i32,
                                   vp, vp, vp, vp, i32, vp, vp, sz, vp]
     lib.flce_backward.restype = i32
+    lib.flce_chunked_workspace_size.argtypes = [i64, i64, i64, i64, i32, ctypes.POINTER(sz)]
+    lib.flce_chunked_workspace_size.restype = i32
+    lib.flce_chunked.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, i64, i32, i32, vp,
+                                 vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]
+    lib.flce_chunked.restype = i32
+    lib.flce_scale_grads.argtypes = [vp, i64, vp, i64, i32, vp, vp]
+    lib.flce_scale_grads.restype = i32
     lib.flce_set_timing.argtypes = [ctypes.c_char_p, vp, i32, ctypes.POINTER(i32)]
     lib.flce_set_timing.restype = i32
     lib.flce_status_string.argtypes = [i32]
@@ -123,6 +134,31 @@ def flce_backward(X, W, labels, B, T, H, V, dtype, ignore_index, reduction, shif
                               grad_scale or None, dX or None, dW or None, grad_dtype,
                               status or None, workspace or None, workspace_bytes,
                               stream or None)
+
+
+def flce_chunked_workspace_size(B: int, T: int, H: int, V: int, dtype: int) -> int:
+    out = ctypes.c_size_t(0)
+    rc = _LIB.flce_chunked_workspace_size(B, T, H, V, dtype, ctypes.byref(out))
+    if rc != FLCE_OK:
+        raise FlceError(rc, "flce_chunked_workspace_size")
+    return int(out.value)
+
+
+def flce_chunked(X, W, labels, B, T, H, V, dtype, ignore_index, reduction, shift,
+                 grad_scale, loss, lse, n_valid, dX, dW, grad_dtype, status, workspace,
+                 workspace_bytes, stream) -> int:
+    """Returns the status code (0 on success); raises nothing."""
+    return _LIB.flce_chunked(X or None, W or None, labels or None, B, T, H, V, dtype,
+                             ignore_index, reduction, int(bool(shift)), grad_scale or None,
+                             loss or None, lse or None, n_valid or None, dX or None,
+                             dW or None, grad_dtype, status or None, workspace or None,
+                             workspace_bytes, stream or None)
+
+
+def flce_scale_grads(dX, nx, dW, nw, grad_dtype, scale, stream) -> int:
+    """Returns the status code (0 on success); raises nothing."""
+    return _LIB.flce_scale_grads(dX or None, nx, dW or None, nw, grad_dtype, scale or None,
+                                 stream or None)
 
 
 def flce_set_timing(kernel, events, capacity, count) -> int:
@@ -257,6 +293,46 @@ def backward(hidden, weight, labels, lse, grad_scale=None, ignore_index=-100,
     return dX, dW, status
 
 
+def chunked_workspace(B, T, H, V, dtype_code, device):
+    torch = _torch()
+    nbytes = flce_chunked_workspace_size(B, T, H, V, dtype_code)
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device), nbytes
+
+
+def chunked(hidden, weight, labels, grad_scale=None, ignore_index=-100, shift=False,
+            reduction="mean", grad_dtype=None, ws=None):
+    """(loss, lse, n_valid, dX, dW, status) from one flce_chunked call."""
+    torch = _torch()
+    _check_tensors(hidden, weight, labels)
+    B, T, H, V = _shape(hidden, weight, labels)
+    dt = _dtype_code(hidden)
+    gd = dt if grad_dtype is None else _dtype_code(torch.empty(0, dtype=grad_dtype))
+    out_dtype = torch.float32 if gd == FLCE_DTYPE_F32 else hidden.dtype
+    dev = hidden.device
+    if ws is None:
+        ws, nbytes = chunked_workspace(B, T, H, V, dt, dev)
+    else:
+        nbytes = ws.numel()
+    loss = torch.empty((), dtype=torch.float32, device=dev)
+    lse = torch.empty(B * T, dtype=torch.float32, device=dev)
+    n_valid = torch.empty((), dtype=torch.int64, device=dev)
+    status = torch.empty((), dtype=torch.int32, device=dev)
+    dX = torch.empty(hidden.shape, dtype=out_dtype, device=dev)
+    dW = torch.empty(weight.shape, dtype=out_dtype, device=dev)
+    gs = 0
+    if grad_scale is not None:
+        grad_scale = grad_scale.to(device=dev, dtype=torch.float32).contiguous()
+        gs = grad_scale.data_ptr()
+    rc = flce_chunked(hidden.data_ptr(), weight.data_ptr(), labels.data_ptr(), B, T, H, V,
+                      dt, int(ignore_index), _reduction_code(reduction), shift, gs,
+                      loss.data_ptr(), lse.data_ptr(), n_valid.data_ptr(), dX.data_ptr(),
+                      dW.data_ptr(), gd, status.data_ptr(), ws.data_ptr(), nbytes,
+                      _stream_handle(dev))
+    if rc != FLCE_OK:
+        raise FlceError(rc, "flce_chunked")
+    return loss, lse, n_valid, dX, dW, status
+
+
 def _autograd_function():
     torch = _torch()
 
@@ -279,23 +355,52 @@ def _autograd_function():
                                  reduction=reduction)
             return dX, dW, None, None, None, None
 
-    return LinearCrossEntropy
+    class LinearCrossEntropyChunked(torch.autograd.Function):
+        """Gradients formed in the forward (flce_chunked, grad_scale 1), scaled
+        by the upstream gradient in the backward (flce_scale_grads)."""
+
+        @staticmethod
+        def forward(ctx, hidden, weight, labels, ignore_index, shift, reduction):
+            loss, _, _, dX, dW, _ = chunked(hidden, weight, labels,
+                                            ignore_index=ignore_index, shift=shift,
+                                            reduction=reduction)
+            ctx.save_for_backward(dX, dW)
+            return loss
+
+        @staticmethod
+        def backward(ctx, grad_out):
+            dX, dW = ctx.saved_tensors
+            g = grad_out.reshape(()).to(dtype=torch.float32).contiguous()
+            gd = _dtype_code(dX)
+            rc = flce_scale_grads(dX.data_ptr(), dX.numel(), dW.data_ptr(), dW.numel(), gd,
+                                  g.data_ptr(), _stream_handle(dX.device))
+            if rc != FLCE_OK:
+                raise FlceError(rc, "flce_scale_grads")
+            return dX, dW, None, None, None, None
+
+    return LinearCrossEntropy, LinearCrossEntropyChunked
 
 
 _FN = None
 
 
 def linear_cross_entropy(hidden, weight, labels, ignore_index=-100, shift=False,
-                         reduction="mean"):
+                         reduction="mean", mode="recompute"):
     """Fused ``cross_entropy(hidden @ weight.T, targets)`` without the logits.
 
     hidden [B, T, H] or [N, H]; weight [V, H]; labels [B, T] (or [N], one
     sequence); bfloat16 or float32 on the GPU.  Returns a float32 scalar loss
-    tensor that backpropagates into hidden and weight."""
+    tensor that backpropagates into hidden and weight.  mode="recompute"
+    (forward, then a backward that recomputes the logits; extra memory linear
+    in N) or "chunked" (gradients formed during the forward over row chunks;
+    one logits pass, extra memory proportional to a chunk of rows times V)."""
     global _FN
     if _FN is None:
         _FN = _autograd_function()
     if reduction not in ("mean", "sum"):
         raise ValueError(f"unsupported reduction {reduction!r} (mean or sum)")
-    return _FN.apply(hidden.contiguous(), weight.contiguous(), labels.contiguous(),
-                     int(ignore_index), bool(shift), reduction)
+    if mode not in ("recompute", "chunked"):
+        raise ValueError(f"unsupported mode {mode!r} (recompute or chunked)")
+    fn = _FN[0] if mode == "recompute" else _FN[1]
+    return fn.apply(hidden.contiguous(), weight.contiguous(), labels.contiguous(),
+                    int(ignore_index), bool(shift), reduction)

@@ -254,6 +254,7 @@ int backward_impl(const Plan& pl, const void* X, const void* W, const int64_t* l
   a.TT = (int)pl.TT;
   a.HT = (int)cdiv(pl.H, kTile);
   a.dw_f32 = grad_f32;
+  a.dw_acc = 0;
   a.v0 = a.vb = a.VTb = 0;
   const int64_t slab = pl.rows_pad * pl.Vb * pl.es;
   auto block = [&](int64_t b) {
@@ -286,6 +287,190 @@ int backward_impl(const Plan& pl, const void* X, const void* W, const int64_t* l
       L.check();
     }
   }
+  hipLaunchKernelGGL(k_dx_final, dim3((unsigned)cdiv(pl.N, 4)), dim3(256), 0, stream,
+                     (const float*)dx32, (const int*)rowpos, (int)pl.N, (int)pl.H,
+                     (char*)dX, grad_f32);
+  L.check();
+  return L.err == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
+}
+
+
+// bytes % 16 == 0 (every caller's sizes are multiples of 8 bf16 / 4 fp32)
+void zero_fill(void* p, int64_t bytes, hipStream_t s) {
+  const int64_t chunks = bytes / 16;
+  const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>(cdiv(chunks, 256), 4096));
+  hipLaunchKernelGGL(k_zero, dim3((unsigned)blocks), dim3(256), 0, s, (char*)p, chunks);
+}
+
+// ---------------------------------------------------------------------------
+// Chunked mode (one call for loss, lse, dX and dW)
+// ---------------------------------------------------------------------------
+#ifndef FLCE_CHUNK_MIB
+#define FLCE_CHUNK_MIB 1024
+#endif
+// the [C, Vp] softmax-gradient slab of one row chunk holds at most this many
+// bytes (unless one 256-row tile of it already needs more)
+constexpr int64_t kChunkBudget = (int64_t)FLCE_CHUNK_MIB << 20;
+// vocabulary block of the dX / dW launches inside a chunk
+constexpr int64_t kChunkVocabBlock = 16384;
+
+struct ChunkPlan {
+  int64_t N, rows_pad, H, V, Vp, es, TT, VT;
+  int64_t C, nchunks;       // chunk rows (multiple of 256), chunks covering rows_pad
+  int64_t o_ctr, o_idx, o_tgt, o_rowpos, o_xc, o_zt, o_lse_c, o_lse2, o_bsum, o_cctr;
+  int64_t o_part, o_slab, o_dx32;
+  int64_t total;
+};
+
+int make_chunk_plan(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, ChunkPlan* p) {
+  Plan base;
+  const int rc = make_plan(B, T, H, V, dtype, &base);
+  if (rc != FLCE_OK) return rc;
+  ChunkPlan q;
+  q.N = base.N;
+  q.rows_pad = base.rows_pad;
+  q.H = H;
+  q.V = V;
+  q.es = base.es;
+  q.TT = base.TT;
+  q.VT = base.VT;
+  q.Vp = q.VT * kTile;
+  int64_t c = std::min(kChunkBudget, kMaxI32) / (q.Vp * q.es) / kTile * kTile;
+  if (c < kTile) c = kTile;
+  q.C = std::min(c, q.rows_pad);
+  if (q.C * q.Vp * q.es > kMaxI32) return FLCE_ERR_SHAPE;
+  q.nchunks = cdiv(q.rows_pad, q.C);
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) {
+    const int64_t o = off;
+    off = round_up(off + bytes, kAlign);
+    return o;
+  };
+  q.o_ctr = take(sizeof(Counters));
+  q.o_idx = take(4 * q.rows_pad);
+  q.o_tgt = take(4 * q.rows_pad);
+  q.o_rowpos = take(4 * q.rows_pad);
+  q.o_xc = take(q.rows_pad * H * q.es);
+  q.o_zt = take(4 * q.rows_pad);
+  q.o_lse_c = take(4 * q.rows_pad);
+  q.o_lse2 = take(4 * q.rows_pad);
+  q.o_bsum = take(4 * q.nchunks * (q.C / kTile));
+  q.o_cctr = take(sizeof(Counters) * q.nchunks);
+  q.o_part = take(8 * 2 * q.VT * q.C);
+  q.o_slab = take(q.C * q.Vp * q.es);
+  q.o_dx32 = take(4 * q.rows_pad * H);
+  q.total = off;
+  *p = q;
+  return FLCE_OK;
+}
+
+template <class E>
+int chunked_impl(const ChunkPlan& pl, const void* X, const void* W, const int64_t* labels,
+                 int64_t B, int64_t T, int64_t ignore_index, int reduction, int shift,
+                 const float* grad_scale, float* loss, float* lse, int64_t* n_valid,
+                 void* dX, void* dW, int grad_f32, int32_t* status, char* ws,
+                 hipStream_t stream) {
+  Launch L{stream};
+  Counters* ctr = (Counters*)(ws + pl.o_ctr);
+  int* idx = (int*)(ws + pl.o_idx);
+  int* tgt = (int*)(ws + pl.o_tgt);
+  int* rowpos = (int*)(ws + pl.o_rowpos);
+  char* xc = ws + pl.o_xc;
+  float* zt = (float*)(ws + pl.o_zt);
+  float* lse_c = (float*)(ws + pl.o_lse_c);
+  float* lse2 = (float*)(ws + pl.o_lse2);
+  float* bsum = (float*)(ws + pl.o_bsum);
+  Counters* cctr = (Counters*)(ws + pl.o_cctr);
+  float2* part = (float2*)(ws + pl.o_part);
+  char* slab = ws + pl.o_slab;
+  float* dx32 = (float*)(ws + pl.o_dx32);
+  const int rows_pad = (int)pl.rows_pad;
+  const int row_bytes = (int)(pl.H * E::kBytes);
+  const int C = (int)pl.C, TTc = C / kTile, HT = (int)cdiv(pl.H, kTile);
+
+  hipLaunchKernelGGL(k_prep, dim3(1), dim3(1024), 0, stream, labels, (int)B, (int)T,
+                     ignore_index, pl.V, shift, reduction, grad_scale, cu_count(), 1, idx,
+                     tgt, rowpos, ctr, status);
+  L.check();
+  hipLaunchKernelGGL(k_gather, dim3((unsigned)cdiv(rows_pad, 4)), dim3(256), 0, stream,
+                     (const char*)X, row_bytes, (const int*)idx, (const Counters*)ctr, xc,
+                     rows_pad, (const float*)nullptr, (float*)nullptr, dx32,
+                     (int)(pl.H * 4));
+  L.check();
+  hipLaunchKernelGGL(k_target<E>, dim3((unsigned)cdiv(rows_pad, 4)), dim3(256), 0, stream,
+                     (const char*)xc, (const char*)W, (int)pl.H, (const int*)tgt,
+                     (const Counters*)ctr, zt);
+  L.check();
+  if (L.err == hipSuccess) L.err = allow_big_lds(k_chunk_z<E>);
+  if (L.err == hipSuccess) L.err = allow_big_lds(k_bwd<E>);
+  for (int64_t ch = 0; ch < pl.nchunks && L.err == hipSuccess; ++ch) {
+    ChunkArgs ca;
+    ca.W = (const char*)W;
+    ca.row0 = (int)(ch * C);
+    ca.Xc = xc + (int64_t)ca.row0 * row_bytes;
+    ca.E = slab;
+    ca.part = part;
+    ca.ctr = ctr;
+    ca.cctr = cctr + ch;
+    ca.zt = zt;
+    ca.tgt = tgt;
+    ca.lse_c = lse_c;
+    ca.lse2 = lse2;
+    ca.bsum = bsum;
+    ca.H = (int)pl.H;
+    ca.V = (int)pl.V;
+    ca.Vp = (int)pl.Vp;
+    ca.C = C;
+    ca.VT = (int)pl.VT;
+    ca.TTc = TTc;
+    {
+      const int nb = (int)pad8(pl.VT * TTc);
+      Timed t("k_chunk_z", stream);
+      hipLaunchKernelGGL(k_chunk_z<E>, dim3((unsigned)nb), dim3(kThreads), kLdsBytes, stream,
+                         ca, nb);
+      L.check();
+    }
+    hipLaunchKernelGGL(k_chunk_lse, dim3((unsigned)TTc), dim3(256), 0, stream, ca);
+    L.check();
+    constexpr int per = 16 / E::kBytes;
+    hipLaunchKernelGGL(k_chunk_scale<E>, dim3((unsigned)cdiv(pl.Vp, 256 * per), (unsigned)C),
+                       dim3(256), 0, stream, ca);
+    L.check();
+    // dX and dW tiles of the chunk, one vocabulary block per launch
+    BwdArgs b;
+    b.W = (const char*)W;
+    b.Xc = ca.Xc;
+    b.lse2 = lse2;
+    b.tgt = tgt;
+    b.dx32 = dx32 + (int64_t)ca.row0 * pl.H;
+    b.dW = (char*)dW;
+    b.ctr = cctr + ch;
+    b.H = (int)pl.H;
+    b.V = (int)pl.V;
+    b.rows_pad = C;
+    b.Vb = (int)pl.Vp;   // the slab's row pitch
+    b.TT = TTc;
+    b.HT = HT;
+    b.dw_f32 = grad_f32;
+    b.dw_acc = ch > 0;
+    for (int64_t v0 = 0; v0 < pl.V && L.err == hipSuccess; v0 += kChunkVocabBlock) {
+      b.v0 = (int)v0;
+      b.vb = (int)std::min<int64_t>(kChunkVocabBlock, pl.V - v0);
+      b.VTb = (int)cdiv(b.vb, kTile);
+      b.G = slab + v0 * E::kBytes;
+      const int nb_dx = (int)pad8((int64_t)HT * TTc), nb_dw = (int)pad8((int64_t)HT * b.VTb);
+      Timed t("k_chunk_dxdw", stream);
+      hipLaunchKernelGGL(k_bwd<E>, dim3((unsigned)(nb_dx + nb_dw)), dim3(kThreads), kLdsBytes,
+                         stream, b, b, nb_dx, nb_dw, 0);
+      L.check();
+    }
+  }
+  hipLaunchKernelGGL(k_lse_out, dim3((unsigned)cdiv(pl.N, 256)), dim3(256), 0, stream,
+                     (const float*)lse_c, (const int*)rowpos, (int)pl.N, lse);
+  L.check();
+  hipLaunchKernelGGL(k_loss, dim3(1), dim3(256), 0, stream, (const float*)bsum,
+                     (int)(pl.nchunks * TTc), (const Counters*)ctr, reduction, loss, n_valid);
+  L.check();
   hipLaunchKernelGGL(k_dx_final, dim3((unsigned)cdiv(pl.N, 4)), dim3(256), 0, stream,
                      (const float*)dx32, (const int*)rowpos, (int)pl.N, (int)pl.H,
                      (char*)dX, grad_f32);
@@ -368,18 +553,85 @@ int flce_backward(const void* X, const void* W, const int64_t* labels, int64_t B
   const int gf32 = grad_dtype == FLCE_DTYPE_F32 ? 1 : 0;
   if (p.N == 0) {
     // no rows: dW = 0 (dX is empty)
-    const hipError_t e = hipMemsetAsync(dW, 0, (size_t)(p.V * p.H * ges), s);
-    if (status != nullptr && e == hipSuccess) {
+    zero_fill(dW, p.V * p.H * ges, s);
+    if (status != nullptr)
       hipLaunchKernelGGL(k_empty, dim3(1), dim3(1), 0, s, (float*)nullptr,
                          (int64_t*)nullptr, status);
-    }
-    return e == hipSuccess && hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
+    return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
   }
   if (dtype == FLCE_DTYPE_BF16)
     return backward_impl<BF16>(p, X, W, labels, B, T, ignore_index, reduction, shift, lse,
                                grad_scale, dX, dW, gf32, status, (char*)workspace, s);
   return backward_impl<F32>(p, X, W, labels, B, T, ignore_index, reduction, shift, lse,
                             grad_scale, dX, dW, gf32, status, (char*)workspace, s);
+}
+
+int flce_chunked_workspace_size(int64_t B, int64_t T, int64_t H, int64_t V, int dtype,
+                                size_t* bytes) {
+  if (bytes == nullptr) return FLCE_ERR_NULL;
+  ChunkPlan p;
+  const int rc = make_chunk_plan(B, T, H, V, dtype, &p);
+  if (rc != FLCE_OK) return rc;
+  *bytes = (size_t)p.total;
+  return FLCE_OK;
+}
+
+int flce_chunked(const void* X, const void* W, const int64_t* labels, int64_t B, int64_t T,
+                 int64_t H, int64_t V, int dtype, int64_t ignore_index, int reduction,
+                 int shift, const float* grad_scale, float* loss, float* lse,
+                 int64_t* n_valid, void* dX, void* dW, int grad_dtype, int32_t* status,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  ChunkPlan p;
+  const int rc = make_chunk_plan(B, T, H, V, dtype, &p);
+  if (rc != FLCE_OK) return rc;
+  if (reduction != FLCE_REDUCTION_MEAN && reduction != FLCE_REDUCTION_SUM)
+    return FLCE_ERR_REDUCTION;
+  if (grad_dtype != dtype && grad_dtype != FLCE_DTYPE_F32) return FLCE_ERR_DTYPE;
+  if (loss == nullptr || W == nullptr || dW == nullptr) return FLCE_ERR_NULL;
+  if (p.N > 0 && (X == nullptr || labels == nullptr || lse == nullptr || dX == nullptr))
+    return FLCE_ERR_NULL;
+  const int64_t ges = grad_dtype == FLCE_DTYPE_F32 ? 4 : 2;
+  if (!aligned16(W) || !aligned16(dW) || (p.N > 0 && (!aligned16(X) || !aligned16(dX))) ||
+      ((uintptr_t)labels & 7u) || ((uintptr_t)lse & 3u) || ((uintptr_t)loss & 3u))
+    return FLCE_ERR_ALIGN;
+  if (overlaps(dW, p.V * p.H * ges, W, p.V * p.H * p.es)) return FLCE_ERR_ALIAS;
+  if (p.N > 0 && overlaps(dX, p.N * p.H * ges, X, p.N * p.H * p.es)) return FLCE_ERR_ALIAS;
+  hipStream_t s = (hipStream_t)stream;
+  const int gf32 = grad_dtype == FLCE_DTYPE_F32 ? 1 : 0;
+  if (p.N == 0) {
+    zero_fill(dW, p.V * p.H * ges, s);
+    hipLaunchKernelGGL(k_empty, dim3(1), dim3(1), 0, s, loss, n_valid, status);
+    return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
+  }
+  if (workspace == nullptr) return FLCE_ERR_WORKSPACE;
+  if ((int64_t)workspace_bytes < p.total || !aligned16(workspace))
+    return FLCE_ERR_WORKSPACE;
+  if (dtype == FLCE_DTYPE_BF16)
+    return chunked_impl<BF16>(p, X, W, labels, B, T, ignore_index, reduction, shift,
+                              grad_scale, loss, lse, n_valid, dX, dW, gf32, status,
+                              (char*)workspace, s);
+  return chunked_impl<F32>(p, X, W, labels, B, T, ignore_index, reduction, shift, grad_scale,
+                           loss, lse, n_valid, dX, dW, gf32, status, (char*)workspace, s);
+}
+
+int flce_scale_grads(void* dX, int64_t nx, void* dW, int64_t nw, int grad_dtype,
+                     const float* scale, void* stream) {
+  if (scale == nullptr) return FLCE_ERR_NULL;
+  if (grad_dtype != FLCE_DTYPE_F32 && grad_dtype != FLCE_DTYPE_BF16) return FLCE_ERR_DTYPE;
+  const int per = grad_dtype == FLCE_DTYPE_F32 ? 4 : 8;
+  if (nx < 0 || nw < 0 || nx % per || nw % per) return FLCE_ERR_SHAPE;
+  if ((nx > 0 && dX == nullptr) || (nw > 0 && dW == nullptr)) return FLCE_ERR_NULL;
+  if ((nx > 0 && !aligned16(dX)) || (nw > 0 && !aligned16(dW))) return FLCE_ERR_ALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  const int f32 = grad_dtype == FLCE_DTYPE_F32;
+  for (int t = 0; t < 2; ++t) {
+    const int64_t chunks = (t == 0 ? nx : nw) / per;
+    if (chunks == 0) continue;
+    const int64_t blocks = std::min<int64_t>(cdiv(chunks, 256), 8192);
+    hipLaunchKernelGGL(k_scale_grads, dim3((unsigned)blocks), dim3(256), 0, s,
+                       (char*)(t == 0 ? dX : dW), chunks, f32, scale);
+  }
+  return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }
 
 int flce_set_timing(const char* kernel, void* const* events, int capacity, int* count) {

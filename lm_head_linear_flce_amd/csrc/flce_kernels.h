@@ -401,6 +401,7 @@ struct BwdArgs {
   int v0, vb;          // block start and width
   int TT, HT, VTb;     // token tiles (bound), hidden tiles, block vocab tiles
   int dw_f32;          // dW written as fp32 (else bf16)
+  int dw_acc;          // dW tiles add to dW (else overwrite it)
 };
 
 // G = c * 2^(z*log2e - lse2) for one tile, stored as G[token][vocab].
@@ -520,10 +521,43 @@ __device__ __forceinline__ void dw_store(const BwdArgs& a, const f32x16 (&acc)[4
   const int64_t left = ((int64_t)a.V * a.H - row0) * es;
   const int64_t span = (int64_t)kTile * a.H * es;
   const rsrc_t wr = make_rsrc((char*)a.dW + row0 * es, left < span ? left : span);
+  const int wave = threadIdx.x >> 6;
+  if (a.dw_acc) {
+    // dW += tile (chunked mode): rows of 4-value groups through LDS, the sum
+    // formed in fp32 and rounded once per call
+    auto off = [&](int o, int x0) {
+      const int m = wn * 128 + o, h = wm * 128 + x0;
+      const bool ok = !kMasked || (m < mlim && h < hlim);
+      return ok ? (m * a.H + h) * es : (int)0x80000000u;
+    };
+    if (a.dw_f32) {
+      rmw_quarter_f32(
+          smem + wave * 32768, lane, acc,
+          [&](int o, int x0) { return __builtin_bit_cast(f32x4, bload128(wr, off(o, x0))); },
+          [&](int o, int x0, f32x4 v) {
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), wr, off(o, x0),
+                                                   0, 0);
+          });
+    } else {
+      rmw_quarter_f32(
+          smem + wave * 32768, lane, acc,
+          [&](int o, int x0) {
+            const i32x2 u = __builtin_amdgcn_raw_buffer_load_b64(wr, off(o, x0), 0, 0);
+            return f32x4{bf2f((uint32_t)u[0] & 0xFFFFu), bf2f((uint32_t)u[0] >> 16),
+                         bf2f((uint32_t)u[1] & 0xFFFFu), bf2f((uint32_t)u[1] >> 16)};
+          },
+          [&](int o, int x0, f32x4 v) {
+            i32x2 pk;
+            pk[0] = pack_bf16(v[0], v[1]);
+            pk[1] = pack_bf16(v[2], v[3]);
+            __builtin_amdgcn_raw_buffer_store_b64(pk, wr, off(o, x0), 0, 0);
+          });
+    }
+    return;
+  }
   if (!a.dw_f32) {
     // bf16 rows through LDS: row o of the quarter is vocabulary entry
     // wn * 128 + o of the tile, inner x its hidden index wm * 128 + x
-    const int wave = threadIdx.x >> 6;
     store_quarter_bf16(
         smem + wave * 32768, lane, [&](int i, int j, int r) { return acc[i][j][r]; },
         [&](int o, int x0, i32x4 v) {
@@ -561,6 +595,7 @@ __device__ __forceinline__ void dw_tile(const BwdArgs& a, int item, lds_t* smem)
   int ht, vt;
   grouped(item, a.HT, a.VTb, ht, vt);
   const int n = a.ctr->n;
+  if (a.dw_acc && n == 0) return;   // nothing to add
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int es = E::kBytes;
@@ -667,6 +702,240 @@ void k_bwd(BwdArgs cur, BwdArgs nxt, int nb_dx, int nb_dw, int nb_g) {
   if (b < nb_g) g_tile<E>(nxt, xcd_item(b, nb_g), smem);
 }
 
+// ---------------------------------------------------------------------------
+// Chunked mode: loss, lse, dX and dW in one call, over chunks of C compacted
+// rows, with the chunk's softmax gradient over the whole vocabulary held in a
+// [C, Vp] slab (the pages' row-chunk recipe: three contractions instead of
+// four, memory proportional to the chunk).  Per chunk:
+//   k_chunk_z      logits tiles of the chunk's rows; each (row, 128-wide half
+//                  of a vocabulary tile) keeps its max M (log2 units) and
+//                  s = sum 2^(z log2e - M); the slab gets e = 2^(z log2e - M)
+//   k_chunk_lse    the rows' lse from the partials, row losses, the chunk's
+//                  counters (rows in the chunk)
+//   k_chunk_scale  G = c e 2^(M - lse2) - c [v = y], in place
+//   k_bwd          dX and dW tiles per vocabulary block of the slab (dW added
+//                  to the previous chunks' sum)
+// ---------------------------------------------------------------------------
+struct ChunkArgs {
+  const char* W;        // [V, H]
+  const char* Xc;       // the chunk's first compacted row
+  char* E;              // [C, Vp] slab
+  float2* part;         // [2 VT][C] (M, s)
+  const Counters* ctr;  // whole-call counters (n, status, c)
+  Counters* cctr;       // this chunk's counters (n = rows in the chunk)
+  const float* zt;      // [rows_pad] target logits (compacted rows)
+  const int* tgt;       // [rows_pad] targets (compacted rows)
+  float* lse_c;         // [rows_pad] lse per compacted row
+  float* lse2;          // [rows_pad] lse * log2(e)
+  float* bsum;          // [rows_pad / 256] row-loss block sums
+  int H, V, Vp, C, row0, VT, TTc;
+};
+
+__device__ __forceinline__ int chunk_rows(const ChunkArgs& a) {
+  const int r = a.ctr->n - a.row0;
+  return r < 0 ? 0 : (r < a.C ? r : a.C);
+}
+
+// Logits tile (vocabulary tile vt x token tile tau of the chunk).
+template <class E>
+__device__ __forceinline__ void z_tile(const ChunkArgs& a, int item, lds_t* smem) {
+  if (item >= a.VT * a.TTc) return;
+  int vt, tau;
+  grouped(item, a.VT, a.TTc, vt, tau);
+  if (tau * kTile >= chunk_rows(a)) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int ldb = a.H * E::kBytes;
+  const int steps = (ldb + kRowBytes - 1) / kRowBytes;
+  Opnd A, B;
+  A.base = a.W + (int64_t)vt * kTile * ldb;
+  A.bytes = (int64_t)(a.V - vt * kTile) * ldb;
+  A.ldb = ldb;
+  A.kbytes = ldb;
+  B.base = a.Xc + (int64_t)tau * kTile * ldb;
+  B.bytes = (int64_t)(a.C - tau * kTile) * ldb;
+  B.ldb = ldb;
+  B.kbytes = ldb;
+  f32x16 acc[4][4];
+  zero_acc(acc);
+  gemm_tile<E, LoadDirect, LoadDirect>(A, B, steps, smem, wm, wn, acc);
+
+  // vocabulary rows 32i + 8g + q < vlim lie inside V; lanes l and l ^ 32 hold
+  // the two halves of the 64 rows a wave keeps per token column
+  const int vlim = a.V - vt * kTile - wm * 128 - 4 * (lane >> 5);
+  float m2[4], sum[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        if (32 * i + 8 * (r >> 2) + (r & 3) < vlim) mx = fmaxf(mx, acc[i][j][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    m2[j] = mx == -INFINITY ? 0.f : mx * kLog2e;
+    sum[j] = 0.f;
+  }
+  auto val = [&](int i, int j, int r) {
+    const bool ok = 32 * i + 8 * (r >> 2) + (r & 3) < vlim;
+    const float e = ok ? __builtin_amdgcn_exp2f(fmaf(acc[i][j][r], kLog2e, -m2[j])) : 0.f;
+    sum[j] += e;
+    return e;
+  };
+  const rsrc_t er = make_rsrc(a.E, (int64_t)a.C * a.Vp * E::kBytes);
+  if constexpr (E::kBytes == 2) {
+    const int tok0 = tau * kTile + wn * 128, voc0 = vt * kTile + wm * 128;
+    store_quarter_bf16(smem + wave * 32768, lane, val, [&](int o, int x0, i32x4 v) {
+      __builtin_amdgcn_raw_buffer_store_b128(v, er, ((tok0 + o) * a.Vp + voc0 + x0) * 2, 0, 0);
+    });
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int tok = tau * kTile + acc_col(wn, j, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int row0 = acc_row(wm, i, 4 * g, lane);
+          const f32x4 fv = {val(i, j, 4 * g), val(i, j, 4 * g + 1), val(i, j, 4 * g + 2),
+                            val(i, j, 4 * g + 3)};
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, fv), er,
+                                                 (tok * a.Vp + vt * kTile + row0) * 4, 0, 0);
+        }
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float s2 = sum[j] + __shfl_xor(sum[j], 32);
+    if (lane < 32)
+      a.part[(int64_t)(2 * vt + wm) * a.C + tau * kTile + acc_col(wn, j, lane)] =
+          make_float2(m2[j], s2);
+  }
+}
+
+template <class E>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_chunk_z(ChunkArgs a, int nblocks) {
+  extern __shared__ __attribute__((aligned(16))) char smem_[];
+  z_tile<E>(a, xcd_item(blockIdx.x, nblocks), (lds_t*)smem_);
+}
+
+// One thread per row of the chunk: lse from the 2 VT partials (fixed order),
+// row loss lse - z_target, fixed-order block sums; block 0 also writes the
+// chunk's counters.
+__global__ __launch_bounds__(256) void k_chunk_lse(ChunkArgs a) {
+  __shared__ float red[256];
+  const int kl = blockIdx.x * 256 + threadIdx.x, k = a.row0 + kl;
+  const int nc = chunk_rows(a);
+  float li = 0.f;
+  if (kl < nc) {
+    float M = -INFINITY, S = 0.f;
+    for (int h = 0; h < 2 * a.VT; ++h) {
+      const float2 v = a.part[(int64_t)h * a.C + kl];
+      if (v.y == 0.f) continue;            // a half-tile past the vocabulary end
+      const float Mn = fmaxf(M, v.x);
+      S = S * exp2f(M - Mn) + v.y * exp2f(v.x - Mn);
+      M = Mn;
+    }
+    const float l2 = M + log2f(S);
+    a.lse2[k] = l2;
+    a.lse_c[k] = l2 * kLn2;
+    li = l2 * kLn2 - a.zt[k];
+  }
+  red[threadIdx.x] = li;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    if (a.row0 + blockIdx.x * 256 < a.row0 + a.C) a.bsum[(a.row0 >> 8) + blockIdx.x] = red[0];
+    if (blockIdx.x == 0) {
+      Counters c = *a.ctr;
+      c.n = nc;
+      c.fwd_p = 0;
+      *a.cctr = c;
+    }
+  }
+}
+
+// G = c e 2^(M - lse2) - c [v = y] in place; 16 bytes per thread, grid
+// (Vp / (256 * per), rows).  Rows from the chunk's row count up to the next
+// multiple of 64 (the last K step of the dW tiles) are zeroed; rows past that
+// are left alone.
+template <class E>
+__global__ __launch_bounds__(256) void k_chunk_scale(ChunkArgs a) {
+  constexpr int per = 16 / E::kBytes;
+  const int kl = blockIdx.y;
+  const int nc = chunk_rows(a);
+  if (kl >= ((nc + 63) & ~63)) return;
+  const int v = (blockIdx.x * 256 + threadIdx.x) * per;
+  if (v >= a.Vp) return;
+  i32x4* p = (i32x4*)(a.E + ((int64_t)kl * a.Vp + v) * E::kBytes);
+  if (kl >= nc) {
+    *p = i32x4{0, 0, 0, 0};
+    return;
+  }
+  const int k = a.row0 + kl;
+  const float c = a.ctr->c;
+  const float f = c * exp2f(a.part[(int64_t)(v >> 7) * a.C + kl].x - a.lse2[k]);
+  const int y = a.tgt[k] - v;
+  const i32x4 u = *p;
+  if constexpr (E::kBytes == 2) {
+    float g[8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      g[2 * q] = bf2f((uint32_t)u[q] & 0xFFFFu) * f;
+      g[2 * q + 1] = bf2f((uint32_t)u[q] >> 16) * f;
+    }
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      if (y == q) g[q] -= c;
+    *p = i32x4{pack_bf16(g[0], g[1]), pack_bf16(g[2], g[3]), pack_bf16(g[4], g[5]),
+               pack_bf16(g[6], g[7])};
+  } else {
+    f32x4 g = __builtin_bit_cast(f32x4, u);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      g[q] *= f;
+      if (y == q) g[q] -= c;
+    }
+    *p = __builtin_bit_cast(i32x4, g);
+  }
+}
+
+// lse of every original row (0 for ignored rows) after the chunks.
+__global__ __launch_bounds__(256) void k_lse_out(const float* __restrict__ lse_c,
+                                                 const int* __restrict__ rowpos, int N,
+                                                 float* __restrict__ lse_out) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= N) return;
+  const int k = rowpos[i];
+  lse_out[i] = k >= 0 ? lse_c[k] : 0.f;
+}
+
+// dX *= s, dW *= s (s a device scalar): gradients computed with grad_scale 1
+// rescaled by the upstream gradient.  Grid-stride, 16 bytes per thread step.
+__global__ __launch_bounds__(256) void k_scale_grads(char* __restrict__ p, int64_t chunks,
+                                                     int f32, const float* __restrict__ s) {
+  const float k = *s;
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < chunks; i += (int64_t)gridDim.x * 256) {
+    i32x4* q = (i32x4*)p + i;
+    i32x4 u = *q;
+    if (f32) {
+      f32x4 g = __builtin_bit_cast(f32x4, u);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) g[e] *= k;
+      u = __builtin_bit_cast(i32x4, g);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        u[e] = pack_bf16(bf2f((uint32_t)u[e] & 0xFFFFu) * k, bf2f((uint32_t)u[e] >> 16) * k);
+    }
+    *q = u;
+  }
+}
+
 __global__ __launch_bounds__(256) void k_dx_final(
     const float* __restrict__ dx32, const int* __restrict__ rowpos, int N, int H,
     char* __restrict__ dX, int out_f32) {
@@ -687,6 +956,12 @@ __global__ __launch_bounds__(256) void k_dx_final(
       *(i32x2*)((uint16_t*)dX + (int64_t)i * H + 4 * g) = pk;
     }
   }
+}
+
+// Zero fill, 16 bytes per thread step (graph-capture safe, unlike a memset).
+__global__ __launch_bounds__(256) void k_zero(char* __restrict__ p, int64_t chunks) {
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < chunks; i += (int64_t)gridDim.x * 256)
+    ((i32x4*)p)[i] = i32x4{0, 0, 0, 0};
 }
 
 // n == 0 rows (N == 0): loss = 0, n_valid = 0.

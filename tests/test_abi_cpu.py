@@ -125,3 +125,52 @@ def test_forward_host_checks(kw, code):
 ])
 def test_backward_host_checks(kw, code):
     assert bwd(**kw) == code
+
+
+def chk(**kw):
+    a = dict(X=P, W=2 * P, labels=3 * P, B=1, T=16, H=128, V=50, dtype=F.FLCE_DTYPE_BF16,
+             ignore_index=-100, reduction=F.FLCE_REDUCTION_MEAN, shift=0, grad_scale=0,
+             loss=4 * P, lse=5 * P, n_valid=0, dX=7 * P, dW=8 * P,
+             grad_dtype=F.FLCE_DTYPE_BF16, status=0, workspace=6 * P,
+             workspace_bytes=1 << 30, stream=0)
+    a.update(kw)
+    return F.flce_chunked(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(X=0), F.FLCE_ERR_NULL), (dict(W=0), F.FLCE_ERR_NULL),
+    (dict(labels=0), F.FLCE_ERR_NULL), (dict(loss=0), F.FLCE_ERR_NULL),
+    (dict(lse=0), F.FLCE_ERR_NULL), (dict(dX=0), F.FLCE_ERR_NULL),
+    (dict(dW=0), F.FLCE_ERR_NULL), (dict(H=100), F.FLCE_ERR_ALIGN),
+    (dict(X=P + 8), F.FLCE_ERR_ALIGN), (dict(dtype=3), F.FLCE_ERR_DTYPE),
+    (dict(grad_dtype=5), F.FLCE_ERR_DTYPE), (dict(reduction=2), F.FLCE_ERR_REDUCTION),
+    (dict(dX=P), F.FLCE_ERR_ALIAS), (dict(dW=2 * P + 64), F.FLCE_ERR_ALIAS),
+    (dict(workspace=0), F.FLCE_ERR_WORKSPACE), (dict(workspace_bytes=64), F.FLCE_ERR_WORKSPACE),
+    (dict(V=-5), F.FLCE_ERR_SHAPE),
+])
+def test_chunked_host_checks(kw, code):
+    assert chk(**kw) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    ((P, 64, 2 * P, 64, F.FLCE_DTYPE_BF16, 0, 0), F.FLCE_ERR_NULL),
+    ((P, 63, 2 * P, 64, F.FLCE_DTYPE_F32, 3 * P, 0), F.FLCE_ERR_SHAPE),
+    ((P, 64, 2 * P, 60, F.FLCE_DTYPE_BF16, 3 * P, 0), F.FLCE_ERR_SHAPE),
+    ((P, 64, 2 * P, 64, 7, 3 * P, 0), F.FLCE_ERR_DTYPE),
+    ((0, 64, 2 * P, 64, F.FLCE_DTYPE_BF16, 3 * P, 0), F.FLCE_ERR_NULL),
+    ((P + 4, 64, 2 * P, 64, F.FLCE_DTYPE_BF16, 3 * P, 0), F.FLCE_ERR_ALIGN),
+])
+def test_scale_grads_host_checks(args, code):
+    assert F.flce_scale_grads(*args) == code
+
+
+def test_chunked_workspace_is_bounded_by_the_chunk():
+    # the slab holds at most 1 GiB of one chunk's softmax gradient: beyond a
+    # few thousand rows the workspace grows only by the per-row buffers
+    H, V = 2048, 152064
+    w1 = F.flce_chunked_workspace_size(1, 8192, H, V, F.FLCE_DTYPE_BF16)
+    w2 = F.flce_chunked_workspace_size(1, 32768, H, V, F.FLCE_DTYPE_BF16)
+    per_row = (w2 - w1) / (32768 - 8192)
+    assert per_row < 4 * H + 2 * H + 64      # dX32 + X copy + a few words per row
+    assert w1 < (1 << 30) + 8192 * (6 * H + 64) + 2 * 3 * 8 * 594 * 3328 + (4 << 20)
+    assert w2 < 32768 * V * 2                # far below the logits

@@ -1,0 +1,98 @@
+"""Parity of the chunked mode (flce_chunked: loss, lse, dX, dW in one call over
+row chunks) with the float64 oracle, through the C ABI.
+
+The oracle is the same plain definition as for the forward / backward pair;
+the chunked schedule must reach the same result (the ms-swift PR "feat(sft):
+Add optional fused linear ce for qwen2/qwen3 on npu", "Mathematical
+Equivalence")."""
+import numpy as np
+import pytest
+import torch
+
+import lm_head_linear_flce_amd as F
+import oracle
+import synth
+from gpu_util import DEV, check, run, run_chunked, to_device
+from test_gpu_parity import SMALL, _ids
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[_ids(p) for p in SMALL])
+def test_chunked_small_parity(case):
+    name, ov = case
+    w = synth.workload(name, **ov)
+    print(f"[chunked] {name} {ov} N={w.N} H={w.H} V={w.V}", flush=True)
+    ref = oracle.flce(w.X, w.W, w.labels, ignore_index=w.ignore_index,
+                      reduction=w.reduction, shift=w.shift, mode="rows", chunk=1024)
+    got = run_chunked(w)
+    check(w, got, ref, what="chunked " + name)
+    _, valid = oracle.targets(w.labels, w.shift, w.ignore_index)
+    assert np.all(got["dX"][~valid] == 0.0)
+
+
+def test_chunked_several_chunks():
+    # V large enough that the [C, V] slab budget holds fewer rows than there
+    # are valid rows: dW is summed over three chunks
+    w = synth.workload("qwen2_7b_head", T=5003, H=64, V=262147, seed=201)
+    print(f"[chunked] several chunks N={w.N} V={w.V}", flush=True)
+    ref = oracle.flce(w.X, w.W, w.labels, ignore_index=w.ignore_index,
+                      reduction=w.reduction, shift=w.shift, mode="rows", chunk=512)
+    assert ref["n_valid"] > 2 * 1792
+    got = run_chunked(w)
+    check(w, got, ref, what="chunked several")
+    got32 = run_chunked(w, grad_dtype=torch.float32)
+    check(w, got32, ref, what="chunked several fp32")
+
+
+@pytest.mark.parametrize("case", SMALL[2:4], ids=[_ids(p) for p in SMALL[2:4]])
+def test_chunked_matches_recompute_path(case):
+    """Same loss / lse as the forward; gradients agree to bf16 rounding."""
+    name, ov = case
+    w = synth.workload(name, **ov)
+    a = run(w)
+    b = run_chunked(w)
+    assert abs(a["loss"] - b["loss"]) <= 1e-5 * abs(a["loss"])
+    np.testing.assert_allclose(b["lse"], a["lse"], rtol=0, atol=2e-5)
+    for k in ("dX", "dW"):
+        assert oracle.cosine(a[k], b[k]) > 0.9999
+
+
+def test_chunked_autograd_and_grad_scale():
+    w = synth.workload("qwen2_7b_head", T=300, H=128, V=700, seed=71)
+    X, W, lab = to_device(w)
+    Xr = X.detach().clone().requires_grad_(True)
+    Wr = W.detach().clone().requires_grad_(True)
+    loss = F.linear_cross_entropy(Xr, Wr, lab, ignore_index=-100, shift=True,
+                                  reduction="mean", mode="chunked")
+    (2.5 * loss).backward()
+    ref = oracle.flce(w.X, w.W, w.labels, shift=True, grad_scale=2.5)
+    assert abs(float(loss.detach()) - ref["loss"]) <= 2e-3 * abs(ref["loss"])
+    gx = Xr.grad.reshape(w.N, w.H).double().cpu().numpy()
+    gw = Wr.grad.double().cpu().numpy()
+    assert oracle.cosine(gx, ref["dX"]) >= 0.9999
+    assert oracle.cosine(gw, ref["dW"]) >= 0.9999
+    # the scale inside the call gives the same gradients
+    got = run_chunked(w, grad_scale=2.5)
+    assert oracle.cosine(got["dW"], ref["dW"]) >= 0.9999
+
+
+def test_chunked_no_valid_rows_and_bad_label():
+    w = synth.workload("long_context", T=500, H=64, V=300, seed=101)
+    w.labels[:] = -100
+    got = run_chunked(w)
+    assert got["n_valid"] == 0 and got["loss"] == 0.0
+    assert not got["dX"].any() and not got["dW"].any() and not got["lse"].any()
+    w = synth.workload("ragged_vocab", T=300, H=64, V=500, seed=121)
+    w.labels[0, 5] = w.V + 3
+    got = run_chunked(w)
+    assert got["status"] == F.FLCE_ERR_LABEL_RANGE
+    assert np.isnan(got["loss"]) and np.isnan(got["dW"]).any()
+
+
+def test_chunked_is_bitwise_deterministic():
+    w = synth.workload("ragged_vocab", T=900, H=256, V=3001, seed=81)
+    outs = [run_chunked(w) for _ in range(2)]
+    assert outs[0]["loss"] == outs[1]["loss"]
+    for k in ("lse", "dX", "dW"):
+        assert np.array_equal(outs[0][k], outs[1][k])

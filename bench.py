@@ -57,6 +57,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="qwen2_7b_head")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-chunked", action="store_true",
+                    help="skip the chunked-mode measurement")
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--summarize", metavar="DIR",
                     help="summarise the rocprofv3 output of PROFILE_COMMANDS under DIR "
@@ -228,6 +230,42 @@ def summarize(prof_dir, command):
     print(md)
 
 
+def chunked_mode(F, X, W, lab, w, dcode, dev, args, peak):
+    """The same workload through flce_chunked (one call: loss, lse, dX, dW over
+    row chunks; 6 n H V executed flop instead of 8), timed like the main step;
+    reported beside the recompute path, not instead of it."""
+    import torch
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    ws, ws_bytes = F.chunked_workspace(w.B, w.T, w.H, w.V, dcode, dev)
+
+    def step():
+        return F.chunked(X, W, lab, ignore_index=w.ignore_index, shift=w.shift,
+                         reduction=w.reduction, ws=ws)
+
+    out = step()
+    torch.cuda.synchronize()
+    peak_extra = torch.cuda.max_memory_allocated() - base
+    del out
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    N, H, V = w.N, w.H, w.V
+    print(f"[bench] chunked mode: {ms:.3f} ms/step", file=sys.stderr, flush=True)
+    return {"ms_per_step": ms, "tokens_per_s": N / (ms / 1e3),
+            "mfma_frac_model": 6.0 * N * H * V / (ms / 1e3) / peak,
+            "workspace_bytes": int(ws_bytes), "peak_extra_bytes": int(peak_extra),
+            "note": "flce_chunked: gradients formed with the logits over row chunks "
+                    "(bounded [C, V] slab), dW summed over chunks"}
+
+
 def main():
     args = parse()
     if args.summarize:
@@ -363,6 +401,8 @@ def main():
                      "peak": peak / 1e12, "unit": "TFLOP/s", "frac": ach / peak,
                      "traffic": measured_traffic(dom, w.name)},
     }
+    if not args.no_chunked:
+        result["chunked_mode"] = chunked_mode(F, X, W, lab, w, dcode, dev, args, peak)
     if not args.no_cpu_baseline:
         print("[bench] oracle on the host", file=sys.stderr, flush=True)
         result["cpu_baseline"] = oracle_baseline(w, args.cpu_rows)

@@ -317,7 +317,7 @@ constexpr int64_t kChunkVocabBlock = 16384;
 struct ChunkPlan {
   int64_t N, rows_pad, H, V, Vp, es, TT, VT;
   int64_t C, nchunks;       // chunk rows (multiple of 256), chunks covering rows_pad
-  int64_t o_ctr, o_idx, o_tgt, o_rowpos, o_xc, o_zt, o_lse_c, o_lse2, o_bsum, o_cctr;
+  int64_t o_ctr, o_idx, o_tgt, o_rowpos, o_xc, o_zt, o_lse_c, o_lse2, o_rloss, o_bsum, o_cctr;
   int64_t o_part, o_slab, o_dx32;
   int64_t total;
 };
@@ -354,7 +354,8 @@ int make_chunk_plan(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, Chunk
   q.o_zt = take(4 * q.rows_pad);
   q.o_lse_c = take(4 * q.rows_pad);
   q.o_lse2 = take(4 * q.rows_pad);
-  q.o_bsum = take(4 * q.nchunks * (q.C / kTile));
+  q.o_rloss = take(4 * q.rows_pad);
+  q.o_bsum = take(4 * q.TT);
   q.o_cctr = take(sizeof(Counters) * q.nchunks);
   q.o_part = take(8 * 2 * q.VT * q.C);
   q.o_slab = take(q.C * q.Vp * q.es);
@@ -379,6 +380,7 @@ int chunked_impl(const ChunkPlan& pl, const void* X, const void* W, const int64_
   float* zt = (float*)(ws + pl.o_zt);
   float* lse_c = (float*)(ws + pl.o_lse_c);
   float* lse2 = (float*)(ws + pl.o_lse2);
+  float* rloss = (float*)(ws + pl.o_rloss);
   float* bsum = (float*)(ws + pl.o_bsum);
   Counters* cctr = (Counters*)(ws + pl.o_cctr);
   float2* part = (float2*)(ws + pl.o_part);
@@ -416,7 +418,7 @@ int chunked_impl(const ChunkPlan& pl, const void* X, const void* W, const int64_
     ca.tgt = tgt;
     ca.lse_c = lse_c;
     ca.lse2 = lse2;
-    ca.bsum = bsum;
+    ca.rloss = rloss;
     ca.H = (int)pl.H;
     ca.V = (int)pl.V;
     ca.Vp = (int)pl.Vp;
@@ -430,7 +432,7 @@ int chunked_impl(const ChunkPlan& pl, const void* X, const void* W, const int64_
                          ca, nb);
       L.check();
     }
-    hipLaunchKernelGGL(k_chunk_lse, dim3((unsigned)TTc), dim3(256), 0, stream, ca);
+    hipLaunchKernelGGL(k_chunk_lse, dim3((unsigned)(C / 4)), dim3(256), 0, stream, ca);
     L.check();
     constexpr int per = 16 / E::kBytes;
     hipLaunchKernelGGL(k_chunk_scale<E>, dim3((unsigned)cdiv(pl.Vp, 256 * per), (unsigned)C),
@@ -468,8 +470,11 @@ int chunked_impl(const ChunkPlan& pl, const void* X, const void* W, const int64_
   hipLaunchKernelGGL(k_lse_out, dim3((unsigned)cdiv(pl.N, 256)), dim3(256), 0, stream,
                      (const float*)lse_c, (const int*)rowpos, (int)pl.N, lse);
   L.check();
-  hipLaunchKernelGGL(k_loss, dim3(1), dim3(256), 0, stream, (const float*)bsum,
-                     (int)(pl.nchunks * TTc), (const Counters*)ctr, reduction, loss, n_valid);
+  hipLaunchKernelGGL(k_block_sums, dim3((unsigned)pl.TT), dim3(256), 0, stream,
+                     (const float*)rloss, (const Counters*)ctr, bsum);
+  L.check();
+  hipLaunchKernelGGL(k_loss, dim3(1), dim3(256), 0, stream, (const float*)bsum, (int)pl.TT,
+                     (const Counters*)ctr, reduction, loss, n_valid);
   L.check();
   hipLaunchKernelGGL(k_dx_final, dim3((unsigned)cdiv(pl.N, 4)), dim3(256), 0, stream,
                      (const float*)dx32, (const int*)rowpos, (int)pl.N, (int)pl.H,

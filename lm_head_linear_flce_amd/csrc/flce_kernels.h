@@ -720,14 +720,14 @@ struct ChunkArgs {
   const char* W;        // [V, H]
   const char* Xc;       // the chunk's first compacted row
   char* E;              // [C, Vp] slab
-  float2* part;         // [2 VT][C] (M, s)
+  float2* part;         // [C][2 VT] (M, s)
   const Counters* ctr;  // whole-call counters (n, status, c)
   Counters* cctr;       // this chunk's counters (n = rows in the chunk)
   const float* zt;      // [rows_pad] target logits (compacted rows)
   const int* tgt;       // [rows_pad] targets (compacted rows)
   float* lse_c;         // [rows_pad] lse per compacted row
   float* lse2;          // [rows_pad] lse * log2(e)
-  float* bsum;          // [rows_pad / 256] row-loss block sums
+  float* rloss;         // [rows_pad] row losses lse - z_target
   int H, V, Vp, C, row0, VT, TTc;
 };
 
@@ -808,7 +808,7 @@ __device__ __forceinline__ void z_tile(const ChunkArgs& a, int item, lds_t* smem
   for (int j = 0; j < 4; ++j) {
     const float s2 = sum[j] + __shfl_xor(sum[j], 32);
     if (lane < 32)
-      a.part[(int64_t)(2 * vt + wm) * a.C + tau * kTile + acc_col(wn, j, lane)] =
+      a.part[(int64_t)(tau * kTile + acc_col(wn, j, lane)) * (2 * a.VT) + 2 * vt + wm] =
           make_float2(m2[j], s2);
   }
 }
@@ -820,43 +820,59 @@ void k_chunk_z(ChunkArgs a, int nblocks) {
   z_tile<E>(a, xcd_item(blockIdx.x, nblocks), (lds_t*)smem_);
 }
 
-// One thread per row of the chunk: lse from the 2 VT partials (fixed order),
-// row loss lse - z_target, fixed-order block sums; block 0 also writes the
-// chunk's counters.
+// One wave per row of the chunk: lse from the row's 2 VT partials (each lane
+// merges every 64th in order, then a fixed butterfly across lanes), the row
+// loss lse - z_target; thread 0 of block 0 also writes the chunk's counters.
+__device__ __forceinline__ void lse_pair_merge(float& M, float& S, float m2, float s2) {
+  const float Mn = fmaxf(M, m2);
+  if (Mn == -INFINITY) return;
+  S = S * exp2f(M - Mn) + s2 * exp2f(m2 - Mn);
+  M = Mn;
+}
+
 __global__ __launch_bounds__(256) void k_chunk_lse(ChunkArgs a) {
-  __shared__ float red[256];
-  const int kl = blockIdx.x * 256 + threadIdx.x, k = a.row0 + kl;
+  const int lane = threadIdx.x & 63;
+  const int kl = blockIdx.x * 4 + (threadIdx.x >> 6), k = a.row0 + kl;
   const int nc = chunk_rows(a);
-  float li = 0.f;
-  if (kl < nc) {
-    float M = -INFINITY, S = 0.f;
-    for (int h = 0; h < 2 * a.VT; ++h) {
-      const float2 v = a.part[(int64_t)h * a.C + kl];
-      if (v.y == 0.f) continue;            // a half-tile past the vocabulary end
-      const float Mn = fmaxf(M, v.x);
-      S = S * exp2f(M - Mn) + v.y * exp2f(v.x - Mn);
-      M = Mn;
-    }
+  if (blockIdx.x == 0 && threadIdx.x == 0) {
+    Counters c = *a.ctr;
+    c.n = nc;
+    c.fwd_p = 0;
+    *a.cctr = c;
+  }
+  if (kl >= nc) return;
+  const float2* pr = a.part + (int64_t)kl * (2 * a.VT);
+  float M = -INFINITY, S = 0.f;
+  for (int h = lane; h < 2 * a.VT; h += 64) {
+    const float2 v = pr[h];
+    if (v.y != 0.f) lse_pair_merge(M, S, v.x, v.y);   // empty half-tiles carry s = 0
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    const float m2 = __shfl_xor(M, d), s2 = __shfl_xor(S, d);
+    lse_pair_merge(M, S, m2, s2);
+  }
+  if (lane == 0) {
     const float l2 = M + log2f(S);
     a.lse2[k] = l2;
     a.lse_c[k] = l2 * kLn2;
-    li = l2 * kLn2 - a.zt[k];
+    a.rloss[k] = l2 * kLn2 - a.zt[k];
   }
-  red[threadIdx.x] = li;
+}
+
+// Fixed-order sums of 256 row losses (compacted rows; rows >= n add 0).
+__global__ __launch_bounds__(256) void k_block_sums(const float* __restrict__ rloss,
+                                                    const Counters* __restrict__ ctr,
+                                                    float* __restrict__ bsum) {
+  __shared__ float red[256];
+  const int k = blockIdx.x * 256 + threadIdx.x;
+  red[threadIdx.x] = k < ctr->n ? rloss[k] : 0.f;
   __syncthreads();
   for (int w = 128; w > 0; w >>= 1) {
     if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
     __syncthreads();
   }
-  if (threadIdx.x == 0) {
-    if (a.row0 + blockIdx.x * 256 < a.row0 + a.C) a.bsum[(a.row0 >> 8) + blockIdx.x] = red[0];
-    if (blockIdx.x == 0) {
-      Counters c = *a.ctr;
-      c.n = nc;
-      c.fwd_p = 0;
-      *a.cctr = c;
-    }
-  }
+  if (threadIdx.x == 0) bsum[blockIdx.x] = red[0];
 }
 
 // G = c e 2^(M - lse2) - c [v = y] in place; 16 bytes per thread, grid
@@ -878,7 +894,7 @@ __global__ __launch_bounds__(256) void k_chunk_scale(ChunkArgs a) {
   }
   const int k = a.row0 + kl;
   const float c = a.ctr->c;
-  const float f = c * exp2f(a.part[(int64_t)(v >> 7) * a.C + kl].x - a.lse2[k]);
+  const float f = c * exp2f(a.part[(int64_t)kl * (2 * a.VT) + (v >> 7)].x - a.lse2[k]);
   const int y = a.tgt[k] - v;
   const i32x4 u = *p;
   if constexpr (E::kBytes == 2) {

@@ -139,19 +139,24 @@ int flce_backward(const void* X, const void* W, const int64_t* labels,
  * computed at once; "Mathematical Equivalence": grad_weight summed over the
  * chunks).  One call returns loss, lse, dX and dW.  A chunk of C valid rows
  * keeps its softmax gradient over the whole vocabulary in a [C, V] slab of
- * the workspace (C chosen from a 1 GiB budget), so the logits are computed
- * once (three contractions, 6 n H V flop, instead of the forward + backward
- * pair's four) at the price of memory proportional to the chunk.
+ * the workspace, so the logits are computed once (three contractions,
+ * 6 n H V flop, instead of the forward + backward pair's four) at the price
+ * of memory proportional to the chunk.
+ *
+ * chunk_rows (both calls, which must agree): rows per chunk, rounded up to a
+ * multiple of 256 (the pages' CHUNK_SIZE); 0 = as many as a 1 GiB slab holds.
+ * Capped at the padded row count and at 2^31 bytes of slab.
  *
  * flce_chunked_workspace_size -- bytes of device scratch flce_chunked needs
- * (host-only arithmetic).  Arguments as flce_workspace_size.
+ * (host-only arithmetic).  Other arguments as flce_workspace_size.
  */
 int flce_chunked_workspace_size(int64_t B, int64_t T, int64_t H, int64_t V, int dtype,
-                                size_t* bytes);
+                                int64_t chunk_rows, size_t* bytes);
 
 /*
  * flce_chunked -- loss, per-row lse and the gradients of grad_scale * loss.
  *   X, W, labels, sizes, dtype, ignore_index, reduction, shift : as forward
+ *   chunk_rows    : as flce_chunked_workspace_size
  *   grad_scale    : float32 scalar, device; NULL = 1
  *   loss, lse, n_valid : as flce_forward's outputs
  *   dX, dW, grad_dtype : as flce_backward's outputs
@@ -164,7 +169,8 @@ int flce_chunked_workspace_size(int64_t B, int64_t T, int64_t H, int64_t V, int 
  */
 int flce_chunked(const void* X, const void* W, const int64_t* labels,
                  int64_t B, int64_t T, int64_t H, int64_t V, int dtype,
-                 int64_t ignore_index, int reduction, int shift, const float* grad_scale,
+                 int64_t ignore_index, int reduction, int shift, int64_t chunk_rows,
+                 const float* grad_scale,
                  float* loss, float* lse, int64_t* n_valid, void* dX, void* dW,
                  int grad_dtype, int32_t* status, void* workspace, size_t workspace_bytes,
                  void* stream);

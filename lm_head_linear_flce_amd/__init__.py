@@ -79,10 +79,11 @@ def _load() -> ctypes.CDLL:
     lib.flce_backward.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, i64, i32, i32,
                                   vp, vp, vp, vp, i32, vp, vp, sz, vp]
     lib.flce_backward.restype = i32
-    lib.flce_chunked_workspace_size.argtypes = [i64, i64, i64, i64, i32, ctypes.POINTER(sz)]
+    lib.flce_chunked_workspace_size.argtypes = [i64, i64, i64, i64, i32, i64,
+                                                ctypes.POINTER(sz)]
     lib.flce_chunked_workspace_size.restype = i32
-    lib.flce_chunked.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, i64, i32, i32, vp,
-                                 vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]
+    lib.flce_chunked.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, i64, i32, i32, i64,
+                                 vp, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]
     lib.flce_chunked.restype = i32
     lib.flce_scale_grads.argtypes = [vp, i64, vp, i64, i32, vp, vp]
     lib.flce_scale_grads.restype = i32
@@ -136,20 +137,22 @@ def flce_backward(X, W, labels, B, T, H, V, dtype, ignore_index, reduction, shif
                               stream or None)
 
 
-def flce_chunked_workspace_size(B: int, T: int, H: int, V: int, dtype: int) -> int:
+def flce_chunked_workspace_size(B: int, T: int, H: int, V: int, dtype: int,
+                                chunk_rows: int = 0) -> int:
     out = ctypes.c_size_t(0)
-    rc = _LIB.flce_chunked_workspace_size(B, T, H, V, dtype, ctypes.byref(out))
+    rc = _LIB.flce_chunked_workspace_size(B, T, H, V, dtype, chunk_rows, ctypes.byref(out))
     if rc != FLCE_OK:
         raise FlceError(rc, "flce_chunked_workspace_size")
     return int(out.value)
 
 
 def flce_chunked(X, W, labels, B, T, H, V, dtype, ignore_index, reduction, shift,
-                 grad_scale, loss, lse, n_valid, dX, dW, grad_dtype, status, workspace,
-                 workspace_bytes, stream) -> int:
+                 chunk_rows, grad_scale, loss, lse, n_valid, dX, dW, grad_dtype, status,
+                 workspace, workspace_bytes, stream) -> int:
     """Returns the status code (0 on success); raises nothing."""
     return _LIB.flce_chunked(X or None, W or None, labels or None, B, T, H, V, dtype,
-                             ignore_index, reduction, int(bool(shift)), grad_scale or None,
+                             ignore_index, reduction, int(bool(shift)), chunk_rows,
+                             grad_scale or None,
                              loss or None, lse or None, n_valid or None, dX or None,
                              dW or None, grad_dtype, status or None, workspace or None,
                              workspace_bytes, stream or None)
@@ -293,15 +296,17 @@ def backward(hidden, weight, labels, lse, grad_scale=None, ignore_index=-100,
     return dX, dW, status
 
 
-def chunked_workspace(B, T, H, V, dtype_code, device):
+def chunked_workspace(B, T, H, V, dtype_code, device, chunk_rows=0):
     torch = _torch()
-    nbytes = flce_chunked_workspace_size(B, T, H, V, dtype_code)
+    nbytes = flce_chunked_workspace_size(B, T, H, V, dtype_code, chunk_rows)
     return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device), nbytes
 
 
 def chunked(hidden, weight, labels, grad_scale=None, ignore_index=-100, shift=False,
-            reduction="mean", grad_dtype=None, ws=None):
-    """(loss, lse, n_valid, dX, dW, status) from one flce_chunked call."""
+            reduction="mean", grad_dtype=None, ws=None, chunk_rows=0):
+    """(loss, lse, n_valid, dX, dW, status) from one flce_chunked call; a
+    caller-provided ws must come from chunked_workspace with the same
+    chunk_rows."""
     torch = _torch()
     _check_tensors(hidden, weight, labels)
     B, T, H, V = _shape(hidden, weight, labels)
@@ -310,7 +315,7 @@ def chunked(hidden, weight, labels, grad_scale=None, ignore_index=-100, shift=Fa
     out_dtype = torch.float32 if gd == FLCE_DTYPE_F32 else hidden.dtype
     dev = hidden.device
     if ws is None:
-        ws, nbytes = chunked_workspace(B, T, H, V, dt, dev)
+        ws, nbytes = chunked_workspace(B, T, H, V, dt, dev, chunk_rows)
     else:
         nbytes = ws.numel()
     loss = torch.empty((), dtype=torch.float32, device=dev)
@@ -324,7 +329,8 @@ def chunked(hidden, weight, labels, grad_scale=None, ignore_index=-100, shift=Fa
         grad_scale = grad_scale.to(device=dev, dtype=torch.float32).contiguous()
         gs = grad_scale.data_ptr()
     rc = flce_chunked(hidden.data_ptr(), weight.data_ptr(), labels.data_ptr(), B, T, H, V,
-                      dt, int(ignore_index), _reduction_code(reduction), shift, gs,
+                      dt, int(ignore_index), _reduction_code(reduction), shift,
+                      int(chunk_rows), gs,
                       loss.data_ptr(), lse.data_ptr(), n_valid.data_ptr(), dX.data_ptr(),
                       dW.data_ptr(), gd, status.data_ptr(), ws.data_ptr(), nbytes,
                       _stream_handle(dev))

@@ -322,7 +322,11 @@ struct ChunkPlan {
   int64_t total;
 };
 
-int make_chunk_plan(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, ChunkPlan* p) {
+// chunk_rows: rows per chunk wanted (rounded up to 256); 0 = as many as the
+// 1 GiB slab budget allows.  Never more than the padded row count or what
+// 32-bit slab offsets reach.
+int make_chunk_plan(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, int64_t chunk_rows,
+                    ChunkPlan* p) {
   Plan base;
   const int rc = make_plan(B, T, H, V, dtype, &base);
   if (rc != FLCE_OK) return rc;
@@ -335,7 +339,10 @@ int make_chunk_plan(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, Chunk
   q.TT = base.TT;
   q.VT = base.VT;
   q.Vp = q.VT * kTile;
-  int64_t c = std::min(kChunkBudget, kMaxI32) / (q.Vp * q.es) / kTile * kTile;
+  if (chunk_rows < 0) return FLCE_ERR_SHAPE;
+  int64_t c = chunk_rows > 0 ? round_up(chunk_rows, kTile)
+                             : std::min(kChunkBudget, kMaxI32) / (q.Vp * q.es) / kTile * kTile;
+  c = std::min(c, kMaxI32 / (q.Vp * q.es) / kTile * kTile);
   if (c < kTile) c = kTile;
   q.C = std::min(c, q.rows_pad);
   if (q.C * q.Vp * q.es > kMaxI32) return FLCE_ERR_SHAPE;
@@ -572,10 +579,10 @@ int flce_backward(const void* X, const void* W, const int64_t* labels, int64_t B
 }
 
 int flce_chunked_workspace_size(int64_t B, int64_t T, int64_t H, int64_t V, int dtype,
-                                size_t* bytes) {
+                                int64_t chunk_rows, size_t* bytes) {
   if (bytes == nullptr) return FLCE_ERR_NULL;
   ChunkPlan p;
-  const int rc = make_chunk_plan(B, T, H, V, dtype, &p);
+  const int rc = make_chunk_plan(B, T, H, V, dtype, chunk_rows, &p);
   if (rc != FLCE_OK) return rc;
   *bytes = (size_t)p.total;
   return FLCE_OK;
@@ -583,11 +590,11 @@ int flce_chunked_workspace_size(int64_t B, int64_t T, int64_t H, int64_t V, int 
 
 int flce_chunked(const void* X, const void* W, const int64_t* labels, int64_t B, int64_t T,
                  int64_t H, int64_t V, int dtype, int64_t ignore_index, int reduction,
-                 int shift, const float* grad_scale, float* loss, float* lse,
-                 int64_t* n_valid, void* dX, void* dW, int grad_dtype, int32_t* status,
-                 void* workspace, size_t workspace_bytes, void* stream) {
+                 int shift, int64_t chunk_rows, const float* grad_scale, float* loss,
+                 float* lse, int64_t* n_valid, void* dX, void* dW, int grad_dtype,
+                 int32_t* status, void* workspace, size_t workspace_bytes, void* stream) {
   ChunkPlan p;
-  const int rc = make_chunk_plan(B, T, H, V, dtype, &p);
+  const int rc = make_chunk_plan(B, T, H, V, dtype, chunk_rows, &p);
   if (rc != FLCE_OK) return rc;
   if (reduction != FLCE_REDUCTION_MEAN && reduction != FLCE_REDUCTION_SUM)
     return FLCE_ERR_REDUCTION;

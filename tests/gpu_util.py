@@ -40,14 +40,14 @@ def run(w, grad_dtype=None, grad_scale=None, X=None, W=None, lab=None):
                 dW=dW.double().cpu().numpy())
 
 
-def run_chunked(w, grad_dtype=None, grad_scale=None):
+def run_chunked(w, grad_dtype=None, grad_scale=None, chunk_rows=0):
     """The same outputs from one flce_chunked call."""
     X, W, lab = to_device(w)
     gs = None if grad_scale is None else torch.tensor(grad_scale, dtype=torch.float32,
                                                         device=DEV)
     loss, lse, n_valid, dX, dW, status = F.chunked(
         X, W, lab, grad_scale=gs, ignore_index=w.ignore_index, shift=w.shift,
-        reduction=w.reduction, grad_dtype=grad_dtype)
+        reduction=w.reduction, grad_dtype=grad_dtype, chunk_rows=chunk_rows)
     torch.cuda.synchronize()
     return dict(loss=float(loss), lse=lse.double().cpu().numpy(),
                 n_valid=int(n_valid), status=int(status), bstatus=int(status),

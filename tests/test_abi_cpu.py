@@ -129,8 +129,8 @@ def test_backward_host_checks(kw, code):
 
 def chk(**kw):
     a = dict(X=P, W=2 * P, labels=3 * P, B=1, T=16, H=128, V=50, dtype=F.FLCE_DTYPE_BF16,
-             ignore_index=-100, reduction=F.FLCE_REDUCTION_MEAN, shift=0, grad_scale=0,
-             loss=4 * P, lse=5 * P, n_valid=0, dX=7 * P, dW=8 * P,
+             ignore_index=-100, reduction=F.FLCE_REDUCTION_MEAN, shift=0, chunk_rows=0,
+             grad_scale=0, loss=4 * P, lse=5 * P, n_valid=0, dX=7 * P, dW=8 * P,
              grad_dtype=F.FLCE_DTYPE_BF16, status=0, workspace=6 * P,
              workspace_bytes=1 << 30, stream=0)
     a.update(kw)
@@ -146,7 +146,7 @@ def chk(**kw):
     (dict(grad_dtype=5), F.FLCE_ERR_DTYPE), (dict(reduction=2), F.FLCE_ERR_REDUCTION),
     (dict(dX=P), F.FLCE_ERR_ALIAS), (dict(dW=2 * P + 64), F.FLCE_ERR_ALIAS),
     (dict(workspace=0), F.FLCE_ERR_WORKSPACE), (dict(workspace_bytes=64), F.FLCE_ERR_WORKSPACE),
-    (dict(V=-5), F.FLCE_ERR_SHAPE),
+    (dict(V=-5), F.FLCE_ERR_SHAPE), (dict(chunk_rows=-1), F.FLCE_ERR_SHAPE),
 ])
 def test_chunked_host_checks(kw, code):
     assert chk(**kw) == code
@@ -174,3 +174,17 @@ def test_chunked_workspace_is_bounded_by_the_chunk():
     assert per_row < 4 * H + 2 * H + 64      # dX32 + X copy + a few words per row
     assert w1 < (1 << 30) + 8192 * (6 * H + 64) + 2 * 3 * 8 * 594 * 3328 + (4 << 20)
     assert w2 < 32768 * V * 2                # far below the logits
+
+
+def test_chunk_rows_parameter():
+    # explicit chunk sizes round up to 256 rows; the slab is chunk x padded V
+    H, V, es = 1024, 50000, 2
+    vp = (V + 255) // 256 * 256
+    w512 = F.flce_chunked_workspace_size(1, 8192, H, V, F.FLCE_DTYPE_BF16, 512)
+    w300 = F.flce_chunked_workspace_size(1, 8192, H, V, F.FLCE_DTYPE_BF16, 300)
+    w1024 = F.flce_chunked_workspace_size(1, 8192, H, V, F.FLCE_DTYPE_BF16, 1024)
+    assert w300 == w512
+    assert w1024 - w512 >= 512 * vp * es
+    # at most the padded row count
+    assert (F.flce_chunked_workspace_size(1, 1000, H, V, F.FLCE_DTYPE_BF16, 1 << 20)
+            == F.flce_chunked_workspace_size(1, 1000, H, V, F.FLCE_DTYPE_BF16, 1024))

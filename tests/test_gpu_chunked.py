@@ -45,6 +45,18 @@ def test_chunked_several_chunks():
     check(w, got32, ref, what="chunked several fp32")
 
 
+@pytest.mark.parametrize("chunk_rows", [256, 700])
+def test_chunked_explicit_chunk_rows(chunk_rows):
+    # the pages' CHUNK_SIZE knob: many small chunks give the same result
+    w = synth.workload("qwen3_sft_batch", T=1500, H=392, V=5003, seed=37)
+    ref = oracle.flce(w.X, w.W, w.labels, ignore_index=w.ignore_index,
+                      reduction=w.reduction, shift=w.shift, mode="rows", chunk=1024)
+    assert ref["n_valid"] > 768
+    check(w, run_chunked(w, chunk_rows=chunk_rows), ref, what=f"chunk_rows={chunk_rows}")
+    check(w, run_chunked(w, chunk_rows=chunk_rows, grad_dtype=torch.float32), ref,
+          what=f"chunk_rows={chunk_rows} fp32")
+
+
 @pytest.mark.parametrize("case", SMALL[2:4], ids=[_ids(p) for p in SMALL[2:4]])
 def test_chunked_matches_recompute_path(case):
     """Same loss / lse as the forward; gradients agree to bf16 rounding."""

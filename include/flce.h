@@ -120,6 +120,10 @@ int flce_forward(const void* X, const void* W, const int64_t* labels,
  *   dW [V, H]     : out, device, fully overwritten
  *   grad_dtype    : element type of dX and dW: the input dtype, or
  *                   FLCE_DTYPE_F32 to receive the FP32 accumulators unrounded
+ *   dW_accumulate : 0 = dW is overwritten; 1 = the gradient is added to the
+ *                   dW already there (beta = 1: gradient accumulation over
+ *                   micro-batches, or the gradient buffer of a weight tied to
+ *                   the input embedding), summed in FP32 and rounded once
  *   status, workspace, workspace_bytes, stream : as forward
  * dX must not alias X and dW must not alias W.  The FP32 accumulation and the
  * single final rounding follow Megatron-LM PR "[Dev] Fix Linear-Cross-Entropy
@@ -129,7 +133,7 @@ int flce_backward(const void* X, const void* W, const int64_t* labels,
                   int64_t B, int64_t T, int64_t H, int64_t V, int dtype,
                   int64_t ignore_index, int reduction, int shift,
                   const float* lse, const float* grad_scale,
-                  void* dX, void* dW, int grad_dtype, int32_t* status,
+                  void* dX, void* dW, int grad_dtype, int dW_accumulate, int32_t* status,
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -159,7 +163,7 @@ int flce_chunked_workspace_size(int64_t B, int64_t T, int64_t H, int64_t V, int 
  *   chunk_rows    : as flce_chunked_workspace_size
  *   grad_scale    : float32 scalar, device; NULL = 1
  *   loss, lse, n_valid : as flce_forward's outputs
- *   dX, dW, grad_dtype : as flce_backward's outputs
+ *   dX, dW, grad_dtype, dW_accumulate : as flce_backward's
  *   status        : as forward (a bad label also makes the gradients NaN)
  *   workspace, workspace_bytes : device scratch of flce_chunked_workspace_size
  *   stream        : hipStream_t
@@ -172,8 +176,8 @@ int flce_chunked(const void* X, const void* W, const int64_t* labels,
                  int64_t ignore_index, int reduction, int shift, int64_t chunk_rows,
                  const float* grad_scale,
                  float* loss, float* lse, int64_t* n_valid, void* dX, void* dW,
-                 int grad_dtype, int32_t* status, void* workspace, size_t workspace_bytes,
-                 void* stream);
+                 int grad_dtype, int dW_accumulate, int32_t* status, void* workspace,
+                 size_t workspace_bytes, void* stream);
 
 /*
  * flce_scale_grads -- dX[0:nx] *= *scale and dW[0:nw] *= *scale in place (the

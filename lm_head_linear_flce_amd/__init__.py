@@ -77,13 +77,13 @@ def _load() -> ctypes.CDLL:
                                  vp, vp, vp, vp, vp, sz, vp]
     lib.flce_forward.restype = i32
     lib.flce_backward.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, i64, i32, i32,
-                                  vp, vp, vp, vp, i32, vp, vp, sz, vp]
+                                  vp, vp, vp, vp, i32, i32, vp, vp, sz, vp]
     lib.flce_backward.restype = i32
     lib.flce_chunked_workspace_size.argtypes = [i64, i64, i64, i64, i32, i64,
                                                 ctypes.POINTER(sz)]
     lib.flce_chunked_workspace_size.restype = i32
     lib.flce_chunked.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, i64, i32, i32, i64,
-                                 vp, vp, vp, vp, vp, vp, i32, vp, vp, sz, vp]
+                                 vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, sz, vp]
     lib.flce_chunked.restype = i32
     lib.flce_scale_grads.argtypes = [vp, i64, vp, i64, i32, vp, vp]
     lib.flce_scale_grads.restype = i32
@@ -127,14 +127,14 @@ def flce_forward(X, W, labels, B, T, H, V, dtype, ignore_index, reduction, shift
 
 
 def flce_backward(X, W, labels, B, T, H, V, dtype, ignore_index, reduction, shift,
-                  lse, grad_scale, dX, dW, grad_dtype, status, workspace,
+                  lse, grad_scale, dX, dW, grad_dtype, dW_accumulate, status, workspace,
                   workspace_bytes, stream) -> int:
     """Returns the status code (0 on success); raises nothing."""
     return _LIB.flce_backward(X or None, W or None, labels or None, B, T, H, V, dtype,
                               ignore_index, reduction, int(bool(shift)), lse or None,
                               grad_scale or None, dX or None, dW or None, grad_dtype,
-                              status or None, workspace or None, workspace_bytes,
-                              stream or None)
+                              int(bool(dW_accumulate)), status or None, workspace or None,
+                              workspace_bytes, stream or None)
 
 
 def flce_chunked_workspace_size(B: int, T: int, H: int, V: int, dtype: int,
@@ -147,15 +147,15 @@ def flce_chunked_workspace_size(B: int, T: int, H: int, V: int, dtype: int,
 
 
 def flce_chunked(X, W, labels, B, T, H, V, dtype, ignore_index, reduction, shift,
-                 chunk_rows, grad_scale, loss, lse, n_valid, dX, dW, grad_dtype, status,
-                 workspace, workspace_bytes, stream) -> int:
+                 chunk_rows, grad_scale, loss, lse, n_valid, dX, dW, grad_dtype,
+                 dW_accumulate, status, workspace, workspace_bytes, stream) -> int:
     """Returns the status code (0 on success); raises nothing."""
     return _LIB.flce_chunked(X or None, W or None, labels or None, B, T, H, V, dtype,
                              ignore_index, reduction, int(bool(shift)), chunk_rows,
-                             grad_scale or None,
-                             loss or None, lse or None, n_valid or None, dX or None,
-                             dW or None, grad_dtype, status or None, workspace or None,
-                             workspace_bytes, stream or None)
+                             grad_scale or None, loss or None, lse or None, n_valid or None,
+                             dX or None, dW or None, grad_dtype, int(bool(dW_accumulate)),
+                             status or None, workspace or None, workspace_bytes,
+                             stream or None)
 
 
 def flce_scale_grads(dX, nx, dW, nw, grad_dtype, scale, stream) -> int:
@@ -265,9 +265,24 @@ def forward(hidden, weight, labels, ignore_index=-100, shift=False, reduction="m
     return loss, lse, n_valid, status
 
 
+def _dw_out(dW, weight, out_dtype, accumulate):
+    torch = _torch()
+    if dW is None:
+        if accumulate:
+            raise ValueError("accumulate=True needs the dW tensor to add to")
+        return torch.empty(weight.shape, dtype=out_dtype, device=weight.device)
+    if (dW.shape != weight.shape or dW.dtype != out_dtype or dW.device != weight.device
+            or not dW.is_contiguous()):
+        raise ValueError("dW must be a contiguous tensor shaped like weight, in the "
+                         "gradient dtype, on the same device")
+    return dW
+
+
 def backward(hidden, weight, labels, lse, grad_scale=None, ignore_index=-100,
-             shift=False, reduction="mean", grad_dtype=None, ws=None):
-    """(dX, dW, status); grad_scale is a device float32 scalar or None (= 1)."""
+             shift=False, reduction="mean", grad_dtype=None, ws=None, dW=None,
+             accumulate=False):
+    """(dX, dW, status); grad_scale is a device float32 scalar or None (= 1).
+    dW: optional output tensor; accumulate=True adds the gradient to it."""
     torch = _torch()
     _check_tensors(hidden, weight, labels)
     B, T, H, V = _shape(hidden, weight, labels)
@@ -280,7 +295,7 @@ def backward(hidden, weight, labels, lse, grad_scale=None, ignore_index=-100,
     else:
         nbytes = ws.numel()
     dX = torch.empty(hidden.shape, dtype=out_dtype, device=dev)
-    dW = torch.empty(weight.shape, dtype=out_dtype, device=dev)
+    dW = _dw_out(dW, weight, out_dtype, accumulate)
     status = torch.empty((), dtype=torch.int32, device=dev)
     gs = 0
     if grad_scale is not None:
@@ -289,7 +304,7 @@ def backward(hidden, weight, labels, lse, grad_scale=None, ignore_index=-100,
     lse = lse.to(device=dev, dtype=torch.float32).contiguous()
     rc = flce_backward(hidden.data_ptr(), weight.data_ptr(), labels.data_ptr(), B, T, H,
                        V, dt, int(ignore_index), _reduction_code(reduction), shift,
-                       lse.data_ptr(), gs, dX.data_ptr(), dW.data_ptr(), gd,
+                       lse.data_ptr(), gs, dX.data_ptr(), dW.data_ptr(), gd, accumulate,
                        status.data_ptr(), ws.data_ptr(), nbytes, _stream_handle(dev))
     if rc != FLCE_OK:
         raise FlceError(rc, "flce_backward")
@@ -303,7 +318,8 @@ def chunked_workspace(B, T, H, V, dtype_code, device, chunk_rows=0):
 
 
 def chunked(hidden, weight, labels, grad_scale=None, ignore_index=-100, shift=False,
-            reduction="mean", grad_dtype=None, ws=None, chunk_rows=0):
+            reduction="mean", grad_dtype=None, ws=None, chunk_rows=0, dW=None,
+            accumulate=False):
     """(loss, lse, n_valid, dX, dW, status) from one flce_chunked call; a
     caller-provided ws must come from chunked_workspace with the same
     chunk_rows."""
@@ -323,7 +339,7 @@ def chunked(hidden, weight, labels, grad_scale=None, ignore_index=-100, shift=Fa
     n_valid = torch.empty((), dtype=torch.int64, device=dev)
     status = torch.empty((), dtype=torch.int32, device=dev)
     dX = torch.empty(hidden.shape, dtype=out_dtype, device=dev)
-    dW = torch.empty(weight.shape, dtype=out_dtype, device=dev)
+    dW = _dw_out(dW, weight, out_dtype, accumulate)
     gs = 0
     if grad_scale is not None:
         grad_scale = grad_scale.to(device=dev, dtype=torch.float32).contiguous()
@@ -332,7 +348,7 @@ def chunked(hidden, weight, labels, grad_scale=None, ignore_index=-100, shift=Fa
                       dt, int(ignore_index), _reduction_code(reduction), shift,
                       int(chunk_rows), gs,
                       loss.data_ptr(), lse.data_ptr(), n_valid.data_ptr(), dX.data_ptr(),
-                      dW.data_ptr(), gd, status.data_ptr(), ws.data_ptr(), nbytes,
+                      dW.data_ptr(), gd, accumulate, status.data_ptr(), ws.data_ptr(), nbytes,
                       _stream_handle(dev))
     if rc != FLCE_OK:
         raise FlceError(rc, "flce_chunked")

@@ -216,7 +216,7 @@ template <class E>
 int backward_impl(const Plan& pl, const void* X, const void* W, const int64_t* labels,
                   int64_t B, int64_t T, int64_t ignore_index, int reduction, int shift,
                   const float* lse, const float* grad_scale, void* dX, void* dW,
-                  int grad_f32, int32_t* status, char* ws, hipStream_t stream) {
+                  int grad_f32, int dw_acc, int32_t* status, char* ws, hipStream_t stream) {
   Launch L{stream};
   Counters* ctr = (Counters*)(ws + pl.o_ctr);
   int* idx = (int*)(ws + pl.o_idx);
@@ -254,7 +254,7 @@ int backward_impl(const Plan& pl, const void* X, const void* W, const int64_t* l
   a.TT = (int)pl.TT;
   a.HT = (int)cdiv(pl.H, kTile);
   a.dw_f32 = grad_f32;
-  a.dw_acc = 0;
+  a.dw_acc = dw_acc;
   a.v0 = a.vb = a.VTb = 0;
   const int64_t slab = pl.rows_pad * pl.Vb * pl.es;
   auto block = [&](int64_t b) {
@@ -376,7 +376,7 @@ template <class E>
 int chunked_impl(const ChunkPlan& pl, const void* X, const void* W, const int64_t* labels,
                  int64_t B, int64_t T, int64_t ignore_index, int reduction, int shift,
                  const float* grad_scale, float* loss, float* lse, int64_t* n_valid,
-                 void* dX, void* dW, int grad_f32, int32_t* status, char* ws,
+                 void* dX, void* dW, int grad_f32, int dw_acc, int32_t* status, char* ws,
                  hipStream_t stream) {
   Launch L{stream};
   Counters* ctr = (Counters*)(ws + pl.o_ctr);
@@ -461,7 +461,7 @@ int chunked_impl(const ChunkPlan& pl, const void* X, const void* W, const int64_
     b.TT = TTc;
     b.HT = HT;
     b.dw_f32 = grad_f32;
-    b.dw_acc = ch > 0;
+    b.dw_acc = ch > 0 || dw_acc;
     for (int64_t v0 = 0; v0 < pl.V && L.err == hipSuccess; v0 += kChunkVocabBlock) {
       b.v0 = (int)v0;
       b.vb = (int)std::min<int64_t>(kChunkVocabBlock, pl.V - v0);
@@ -541,8 +541,8 @@ int flce_forward(const void* X, const void* W, const int64_t* labels, int64_t B,
 int flce_backward(const void* X, const void* W, const int64_t* labels, int64_t B,
                   int64_t T, int64_t H, int64_t V, int dtype, int64_t ignore_index,
                   int reduction, int shift, const float* lse, const float* grad_scale,
-                  void* dX, void* dW, int grad_dtype, int32_t* status, void* workspace,
-                  size_t workspace_bytes, void* stream) {
+                  void* dX, void* dW, int grad_dtype, int dW_accumulate, int32_t* status,
+                  void* workspace, size_t workspace_bytes, void* stream) {
   Plan p;
   int rc = make_plan(B, T, H, V, dtype, &p);
   if (rc != FLCE_OK) return rc;
@@ -564,8 +564,8 @@ int flce_backward(const void* X, const void* W, const int64_t* labels, int64_t B
   hipStream_t s = (hipStream_t)stream;
   const int gf32 = grad_dtype == FLCE_DTYPE_F32 ? 1 : 0;
   if (p.N == 0) {
-    // no rows: dW = 0 (dX is empty)
-    zero_fill(dW, p.V * p.H * ges, s);
+    // no rows: dW = 0 (dX is empty); accumulating adds nothing
+    if (!dW_accumulate) zero_fill(dW, p.V * p.H * ges, s);
     if (status != nullptr)
       hipLaunchKernelGGL(k_empty, dim3(1), dim3(1), 0, s, (float*)nullptr,
                          (int64_t*)nullptr, status);
@@ -573,9 +573,11 @@ int flce_backward(const void* X, const void* W, const int64_t* labels, int64_t B
   }
   if (dtype == FLCE_DTYPE_BF16)
     return backward_impl<BF16>(p, X, W, labels, B, T, ignore_index, reduction, shift, lse,
-                               grad_scale, dX, dW, gf32, status, (char*)workspace, s);
+                               grad_scale, dX, dW, gf32, dW_accumulate ? 1 : 0, status,
+                               (char*)workspace, s);
   return backward_impl<F32>(p, X, W, labels, B, T, ignore_index, reduction, shift, lse,
-                            grad_scale, dX, dW, gf32, status, (char*)workspace, s);
+                            grad_scale, dX, dW, gf32, dW_accumulate ? 1 : 0, status,
+                            (char*)workspace, s);
 }
 
 int flce_chunked_workspace_size(int64_t B, int64_t T, int64_t H, int64_t V, int dtype,
@@ -592,7 +594,8 @@ int flce_chunked(const void* X, const void* W, const int64_t* labels, int64_t B,
                  int64_t H, int64_t V, int dtype, int64_t ignore_index, int reduction,
                  int shift, int64_t chunk_rows, const float* grad_scale, float* loss,
                  float* lse, int64_t* n_valid, void* dX, void* dW, int grad_dtype,
-                 int32_t* status, void* workspace, size_t workspace_bytes, void* stream) {
+                 int dW_accumulate, int32_t* status, void* workspace, size_t workspace_bytes,
+                 void* stream) {
   ChunkPlan p;
   const int rc = make_chunk_plan(B, T, H, V, dtype, chunk_rows, &p);
   if (rc != FLCE_OK) return rc;
@@ -611,7 +614,7 @@ int flce_chunked(const void* X, const void* W, const int64_t* labels, int64_t B,
   hipStream_t s = (hipStream_t)stream;
   const int gf32 = grad_dtype == FLCE_DTYPE_F32 ? 1 : 0;
   if (p.N == 0) {
-    zero_fill(dW, p.V * p.H * ges, s);
+    if (!dW_accumulate) zero_fill(dW, p.V * p.H * ges, s);
     hipLaunchKernelGGL(k_empty, dim3(1), dim3(1), 0, s, loss, n_valid, status);
     return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
   }
@@ -620,10 +623,11 @@ int flce_chunked(const void* X, const void* W, const int64_t* labels, int64_t B,
     return FLCE_ERR_WORKSPACE;
   if (dtype == FLCE_DTYPE_BF16)
     return chunked_impl<BF16>(p, X, W, labels, B, T, ignore_index, reduction, shift,
-                              grad_scale, loss, lse, n_valid, dX, dW, gf32, status,
-                              (char*)workspace, s);
+                              grad_scale, loss, lse, n_valid, dX, dW, gf32,
+                              dW_accumulate ? 1 : 0, status, (char*)workspace, s);
   return chunked_impl<F32>(p, X, W, labels, B, T, ignore_index, reduction, shift, grad_scale,
-                           loss, lse, n_valid, dX, dW, gf32, status, (char*)workspace, s);
+                           loss, lse, n_valid, dX, dW, gf32, dW_accumulate ? 1 : 0, status,
+                           (char*)workspace, s);
 }
 
 int flce_scale_grads(void* dX, int64_t nx, void* dW, int64_t nw, int grad_dtype,

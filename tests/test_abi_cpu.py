@@ -97,8 +97,8 @@ def fwd(**kw):
 def bwd(**kw):
     a = dict(X=P, W=2 * P, labels=3 * P, B=1, T=16, H=128, V=50, dtype=F.FLCE_DTYPE_BF16,
              ignore_index=-100, reduction=F.FLCE_REDUCTION_MEAN, shift=0, lse=5 * P,
-             grad_scale=0, dX=7 * P, dW=8 * P, grad_dtype=F.FLCE_DTYPE_BF16, status=0,
-             workspace=6 * P, workspace_bytes=1 << 30, stream=0)
+             grad_scale=0, dX=7 * P, dW=8 * P, grad_dtype=F.FLCE_DTYPE_BF16, dW_accumulate=0,
+             status=0, workspace=6 * P, workspace_bytes=1 << 30, stream=0)
     a.update(kw)
     return F.flce_backward(*a.values())
 
@@ -131,7 +131,7 @@ def chk(**kw):
     a = dict(X=P, W=2 * P, labels=3 * P, B=1, T=16, H=128, V=50, dtype=F.FLCE_DTYPE_BF16,
              ignore_index=-100, reduction=F.FLCE_REDUCTION_MEAN, shift=0, chunk_rows=0,
              grad_scale=0, loss=4 * P, lse=5 * P, n_valid=0, dX=7 * P, dW=8 * P,
-             grad_dtype=F.FLCE_DTYPE_BF16, status=0, workspace=6 * P,
+             grad_dtype=F.FLCE_DTYPE_BF16, dW_accumulate=0, status=0, workspace=6 * P,
              workspace_bytes=1 << 30, stream=0)
     a.update(kw)
     return F.flce_chunked(*a.values())

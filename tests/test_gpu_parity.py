@@ -214,3 +214,33 @@ def test_full_size_against_stored_oracle(name):
     bound = 2 * u * c * np.abs(Xv).sum(axis=0) + u * np.abs(got["dW"]).sum(axis=0)
     colsum = np.abs(got["dW"].sum(axis=0))
     assert np.all(colsum <= 1.01 * bound + 1e-12), (colsum / bound).max()
+
+
+@pytest.mark.parametrize("grad_dtype", [None, torch.float32])
+@pytest.mark.parametrize("mode", ["recompute", "chunked"])
+def test_dW_accumulates_over_micro_batches(mode, grad_dtype):
+    """dW_accumulate = 1 adds the gradient to dW (gradient accumulation; a
+    weight tied to the input embedding): two micro-batches sharing W give the
+    oracle's summed dW."""
+    wa = synth.workload("qwen2_7b_head", T=700, H=256, V=3001, seed=161)
+    wb = synth.workload("qwen2_7b_head", T=500, H=256, V=3001, seed=162)
+    wb.W = wa.W
+    refs = [oracle.flce(w.X, w.W, w.labels, shift=w.shift) for w in (wa, wb)]
+    dW = None
+    for k, w in enumerate((wa, wb)):
+        X, W, lab = to_device(w)
+        if mode == "recompute":
+            _, lse, _, _ = F.forward(X, W, lab, -100, w.shift, w.reduction)
+            dX, dW, st = F.backward(X, W, lab, lse, shift=w.shift, reduction=w.reduction,
+                                    grad_dtype=grad_dtype, dW=dW, accumulate=k > 0)
+        else:
+            _, _, _, dX, dW, st = F.chunked(X, W, lab, shift=w.shift, reduction=w.reduction,
+                                            grad_dtype=grad_dtype, dW=dW, accumulate=k > 0)
+    torch.cuda.synchronize()
+    assert int(st) == 0
+    want = refs[0]["dW"] + refs[1]["dW"]
+    got = dW.double().cpu().numpy()
+    assert oracle.cosine(got, want) >= 0.9999
+    assert np.abs(got - want).max() <= 1e-2 * np.abs(want).max()
+    gx = dX.reshape(wb.N, wb.H).double().cpu().numpy()
+    assert oracle.cosine(gx, refs[1]["dX"]) >= 0.9999

@@ -17,9 +17,13 @@ values the GPU receives (bf16 inputs are upcast without rounding):
   logits    Z = X . W^T (no bias)  -- ms-swift PR "Add optional fused linear ce
             for qwen2/qwen3 on npu", section "Mathematical Equivalence".
   lse_i     = log sum_v exp(Z_iv)  (computed as m_i + log sum exp(Z_iv - m_i)).
-  loss      = sum_valid (lse_i - Z_{i,y_i}) / n   (mean)  or the plain sum.
+  loss      = sum_valid (lse_i - Z_{i,y_i}) / n   (mean)  or the plain sum;
+            reduction "none": the per-row losses l_i = lse_i - Z_{i,y_i}
+            (0 on ignored rows), whose negatives are the target log-probs.
   G         = c (softmax(Z_i) - onehot(y_i)) on valid rows, 0 elsewhere,
-            c = grad_scale / n (mean) or grad_scale (sum).
+            c = grad_scale / n (mean) or grad_scale (sum); with "none",
+            grad_scale may be a per-row array g (the upstream gradient of the
+            per-row losses) and row i uses c_i = g_i.
   grads     dX = G . W and dW = G^T . X, the two identities of the same section.
 
 Three evaluation orders are provided, all meant to agree to rounding:
@@ -80,12 +84,20 @@ def _check_range(y, valid, V):
         raise ValueError(f"target {int(y[i])} of row {i} is outside [0, {V})")
 
 
-def _scale(reduction, n, grad_scale):
+def _scale(reduction, n, grad_scale, N):
+    """Gradient factor: a scalar, or for "none" a per-row array [N]."""
     if reduction == "mean":
         return 0.0 if n == 0 else grad_scale / n
     if reduction == "sum":
         return float(grad_scale)
+    if reduction == "none":
+        return np.broadcast_to(_as_f64(grad_scale), (N,)).copy()
     raise ValueError(f"unknown reduction {reduction!r}")
+
+
+def _rows_factor(c, rows):
+    """c for the given rows, shaped to scale rows of G."""
+    return c[rows][:, None] if np.ndim(c) else c
 
 
 def _row_lse(Z):
@@ -137,8 +149,8 @@ def flce(X, W, labels, *, ignore_index=-100, reduction="mean", shift=False,
         raise ValueError("labels and hidden states disagree on the row count")
     _check_range(y, valid, V)
     n = int(valid.sum())
-    c = _scale(reduction, n, grad_scale)
-    out = dict(n_valid=n, lse=np.zeros(N), loss=0.0)
+    c = _scale(reduction, n, grad_scale, N)
+    out = dict(n_valid=n, lse=np.zeros(N), loss=np.zeros(N) if reduction == "none" else 0.0)
     if grads:
         out["dX"] = np.zeros((N, H))
         out["dW"] = np.zeros((V, H))
@@ -155,8 +167,14 @@ def flce(X, W, labels, *, ignore_index=-100, reduction="mean", shift=False,
     return out
 
 
-def _finish_loss(row_loss_sum, reduction, n):
-    return row_loss_sum / n if reduction == "mean" else row_loss_sum
+def _finish_loss(out, rows, row_losses, reduction, n):
+    """Store the loss: mean or sum of the valid rows' losses, or (none) the
+    per-row losses at their rows."""
+    if reduction == "none":
+        out["loss"][rows] = row_losses
+    else:
+        s = float(np.sum(row_losses))
+        out["loss"] = s / n if reduction == "mean" else s
 
 
 def _global(X, W, y, valid, c, reduction, n, out, grads):
@@ -167,11 +185,11 @@ def _global(X, W, y, valid, c, reduction, n, out, grads):
     lse = _row_lse(Z)
     zt = Z[np.arange(n), yv]
     out["lse"][rows] = lse
-    out["loss"] = _finish_loss(float(np.sum(lse - zt)), reduction, n)
+    _finish_loss(out, rows, lse - zt, reduction, n)
     if grads:
         P = np.exp(Z - lse[:, None])
         P[np.arange(n), yv] -= 1.0
-        G = c * P
+        G = _rows_factor(c, rows) * P
         out["dX"][rows] = G @ W
         out["dW"][:] = G.T @ Xv
 
@@ -180,7 +198,7 @@ def _rows(X, W, y, valid, c, reduction, n, out, grads, chunk):
     """Chunks along the flattened sequence; each chunk is a small linear +
     cross-entropy whose weight gradient is summed into one buffer."""
     N = X.shape[0]
-    total = 0.0
+    all_rows, all_losses = [], []
     for r0 in range(0, N, chunk):
         sl = slice(r0, min(N, r0 + chunk))
         vmask = valid[sl]
@@ -192,15 +210,16 @@ def _rows(X, W, y, valid, c, reduction, n, out, grads, chunk):
         Z = Xc @ W.T
         lse = _row_lse(Z)
         k = np.arange(len(rows))
-        total += float(np.sum(lse - Z[k, yc]))
+        all_rows.append(rows)
+        all_losses.append(lse - Z[k, yc])
         out["lse"][rows] = lse
         if grads:
             P = np.exp(Z - lse[:, None])
             P[k, yc] -= 1.0
-            G = c * P
+            G = _rows_factor(c, rows) * P
             out["dX"][rows] = G @ W
             out["dW"] += G.T @ Xc
-    out["loss"] = _finish_loss(total, reduction, n)
+    _finish_loss(out, np.concatenate(all_rows), np.concatenate(all_losses), reduction, n)
 
 
 def _vocab(X, W, y, valid, c, reduction, n, out, grads, chunk, acc):
@@ -223,7 +242,7 @@ def _vocab(X, W, y, valid, c, reduction, n, out, grads, chunk, acc):
         zt[hit] = Z[np.flatnonzero(hit), yv[hit] - v0]
     lse = m + np.log(s)
     out["lse"][rows] = lse
-    out["loss"] = _finish_loss(float(np.sum(lse - zt)), reduction, n)
+    _finish_loss(out, rows, lse - zt, reduction, n)
     if not grads:
         return
     dX = np.zeros((n, X.shape[1]))
@@ -233,7 +252,7 @@ def _vocab(X, W, y, valid, c, reduction, n, out, grads, chunk, acc):
         P = np.exp(Z - lse[:, None])
         hit = np.flatnonzero((yv >= v0) & (yv < v1))
         P[hit, yv[hit] - v0] -= 1.0
-        G = c * P
+        G = _rows_factor(c, rows) * P
         if acc == "f64":
             piece = G @ W[v0:v1]
         else:
@@ -274,7 +293,7 @@ def forward_rows(X, W, labels, *, ignore_index=-100, reduction="mean",
         total += float(np.sum(l - Z[np.arange(len(r)), y[r]]))
     loss = None
     if rows is None:
-        loss = 0.0 if n == 0 else _finish_loss(total, reduction, n)
+        loss = 0.0 if n == 0 else (total / n if reduction == "mean" else total)
     return dict(lse=lse, loss=loss, n_valid=n, y=y, valid=valid)
 
 

@@ -358,3 +358,55 @@ def test_row_helpers_match_full_oracle():
             np.testing.assert_allclose(
                 oracle.dw_rows(X, W, f["y"], f["valid"], f["lse"], c, vids, chunk=9),
                 r["dW"][vids], rtol=1e-12, atol=1e-16)
+
+
+# --- C15: reduction "none" (per-token losses, per-token upstream gradients) --
+
+@pytest.mark.parametrize("mode", ["global", "rows", "vocab"])
+def test_per_row_losses_are_negative_log_softmax(mode):
+    """Each valid row's loss is -log_softmax(z_i)[y_i] (scipy's routine on the
+    textbook logits), 0 on ignored rows; the target log-prob is its negative."""
+    from scipy.special import log_softmax
+    X, W, lab = _problem(15, B=2, T=7, H=5, V=13)
+    r = oracle.flce(X, W, lab, shift=True, reduction="none", mode=mode, chunk=3)
+    y, valid = oracle.targets(lab, True)
+    ls = log_softmax(X @ W.T, axis=1)
+    want = np.where(valid, -ls[np.arange(len(y)), np.where(valid, y, 0)], 0.0)
+    np.testing.assert_allclose(r["loss"], want, rtol=1e-13, atol=1e-13)
+    s = oracle.flce(X, W, lab, shift=True, reduction="sum", grads=False)
+    assert float(np.sum(r["loss"])) == pytest.approx(s["loss"], rel=1e-13)
+
+
+@pytest.mark.parametrize("mode", ["global", "rows", "vocab"])
+def test_per_row_upstream_gradient_finite_differences(mode):
+    """With reduction "none" and per-row weights g, dX and dW are the
+    gradients of sum_i g_i l_i (central finite differences)."""
+    X, W, lab = _problem(16, B=2, T=3, H=4, V=5, ignore_frac=0.2)
+    g = np.random.default_rng(0).standard_normal(X.shape[0])
+    r = oracle.flce(X, W, lab, reduction="none", grad_scale=g, mode=mode, chunk=2)
+
+    def loss(Xa, Wa):
+        return float(g @ oracle.flce(Xa, Wa, lab, reduction="none", grads=False)["loss"])
+
+    h = 1e-6
+    for name, A, G in (("X", X, r["dX"]), ("W", W, r["dW"])):
+        num = np.zeros_like(A)
+        for idx in np.ndindex(A.shape):
+            Ap = A.copy()
+            Am = A.copy()
+            Ap[idx] += h
+            Am[idx] -= h
+            if name == "X":
+                num[idx] = (loss(Ap, W) - loss(Am, W)) / (2 * h)
+            else:
+                num[idx] = (loss(X, Ap) - loss(X, Am)) / (2 * h)
+        assert np.abs(num - G).max() <= 1e-7 * np.abs(num).max(), name
+
+
+def test_uniform_per_row_weights_equal_mean():
+    X, W, lab = _problem(17, B=2, T=8, H=6, V=9)
+    m = oracle.flce(X, W, lab, reduction="mean", grad_scale=0.8)
+    n = m["n_valid"]
+    r = oracle.flce(X, W, lab, reduction="none", grad_scale=np.full(X.shape[0], 0.8 / n))
+    np.testing.assert_allclose(r["dX"], m["dX"], rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(r["dW"], m["dW"], rtol=1e-12, atol=1e-15)

@@ -70,9 +70,13 @@ extern "C" {
 #define FLCE_DTYPE_F32 0
 #define FLCE_DTYPE_BF16 1
 
-/* reductions */
+/* reductions.  NONE returns the per-row losses l_i = lse_i - z_{i,y_i} (their
+ * negatives are the target log-probs) and takes a per-row upstream gradient:
+ * the per-token outputs that RL objectives need (the ms-swift PR lists
+ * GRPO/PPO under "Limitations" because mean cross-entropy is not enough). */
 #define FLCE_REDUCTION_MEAN 0
 #define FLCE_REDUCTION_SUM 1
+#define FLCE_REDUCTION_NONE 2
 
 /*
  * flce_workspace_size -- bytes of device scratch that flce_forward and
@@ -93,9 +97,11 @@ int flce_workspace_size(int64_t B, int64_t T, int64_t H, int64_t V, int dtype,
  *   X [B*T, H], W [V, H] : dtype elements, device
  *   labels [B, T]        : int64, device
  *   ignore_index         : label value that marks a row as ignored (e.g. -100)
- *   reduction            : FLCE_REDUCTION_MEAN or FLCE_REDUCTION_SUM
+ *   reduction            : FLCE_REDUCTION_MEAN, _SUM or _NONE
  *   shift                : nonzero = next-token targets inside each sequence
- *   loss                 : out, float32 scalar, device
+ *   loss                 : out, float32, device: a scalar (MEAN, SUM), or
+ *                          [B*T] per-row losses (NONE: 0.0 on ignored rows,
+ *                          NaN everywhere after a bad label)
  *   lse [B*T]            : out, float32, device; log sum_v exp(z_iv) of every
  *                          row with a target, 0.0 for ignored rows.  Keep it
  *                          for flce_backward.
@@ -115,7 +121,8 @@ int flce_forward(const void* X, const void* W, const int64_t* labels,
  * flce_backward -- gradients of grad_scale * loss with respect to X and W.
  *   X, W, labels, sizes, dtype, ignore_index, reduction, shift : as forward
  *   lse [B*T]     : float32, device, the forward's output for the same inputs
- *   grad_scale    : float32 scalar, device (the upstream dL/dloss); NULL = 1
+ *   grad_scale    : float32, device: the upstream dL/dloss, a scalar (MEAN,
+ *                   SUM) or [B*T] per-row values (NONE); NULL = 1
  *   dX [B*T, H]   : out, device, fully overwritten (ignored rows are 0)
  *   dW [V, H]     : out, device, fully overwritten
  *   grad_dtype    : element type of dX and dW: the input dtype, or
@@ -161,7 +168,7 @@ int flce_chunked_workspace_size(int64_t B, int64_t T, int64_t H, int64_t V, int 
  * flce_chunked -- loss, per-row lse and the gradients of grad_scale * loss.
  *   X, W, labels, sizes, dtype, ignore_index, reduction, shift : as forward
  *   chunk_rows    : as flce_chunked_workspace_size
- *   grad_scale    : float32 scalar, device; NULL = 1
+ *   grad_scale    : as flce_backward (scalar, or per row under NONE); NULL = 1
  *   loss, lse, n_valid : as flce_forward's outputs
  *   dX, dW, grad_dtype, dW_accumulate : as flce_backward's
  *   status        : as forward (a bad label also makes the gradients NaN)

@@ -24,7 +24,7 @@ import os
 
 __all__ = [
     "FLCE_OK", "FLCE_DTYPE_F32", "FLCE_DTYPE_BF16", "FLCE_REDUCTION_MEAN",
-    "FLCE_REDUCTION_SUM", "FlceError", "flce_workspace_size", "flce_forward",
+    "FLCE_REDUCTION_SUM", "FLCE_REDUCTION_NONE", "FlceError", "flce_workspace_size", "flce_forward",
     "flce_backward", "flce_chunked_workspace_size", "flce_chunked", "flce_scale_grads",
     "flce_set_timing", "flce_status_string", "linear_cross_entropy", "library_path",
 ]
@@ -46,6 +46,7 @@ FLCE_DTYPE_F32 = 0
 FLCE_DTYPE_BF16 = 1
 FLCE_REDUCTION_MEAN = 0
 FLCE_REDUCTION_SUM = 1
+FLCE_REDUCTION_NONE = 2
 
 EXPORTS = ("flce_workspace_size", "flce_forward", "flce_backward",
            "flce_chunked_workspace_size", "flce_chunked", "flce_scale_grads",
@@ -195,7 +196,9 @@ def _reduction_code(reduction: str) -> int:
         return FLCE_REDUCTION_MEAN
     if reduction == "sum":
         return FLCE_REDUCTION_SUM
-    raise ValueError(f"unsupported reduction {reduction!r} (mean or sum)")
+    if reduction == "none":
+        return FLCE_REDUCTION_NONE
+    raise ValueError(f"unsupported reduction {reduction!r} (mean, sum or none)")
 
 
 def _shape(hidden, weight, labels):
@@ -242,7 +245,8 @@ def workspace(B, T, H, V, dtype_code, device):
 
 def forward(hidden, weight, labels, ignore_index=-100, shift=False, reduction="mean",
             ws=None):
-    """(loss, lse, n_valid, status) as device tensors, no host synchronisation."""
+    """(loss, lse, n_valid, status) as device tensors, no host synchronisation;
+    loss is a scalar, or [B*T] per-row losses for reduction="none"."""
     torch = _torch()
     _check_tensors(hidden, weight, labels)
     B, T, H, V = _shape(hidden, weight, labels)
@@ -252,7 +256,8 @@ def forward(hidden, weight, labels, ignore_index=-100, shift=False, reduction="m
         ws, nbytes = workspace(B, T, H, V, dt, dev)
     else:
         nbytes = ws.numel()
-    loss = torch.empty((), dtype=torch.float32, device=dev)
+    loss = torch.empty((B * T,) if reduction == "none" else (), dtype=torch.float32,
+                       device=dev)
     lse = torch.empty(B * T, dtype=torch.float32, device=dev)
     n_valid = torch.empty((), dtype=torch.int64, device=dev)
     status = torch.empty((), dtype=torch.int32, device=dev)
@@ -281,8 +286,9 @@ def _dw_out(dW, weight, out_dtype, accumulate):
 def backward(hidden, weight, labels, lse, grad_scale=None, ignore_index=-100,
              shift=False, reduction="mean", grad_dtype=None, ws=None, dW=None,
              accumulate=False):
-    """(dX, dW, status); grad_scale is a device float32 scalar or None (= 1).
-    dW: optional output tensor; accumulate=True adds the gradient to it."""
+    """(dX, dW, status); grad_scale is a device float32 scalar, or [B*T] per-row
+    values for reduction="none", or None (= 1).  dW: optional output tensor;
+    accumulate=True adds the gradient to it."""
     torch = _torch()
     _check_tensors(hidden, weight, labels)
     B, T, H, V = _shape(hidden, weight, labels)
@@ -334,7 +340,8 @@ def chunked(hidden, weight, labels, grad_scale=None, ignore_index=-100, shift=Fa
         ws, nbytes = chunked_workspace(B, T, H, V, dt, dev, chunk_rows)
     else:
         nbytes = ws.numel()
-    loss = torch.empty((), dtype=torch.float32, device=dev)
+    loss = torch.empty((B * T,) if reduction == "none" else (), dtype=torch.float32,
+                       device=dev)
     lse = torch.empty(B * T, dtype=torch.float32, device=dev)
     n_valid = torch.empty((), dtype=torch.int64, device=dev)
     status = torch.empty((), dtype=torch.int32, device=dev)
@@ -365,14 +372,14 @@ def _autograd_function():
                                       reduction)
             ctx.save_for_backward(hidden, weight, labels, lse)
             ctx.args = (ignore_index, shift, reduction)
-            return loss
+            return loss.reshape(labels.shape) if reduction == "none" else loss
 
         @staticmethod
         def backward(ctx, grad_out):
             hidden, weight, labels, lse = ctx.saved_tensors
             ignore_index, shift, reduction = ctx.args
-            dX, dW, _ = backward(hidden, weight, labels, lse,
-                                 grad_scale=grad_out.reshape(()),
+            g = grad_out.reshape(-1) if reduction == "none" else grad_out.reshape(())
+            dX, dW, _ = backward(hidden, weight, labels, lse, grad_scale=g,
                                  ignore_index=ignore_index, shift=shift,
                                  reduction=reduction)
             return dX, dW, None, None, None, None
@@ -412,17 +419,23 @@ def linear_cross_entropy(hidden, weight, labels, ignore_index=-100, shift=False,
 
     hidden [B, T, H] or [N, H]; weight [V, H]; labels [B, T] (or [N], one
     sequence); bfloat16 or float32 on the GPU.  Returns a float32 scalar loss
-    tensor that backpropagates into hidden and weight.  mode="recompute"
+    (reduction "mean" or "sum") or per-token losses shaped like labels
+    ("none"; 0 on ignored tokens, their negatives are the target log-probs),
+    which backpropagate into hidden and weight.  mode="recompute"
     (forward, then a backward that recomputes the logits; extra memory linear
     in N) or "chunked" (gradients formed during the forward over row chunks;
     one logits pass, extra memory proportional to a chunk of rows times V)."""
     global _FN
     if _FN is None:
         _FN = _autograd_function()
-    if reduction not in ("mean", "sum"):
-        raise ValueError(f"unsupported reduction {reduction!r} (mean or sum)")
+    if reduction not in ("mean", "sum", "none"):
+        raise ValueError(f"unsupported reduction {reduction!r} (mean, sum or none)")
     if mode not in ("recompute", "chunked"):
         raise ValueError(f"unsupported mode {mode!r} (recompute or chunked)")
+    if mode == "chunked" and reduction == "none":
+        # the chunked mode forms the gradients before the upstream gradient
+        # exists; a per-token one cannot be applied afterwards
+        raise ValueError('mode="chunked" needs a scalar loss (mean or sum)')
     fn = _FN[0] if mode == "recompute" else _FN[1]
     return fn.apply(hidden.contiguous(), weight.contiguous(), labels.contiguous(),
                     int(ignore_index), bool(shift), reduction)

@@ -34,7 +34,7 @@ struct Plan {
   // workspace offsets (bytes)
   int64_t o_ctr, o_idx, o_tgt, o_rowpos, o_xc;
   int64_t o_part, o_zt, o_bsum;            // forward region
-  int64_t o_lse2, o_g, o_dx32;             // backward region
+  int64_t o_lse2, o_rs, o_g, o_dx32;       // backward region
   int64_t total;
 };
 
@@ -86,6 +86,7 @@ int make_plan(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, Plan* p) {
   const int64_t fwd_end = off;
   off = common;
   q.o_lse2 = take(4 * q.rows_pad);
+  q.o_rs = take(4 * q.rows_pad);
   q.o_g = take(2 * q.rows_pad * q.Vb * q.es);   // two slabs, alternating blocks
   q.o_dx32 = take(4 * q.rows_pad * H);
   const int64_t bwd_end = off;
@@ -171,6 +172,7 @@ int forward_impl(const Plan& pl, const void* X, const void* W, const int64_t* la
   float* bsum = (float*)(ws + pl.o_bsum);
   const int rows_pad = (int)pl.rows_pad;
   const int row_bytes = (int)(pl.H * E::kBytes);
+  const bool none = reduction == FLCE_REDUCTION_NONE;
 
   hipLaunchKernelGGL(k_prep, dim3(1), dim3(1024), 0, stream, labels, (int)B, (int)T,
                      ignore_index, pl.V, shift, reduction, (const float*)nullptr,
@@ -179,7 +181,7 @@ int forward_impl(const Plan& pl, const void* X, const void* W, const int64_t* la
   hipLaunchKernelGGL(k_gather, dim3((unsigned)cdiv(rows_pad, 4)), dim3(256), 0, stream,
                      (const char*)X, row_bytes, (const int*)idx, (const Counters*)ctr,
                      xc, rows_pad, (const float*)nullptr, (float*)nullptr,
-                     (float*)nullptr, 0);
+                     (float*)nullptr, 0, (const float*)nullptr, (float*)nullptr);
   L.check();
   hipLaunchKernelGGL(k_target<E>, dim3((unsigned)cdiv(rows_pad, 4)), dim3(256), 0, stream,
                      (const char*)xc, (const char*)W, (int)pl.H, (const int*)tgt,
@@ -204,10 +206,10 @@ int forward_impl(const Plan& pl, const void* X, const void* W, const int64_t* la
   const int nb = (int)cdiv(pl.N, 256);
   hipLaunchKernelGGL(k_merge, dim3(nb), dim3(256), 0, stream, (const float2*)part,
                      (const Counters*)ctr, (const int*)rowpos, (const float*)zt,
-                     (int)pl.N, lse, bsum);
+                     (int)pl.N, lse, bsum, none ? loss : (float*)nullptr);
   L.check();
   hipLaunchKernelGGL(k_loss, dim3(1), dim3(256), 0, stream, (const float*)bsum, nb,
-                     (const Counters*)ctr, reduction, loss, n_valid);
+                     (const Counters*)ctr, reduction, none ? (float*)nullptr : loss, n_valid);
   L.check();
   return L.err == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }
@@ -229,13 +231,16 @@ int backward_impl(const Plan& pl, const void* X, const void* W, const int64_t* l
   const int rows_pad = (int)pl.rows_pad;
   const int row_bytes = (int)(pl.H * E::kBytes);
 
+  // reduction "none": grad_scale is per row, gathered into compacted order
+  const bool none = reduction == FLCE_REDUCTION_NONE;
+  float* rs = none && grad_scale ? (float*)(ws + pl.o_rs) : nullptr;
   hipLaunchKernelGGL(k_prep, dim3(1), dim3(1024), 0, stream, labels, (int)B, (int)T,
-                     ignore_index, pl.V, shift, reduction, grad_scale, cu_count(),
-                     (int)pl.fwd_items, idx, tgt, rowpos, ctr, status);
+                     ignore_index, pl.V, shift, reduction, none ? nullptr : grad_scale,
+                     cu_count(), (int)pl.fwd_items, idx, tgt, rowpos, ctr, status);
   L.check();
   hipLaunchKernelGGL(k_gather, dim3((unsigned)cdiv(rows_pad, 4)), dim3(256), 0, stream,
                      (const char*)X, row_bytes, (const int*)idx, (const Counters*)ctr,
-                     xc, rows_pad, lse, lse2, dx32, (int)(pl.H * 4));
+                     xc, rows_pad, lse, lse2, dx32, (int)(pl.H * 4), grad_scale, rs);
   L.check();
 
   BwdArgs a;
@@ -243,6 +248,7 @@ int backward_impl(const Plan& pl, const void* X, const void* W, const int64_t* l
   a.Xc = xc;
   a.G = g;
   a.lse2 = lse2;
+  a.rs = rs;
   a.tgt = tgt;
   a.dx32 = dx32;
   a.dW = (char*)dW;
@@ -318,6 +324,7 @@ struct ChunkPlan {
   int64_t N, rows_pad, H, V, Vp, es, TT, VT;
   int64_t C, nchunks;       // chunk rows (multiple of 256), chunks covering rows_pad
   int64_t o_ctr, o_idx, o_tgt, o_rowpos, o_xc, o_zt, o_lse_c, o_lse2, o_rloss, o_bsum, o_cctr;
+  int64_t o_rs;
   int64_t o_part, o_slab, o_dx32;
   int64_t total;
 };
@@ -362,6 +369,7 @@ int make_chunk_plan(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, int64
   q.o_lse_c = take(4 * q.rows_pad);
   q.o_lse2 = take(4 * q.rows_pad);
   q.o_rloss = take(4 * q.rows_pad);
+  q.o_rs = take(4 * q.rows_pad);
   q.o_bsum = take(4 * q.TT);
   q.o_cctr = take(sizeof(Counters) * q.nchunks);
   q.o_part = take(8 * 2 * q.VT * q.C);
@@ -396,15 +404,17 @@ int chunked_impl(const ChunkPlan& pl, const void* X, const void* W, const int64_
   const int rows_pad = (int)pl.rows_pad;
   const int row_bytes = (int)(pl.H * E::kBytes);
   const int C = (int)pl.C, TTc = C / kTile, HT = (int)cdiv(pl.H, kTile);
+  const bool none = reduction == FLCE_REDUCTION_NONE;
+  float* rs = none && grad_scale ? (float*)(ws + pl.o_rs) : nullptr;
 
   hipLaunchKernelGGL(k_prep, dim3(1), dim3(1024), 0, stream, labels, (int)B, (int)T,
-                     ignore_index, pl.V, shift, reduction, grad_scale, cu_count(), 1, idx,
-                     tgt, rowpos, ctr, status);
+                     ignore_index, pl.V, shift, reduction, none ? nullptr : grad_scale,
+                     cu_count(), 1, idx, tgt, rowpos, ctr, status);
   L.check();
   hipLaunchKernelGGL(k_gather, dim3((unsigned)cdiv(rows_pad, 4)), dim3(256), 0, stream,
                      (const char*)X, row_bytes, (const int*)idx, (const Counters*)ctr, xc,
                      rows_pad, (const float*)nullptr, (float*)nullptr, dx32,
-                     (int)(pl.H * 4));
+                     (int)(pl.H * 4), grad_scale, rs);
   L.check();
   hipLaunchKernelGGL(k_target<E>, dim3((unsigned)cdiv(rows_pad, 4)), dim3(256), 0, stream,
                      (const char*)xc, (const char*)W, (int)pl.H, (const int*)tgt,
@@ -423,6 +433,7 @@ int chunked_impl(const ChunkPlan& pl, const void* X, const void* W, const int64_
     ca.cctr = cctr + ch;
     ca.zt = zt;
     ca.tgt = tgt;
+    ca.rs = rs;
     ca.lse_c = lse_c;
     ca.lse2 = lse2;
     ca.rloss = rloss;
@@ -450,6 +461,7 @@ int chunked_impl(const ChunkPlan& pl, const void* X, const void* W, const int64_
     b.W = (const char*)W;
     b.Xc = ca.Xc;
     b.lse2 = lse2;
+    b.rs = rs;
     b.tgt = tgt;
     b.dx32 = dx32 + (int64_t)ca.row0 * pl.H;
     b.dW = (char*)dW;
@@ -475,13 +487,14 @@ int chunked_impl(const ChunkPlan& pl, const void* X, const void* W, const int64_
     }
   }
   hipLaunchKernelGGL(k_lse_out, dim3((unsigned)cdiv(pl.N, 256)), dim3(256), 0, stream,
-                     (const float*)lse_c, (const int*)rowpos, (int)pl.N, lse);
+                     (const float*)lse_c, (const int*)rowpos, (int)pl.N, lse,
+                     (const float*)rloss, (const Counters*)ctr, none ? loss : (float*)nullptr);
   L.check();
   hipLaunchKernelGGL(k_block_sums, dim3((unsigned)pl.TT), dim3(256), 0, stream,
                      (const float*)rloss, (const Counters*)ctr, bsum);
   L.check();
   hipLaunchKernelGGL(k_loss, dim3(1), dim3(256), 0, stream, (const float*)bsum, (int)pl.TT,
-                     (const Counters*)ctr, reduction, loss, n_valid);
+                     (const Counters*)ctr, reduction, none ? (float*)nullptr : loss, n_valid);
   L.check();
   hipLaunchKernelGGL(k_dx_final, dim3((unsigned)cdiv(pl.N, 4)), dim3(256), 0, stream,
                      (const float*)dx32, (const int*)rowpos, (int)pl.N, (int)pl.H,
@@ -516,11 +529,15 @@ int flce_forward(const void* X, const void* W, const int64_t* labels, int64_t B,
   Plan p;
   int rc = make_plan(B, T, H, V, dtype, &p);
   if (rc != FLCE_OK) return rc;
-  if (reduction != FLCE_REDUCTION_MEAN && reduction != FLCE_REDUCTION_SUM)
+  if (reduction != FLCE_REDUCTION_MEAN && reduction != FLCE_REDUCTION_SUM &&
+      reduction != FLCE_REDUCTION_NONE)
     return FLCE_ERR_REDUCTION;
   hipStream_t s = (hipStream_t)stream;
   if (p.N == 0) {
-    hipLaunchKernelGGL(k_empty, dim3(1), dim3(1), 0, s, loss, n_valid, status);
+    // reduction "none": the per-row loss array is empty
+    hipLaunchKernelGGL(k_empty, dim3(1), dim3(1), 0, s,
+                       reduction == FLCE_REDUCTION_NONE ? (float*)nullptr : loss, n_valid,
+                       status);
     return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
   }
   if (X == nullptr || W == nullptr || labels == nullptr || lse == nullptr)
@@ -546,7 +563,8 @@ int flce_backward(const void* X, const void* W, const int64_t* labels, int64_t B
   Plan p;
   int rc = make_plan(B, T, H, V, dtype, &p);
   if (rc != FLCE_OK) return rc;
-  if (reduction != FLCE_REDUCTION_MEAN && reduction != FLCE_REDUCTION_SUM)
+  if (reduction != FLCE_REDUCTION_MEAN && reduction != FLCE_REDUCTION_SUM &&
+      reduction != FLCE_REDUCTION_NONE)
     return FLCE_ERR_REDUCTION;
   if (grad_dtype != dtype && grad_dtype != FLCE_DTYPE_F32) return FLCE_ERR_DTYPE;
   if (W == nullptr || dW == nullptr) return FLCE_ERR_NULL;
@@ -599,7 +617,8 @@ int flce_chunked(const void* X, const void* W, const int64_t* labels, int64_t B,
   ChunkPlan p;
   const int rc = make_chunk_plan(B, T, H, V, dtype, chunk_rows, &p);
   if (rc != FLCE_OK) return rc;
-  if (reduction != FLCE_REDUCTION_MEAN && reduction != FLCE_REDUCTION_SUM)
+  if (reduction != FLCE_REDUCTION_MEAN && reduction != FLCE_REDUCTION_SUM &&
+      reduction != FLCE_REDUCTION_NONE)
     return FLCE_ERR_REDUCTION;
   if (grad_dtype != dtype && grad_dtype != FLCE_DTYPE_F32) return FLCE_ERR_DTYPE;
   if (loss == nullptr || W == nullptr || dW == nullptr) return FLCE_ERR_NULL;
@@ -615,7 +634,9 @@ int flce_chunked(const void* X, const void* W, const int64_t* labels, int64_t B,
   const int gf32 = grad_dtype == FLCE_DTYPE_F32 ? 1 : 0;
   if (p.N == 0) {
     if (!dW_accumulate) zero_fill(dW, p.V * p.H * ges, s);
-    hipLaunchKernelGGL(k_empty, dim3(1), dim3(1), 0, s, loss, n_valid, status);
+    hipLaunchKernelGGL(k_empty, dim3(1), dim3(1), 0, s,
+                       reduction == FLCE_REDUCTION_NONE ? (float*)nullptr : loss, n_valid,
+                       status);
     return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
   }
   if (workspace == nullptr) return FLCE_ERR_WORKSPACE;

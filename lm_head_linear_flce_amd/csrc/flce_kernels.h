@@ -138,7 +138,8 @@ __global__ __launch_bounds__(256) void k_gather(
     const char* __restrict__ X, int row_bytes, const int* __restrict__ idx,
     const Counters* __restrict__ ctr, char* __restrict__ Xc, int rows_pad,
     const float* __restrict__ lse, float* __restrict__ lse2,
-    float* __restrict__ dx32, int dx32_row_bytes) {
+    float* __restrict__ dx32, int dx32_row_bytes, const float* __restrict__ rs_in,
+    float* __restrict__ rs_c) {
   const int k = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (k >= rows_pad) return;
@@ -152,6 +153,7 @@ __global__ __launch_bounds__(256) void k_gather(
     for (int c = lane; c < chunks; c += 64) dst[c] = i32x4{0, 0, 0, 0};
   }
   if (lse2 != nullptr && lane == 0) lse2[k] = k < n ? lse[idx[k]] * kLog2e : 0.f;
+  if (rs_c != nullptr && lane == 0) rs_c[k] = k < n ? rs_in[idx[k]] : 0.f;
   if (dx32 != nullptr) {
     i32x4* d = (i32x4*)((char*)dx32 + (int64_t)k * dx32_row_bytes);
     for (int c = lane; c < (dx32_row_bytes >> 4); c += 64) d[c] = i32x4{0, 0, 0, 0};
@@ -324,7 +326,7 @@ void k_fwd_lse(FwdArgs a) {
 __global__ __launch_bounds__(256) void k_merge(
     const float2* __restrict__ part, const Counters* __restrict__ ctr,
     const int* __restrict__ rowpos, const float* __restrict__ zt, int N,
-    float* __restrict__ lse_out, float* __restrict__ blocksum) {
+    float* __restrict__ lse_out, float* __restrict__ blocksum, float* __restrict__ rloss_out) {
   __shared__ float red[256];
   const int i = blockIdx.x * 256 + threadIdx.x;
   const int P = ctr->fwd_p, TTn = (ctr->n + kTile - 1) / kTile;
@@ -346,6 +348,8 @@ __global__ __launch_bounds__(256) void k_merge(
       li = lse - zt[k];
     }
     lse_out[i] = lse;
+    // per-row losses (reduction "none"): 0 on ignored rows, NaN after a bad label
+    if (rloss_out) rloss_out[i] = ctr->status ? __builtin_nanf("") : li;
   }
   red[threadIdx.x] = li;
   __syncthreads();
@@ -374,7 +378,7 @@ __global__ __launch_bounds__(256) void k_loss(
     float L = red[0];
     if (reduction == 0) L = n > 0 ? L / (float)n : 0.f;
     if (ctr->status != 0) L = __builtin_nanf("");
-    *loss = L;
+    if (loss) *loss = L;
     if (n_valid) *n_valid = n;
   }
 }
@@ -393,6 +397,7 @@ struct BwdArgs {
   const char* Xc;      // [rows_pad, H] compacted valid rows
   char* G;             // [rows_pad, Vb] this block's softmax-gradient slab
   const float* lse2;   // [rows_pad] lse * log2(e)
+  const float* rs;     // [rows_pad] per-row gradient factors (reduction "none") or NULL
   const int* tgt;      // [n]
   float* dx32;         // [rows_pad, H]
   char* dW;            // [V, H] output (grad dtype)
@@ -407,16 +412,17 @@ struct BwdArgs {
 // G = c * 2^(z*log2e - lse2) for one tile, stored as G[token][vocab].
 // kMasked: tile rows with (32i + 8g + q) >= vlim_lane lie past the vocabulary
 // end and token columns >= nlim are padding; both become 0.
-// l2[j]: lse2 of the lane's token column j, loaded before the tile's K loop.
+// l2[j], cs[j]: lse2 and gradient factor c (times the row's factor under
+// reduction "none") of the lane's token column j, loaded before the K loop.
 // bf16: through LDS (store_quarter_bf16); fp32: direct 16-byte stores.
 template <class E, bool kMasked>
 __device__ __forceinline__ void g_store(const BwdArgs& a, const f32x16 (&acc)[4][4],
-                                        const float (&l2)[4], float c, int vt, int tau,
-                                        int wm, int wn, int lane, int vlim_lane, int nlim,
-                                        lds_t* smem) {
+                                        const float (&l2)[4], const float (&cs)[4], int vt,
+                                        int tau, int wm, int wn, int lane, int vlim_lane,
+                                        int nlim, lds_t* smem) {
   const rsrc_t gr = make_rsrc(a.G, (int64_t)a.rows_pad * a.Vb * E::kBytes);
   auto val = [&](int i, int j, int r) {
-    const float v = c * __builtin_amdgcn_exp2f(fmaf(acc[i][j][r], kLog2e, -l2[j]));
+    const float v = cs[j] * __builtin_amdgcn_exp2f(fmaf(acc[i][j][r], kLog2e, -l2[j]));
     const bool ok = !kMasked || (acc_col(wn, j, lane) < nlim &&
                                  32 * i + 8 * (r >> 2) + (r & 3) < vlim_lane);
     return ok ? v : 0.f;
@@ -472,19 +478,24 @@ __device__ __forceinline__ void g_tile(const BwdArgs& a, int item, lds_t* smem) 
   B.bytes = (int64_t)(a.rows_pad - tau * kTile) * ldb;
   B.ldb = ldb;
   B.kbytes = ldb;
-  // the rows' lse, fetched now so the epilogue does not wait on it
-  float l2[4];
+  // the rows' lse and gradient factors, fetched now so the epilogue does not
+  // wait on them
+  float l2[4], cs[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) l2[j] = a.lse2[tau * kTile + acc_col(wn, j, lane)];
+  for (int j = 0; j < 4; ++j) {
+    const int tok = tau * kTile + acc_col(wn, j, lane);
+    l2[j] = a.lse2[tok];
+    cs[j] = a.rs ? c * a.rs[tok] : c;
+  }
   f32x16 acc[4][4];
   zero_acc(acc);
   gemm_tile<E, LoadDirect, LoadDirect>(A, B, steps, smem, wm, wn, acc);
 
   const int vlim = a.V - vbase;
   if (vlim >= kTile && (tau + 1) * kTile <= n)
-    g_store<E, false>(a, acc, l2, c, vt, tau, wm, wn, lane, 0, 0, smem);
+    g_store<E, false>(a, acc, l2, cs, vt, tau, wm, wn, lane, 0, 0, smem);
   else
-    g_store<E, true>(a, acc, l2, c, vt, tau, wm, wn, lane,
+    g_store<E, true>(a, acc, l2, cs, vt, tau, wm, wn, lane,
                      vlim - wm * 128 - 4 * (lane >> 5), n - tau * kTile, smem);
 }
 
@@ -495,7 +506,7 @@ __global__ __launch_bounds__(256) void k_fixup(BwdArgs a) {
   if (k >= a.ctr->n) return;
   const int y = a.tgt[k] - a.v0;
   if (y < 0 || y >= a.vb) return;
-  const float c = a.ctr->c;
+  const float c = a.rs ? a.ctr->c * a.rs[k] : a.ctr->c;
   const int64_t off = (int64_t)k * a.Vb + y;
   if constexpr (E::kBytes == 2) {
     uint16_t* g = (uint16_t*)a.G + off;
@@ -725,6 +736,7 @@ struct ChunkArgs {
   Counters* cctr;       // this chunk's counters (n = rows in the chunk)
   const float* zt;      // [rows_pad] target logits (compacted rows)
   const int* tgt;       // [rows_pad] targets (compacted rows)
+  const float* rs;      // [rows_pad] per-row gradient factors (reduction "none") or NULL
   float* lse_c;         // [rows_pad] lse per compacted row
   float* lse2;          // [rows_pad] lse * log2(e)
   float* rloss;         // [rows_pad] row losses lse - z_target
@@ -893,7 +905,7 @@ __global__ __launch_bounds__(256) void k_chunk_scale(ChunkArgs a) {
     return;
   }
   const int k = a.row0 + kl;
-  const float c = a.ctr->c;
+  const float c = a.rs ? a.ctr->c * a.rs[k] : a.ctr->c;
   const float f = c * exp2f(a.part[(int64_t)kl * (2 * a.VT) + (v >> 7)].x - a.lse2[k]);
   const int y = a.tgt[k] - v;
   const i32x4 u = *p;
@@ -923,11 +935,16 @@ __global__ __launch_bounds__(256) void k_chunk_scale(ChunkArgs a) {
 // lse of every original row (0 for ignored rows) after the chunks.
 __global__ __launch_bounds__(256) void k_lse_out(const float* __restrict__ lse_c,
                                                  const int* __restrict__ rowpos, int N,
-                                                 float* __restrict__ lse_out) {
+                                                 float* __restrict__ lse_out,
+                                                 const float* __restrict__ rloss,
+                                                 const Counters* __restrict__ ctr,
+                                                 float* __restrict__ rloss_out) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= N) return;
   const int k = rowpos[i];
   lse_out[i] = k >= 0 ? lse_c[k] : 0.f;
+  // per-row losses (reduction "none"): 0 on ignored rows, NaN after a bad label
+  if (rloss_out) rloss_out[i] = ctr->status ? __builtin_nanf("") : (k >= 0 ? rloss[k] : 0.f);
 }
 
 // dX *= s, dW *= s (s a device scalar): gradients computed with grad_scale 1
@@ -982,7 +999,7 @@ __global__ __launch_bounds__(256) void k_zero(char* __restrict__ p, int64_t chun
 
 // n == 0 rows (N == 0): loss = 0, n_valid = 0.
 __global__ void k_empty(float* loss, int64_t* n_valid, int32_t* status) {
-  *loss = 0.f;
+  if (loss) *loss = 0.f;
   if (n_valid) *n_valid = 0;
   if (status) *status = 0;
 }

@@ -108,7 +108,7 @@ def bwd(**kw):
     (dict(labels=0), F.FLCE_ERR_NULL), (dict(loss=0), F.FLCE_ERR_NULL),
     (dict(lse=0), F.FLCE_ERR_NULL), (dict(H=100), F.FLCE_ERR_ALIGN),
     (dict(X=P + 8), F.FLCE_ERR_ALIGN), (dict(dtype=3), F.FLCE_ERR_DTYPE),
-    (dict(reduction=2), F.FLCE_ERR_REDUCTION), (dict(workspace=0), F.FLCE_ERR_WORKSPACE),
+    (dict(reduction=3), F.FLCE_ERR_REDUCTION), (dict(workspace=0), F.FLCE_ERR_WORKSPACE),
     (dict(workspace_bytes=64), F.FLCE_ERR_WORKSPACE), (dict(V=-5), F.FLCE_ERR_SHAPE),
 ])
 def test_forward_host_checks(kw, code):
@@ -143,7 +143,7 @@ def chk(**kw):
     (dict(lse=0), F.FLCE_ERR_NULL), (dict(dX=0), F.FLCE_ERR_NULL),
     (dict(dW=0), F.FLCE_ERR_NULL), (dict(H=100), F.FLCE_ERR_ALIGN),
     (dict(X=P + 8), F.FLCE_ERR_ALIGN), (dict(dtype=3), F.FLCE_ERR_DTYPE),
-    (dict(grad_dtype=5), F.FLCE_ERR_DTYPE), (dict(reduction=2), F.FLCE_ERR_REDUCTION),
+    (dict(grad_dtype=5), F.FLCE_ERR_DTYPE), (dict(reduction=3), F.FLCE_ERR_REDUCTION),
     (dict(dX=P), F.FLCE_ERR_ALIAS), (dict(dW=2 * P + 64), F.FLCE_ERR_ALIAS),
     (dict(workspace=0), F.FLCE_ERR_WORKSPACE), (dict(workspace_bytes=64), F.FLCE_ERR_WORKSPACE),
     (dict(V=-5), F.FLCE_ERR_SHAPE), (dict(chunk_rows=-1), F.FLCE_ERR_SHAPE),

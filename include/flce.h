@@ -144,6 +144,71 @@ int flce_backward(const void* X, const void* W, const int64_t* labels,
                   void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Vocabulary shards: the output layer split along V across devices, as the
+ * column-parallel output layer of Megatron-LM PR "[Dev] Fix Linear-Cross-
+ * Entropy Convergence Issue" (item 1; its item 2 is why the dX partials stay
+ * FP32 until they are summed).  A device holding W rows [v_begin, v_begin + V)
+ * of a V_total vocabulary runs flce_shard_forward; the per-row (lse, target
+ * logit) pairs of all shards are then gathered (the one exchange of the
+ * forward; [N] floats twice per shard) and merged by flce_shard_merge into the
+ * loss and the global lse; flce_shard_backward with that lse gives the shard's
+ * dW rows (complete) and its FP32 share of dX, to be summed over the shards
+ * (an all-reduce) and rounded once.  The calls are the same on one device;
+ * moving the partials between devices is the caller's (RCCL) business.
+ *
+ * flce_shard_forward -- per-row lse over this shard and target logits.
+ *   X, labels, B, T, H, dtype, ignore_index, shift, status, stream : as
+ *                  flce_forward (labels index the whole vocabulary)
+ *   W [V, H]     : this shard's rows of the output weight
+ *   V, v_begin, V_total : shard rows, first row's vocabulary index, vocabulary
+ *                  size; 0 <= v_begin, v_begin + V <= V_total
+ *   lse [B*T]    : out, float32, device: log sum over the shard's entries (0 on
+ *                  ignored rows)
+ *   zt [B*T]     : out, float32, device: z_{i,y_i} when y_i lies in this shard,
+ *                  else 0
+ *   workspace    : flce_workspace_size(B, T, H, V, dtype) bytes
+ */
+int flce_shard_forward(const void* X, const void* W, const int64_t* labels,
+                       int64_t B, int64_t T, int64_t H, int64_t V, int64_t v_begin,
+                       int64_t V_total, int dtype, int64_t ignore_index, int shift,
+                       float* lse, float* zt, int32_t* status, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+/* flce_shard_merge_workspace_size -- device scratch bytes of flce_shard_merge. */
+int flce_shard_merge_workspace_size(int64_t B, int64_t T, size_t* bytes);
+
+/*
+ * flce_shard_merge -- loss and global lse from the shards' partials.
+ *   lse_shards, zt_shards [shards][B*T] : float32, device: the shards' outputs
+ *   labels, B, T, ignore_index, shift, reduction, loss, lse, n_valid, status :
+ *                  as flce_forward (V_total: the vocabulary size, for the
+ *                  label check)
+ */
+int flce_shard_merge(const float* lse_shards, const float* zt_shards, int shards,
+                     const int64_t* labels, int64_t B, int64_t T, int64_t V_total,
+                     int64_t ignore_index, int shift, int reduction, float* loss, float* lse,
+                     int64_t* n_valid, int32_t* status, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/*
+ * flce_shard_backward -- this shard's dW rows and its share of dX.
+ *   arguments as flce_backward, with W, V, v_begin, V_total as in
+ *   flce_shard_forward and lse the merged (global) lse;
+ *   dX_partial [B*T, H] : out, float32, device: sum over the shard's
+ *                  vocabulary of G_iv W_v (ignored rows 0); sum over the
+ *                  shards, then round once
+ *   dW [V, H]    : out, grad_dtype, this shard's rows (dW_accumulate as in
+ *                  flce_backward)
+ */
+int flce_shard_backward(const void* X, const void* W, const int64_t* labels,
+                        int64_t B, int64_t T, int64_t H, int64_t V, int64_t v_begin,
+                        int64_t V_total, int dtype, int64_t ignore_index, int reduction,
+                        int shift, const float* lse, const float* grad_scale,
+                        float* dX_partial, void* dW, int grad_dtype, int dW_accumulate,
+                        int32_t* status, void* workspace, size_t workspace_bytes,
+                        void* stream);
+
+/*
  * Chunked mode: the row-chunk recipe of the ms-swift PR "feat(sft): Add
  * optional fused linear ce for qwen2/qwen3 on npu" ("What this PR does": the
  * sequence cut into chunks, each chunk's logits, loss and both gradients

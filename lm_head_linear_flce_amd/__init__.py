@@ -26,6 +26,8 @@ __all__ = [
     "FLCE_OK", "FLCE_DTYPE_F32", "FLCE_DTYPE_BF16", "FLCE_REDUCTION_MEAN",
     "FLCE_REDUCTION_SUM", "FLCE_REDUCTION_NONE", "FlceError", "flce_workspace_size", "flce_forward",
     "flce_backward", "flce_chunked_workspace_size", "flce_chunked", "flce_scale_grads",
+    "flce_shard_forward", "flce_shard_merge_workspace_size", "flce_shard_merge",
+    "flce_shard_backward",
     "flce_set_timing", "flce_status_string", "linear_cross_entropy", "library_path",
 ]
 
@@ -49,8 +51,9 @@ FLCE_REDUCTION_SUM = 1
 FLCE_REDUCTION_NONE = 2
 
 EXPORTS = ("flce_workspace_size", "flce_forward", "flce_backward",
-           "flce_chunked_workspace_size", "flce_chunked", "flce_scale_grads",
-           "flce_set_timing", "flce_status_string")
+           "flce_shard_forward", "flce_shard_merge_workspace_size", "flce_shard_merge",
+           "flce_shard_backward", "flce_chunked_workspace_size", "flce_chunked",
+           "flce_scale_grads", "flce_set_timing", "flce_status_string")
 
 
 class FlceError(RuntimeError):
@@ -80,6 +83,17 @@ def _load() -> ctypes.CDLL:
     lib.flce_backward.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, i64, i32, i32,
                                   vp, vp, vp, vp, i32, i32, vp, vp, sz, vp]
     lib.flce_backward.restype = i32
+    lib.flce_shard_forward.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, i64,
+                                       i32, vp, vp, vp, vp, sz, vp]
+    lib.flce_shard_forward.restype = i32
+    lib.flce_shard_merge_workspace_size.argtypes = [i64, i64, ctypes.POINTER(sz)]
+    lib.flce_shard_merge_workspace_size.restype = i32
+    lib.flce_shard_merge.argtypes = [vp, vp, i32, vp, i64, i64, i64, i64, i32, i32, vp, vp,
+                                     vp, vp, vp, sz, vp]
+    lib.flce_shard_merge.restype = i32
+    lib.flce_shard_backward.argtypes = [vp, vp, vp, i64, i64, i64, i64, i64, i64, i32, i64,
+                                        i32, i32, vp, vp, vp, vp, i32, i32, vp, vp, sz, vp]
+    lib.flce_shard_backward.restype = i32
     lib.flce_chunked_workspace_size.argtypes = [i64, i64, i64, i64, i32, i64,
                                                 ctypes.POINTER(sz)]
     lib.flce_chunked_workspace_size.restype = i32
@@ -136,6 +150,46 @@ def flce_backward(X, W, labels, B, T, H, V, dtype, ignore_index, reduction, shif
                               grad_scale or None, dX or None, dW or None, grad_dtype,
                               int(bool(dW_accumulate)), status or None, workspace or None,
                               workspace_bytes, stream or None)
+
+
+def flce_shard_forward(X, W, labels, B, T, H, V, v_begin, V_total, dtype, ignore_index,
+                       shift, lse, zt, status, workspace, workspace_bytes, stream) -> int:
+    """Returns the status code (0 on success); raises nothing."""
+    return _LIB.flce_shard_forward(X or None, W or None, labels or None, B, T, H, V, v_begin,
+                                   V_total, dtype, ignore_index, int(bool(shift)), lse or None,
+                                   zt or None, status or None, workspace or None,
+                                   workspace_bytes, stream or None)
+
+
+def flce_shard_merge_workspace_size(B: int, T: int) -> int:
+    out = ctypes.c_size_t(0)
+    rc = _LIB.flce_shard_merge_workspace_size(B, T, ctypes.byref(out))
+    if rc != FLCE_OK:
+        raise FlceError(rc, "flce_shard_merge_workspace_size")
+    return int(out.value)
+
+
+def flce_shard_merge(lse_shards, zt_shards, shards, labels, B, T, V_total, ignore_index,
+                     shift, reduction, loss, lse, n_valid, status, workspace,
+                     workspace_bytes, stream) -> int:
+    """Returns the status code (0 on success); raises nothing."""
+    return _LIB.flce_shard_merge(lse_shards or None, zt_shards or None, shards,
+                                 labels or None, B, T, V_total, ignore_index,
+                                 int(bool(shift)), reduction, loss or None, lse or None,
+                                 n_valid or None, status or None, workspace or None,
+                                 workspace_bytes, stream or None)
+
+
+def flce_shard_backward(X, W, labels, B, T, H, V, v_begin, V_total, dtype, ignore_index,
+                        reduction, shift, lse, grad_scale, dX_partial, dW, grad_dtype,
+                        dW_accumulate, status, workspace, workspace_bytes, stream) -> int:
+    """Returns the status code (0 on success); raises nothing."""
+    return _LIB.flce_shard_backward(X or None, W or None, labels or None, B, T, H, V, v_begin,
+                                    V_total, dtype, ignore_index, reduction, int(bool(shift)),
+                                    lse or None, grad_scale or None, dX_partial or None,
+                                    dW or None, grad_dtype, int(bool(dW_accumulate)),
+                                    status or None, workspace or None, workspace_bytes,
+                                    stream or None)
 
 
 def flce_chunked_workspace_size(B: int, T: int, H: int, V: int, dtype: int,
@@ -315,6 +369,91 @@ def backward(hidden, weight, labels, lse, grad_scale=None, ignore_index=-100,
     if rc != FLCE_OK:
         raise FlceError(rc, "flce_backward")
     return dX, dW, status
+
+
+def shard_forward(hidden, weight_shard, labels, v_begin, V_total, ignore_index=-100,
+                  shift=False, ws=None):
+    """(lse_shard, zt_shard, status) of one vocabulary shard."""
+    torch = _torch()
+    _check_tensors(hidden, weight_shard, labels)
+    B, T, H, V = _shape(hidden, weight_shard, labels)
+    dt = _dtype_code(hidden)
+    dev = hidden.device
+    if ws is None:
+        ws, nbytes = workspace(B, T, H, V, dt, dev)
+    else:
+        nbytes = ws.numel()
+    lse = torch.empty(B * T, dtype=torch.float32, device=dev)
+    zt = torch.empty(B * T, dtype=torch.float32, device=dev)
+    status = torch.empty((), dtype=torch.int32, device=dev)
+    rc = flce_shard_forward(hidden.data_ptr(), weight_shard.data_ptr(), labels.data_ptr(), B,
+                            T, H, V, int(v_begin), int(V_total), dt, int(ignore_index), shift,
+                            lse.data_ptr(), zt.data_ptr(), status.data_ptr(), ws.data_ptr(),
+                            nbytes, _stream_handle(dev))
+    if rc != FLCE_OK:
+        raise FlceError(rc, "flce_shard_forward")
+    return lse, zt, status
+
+
+def shard_merge(lse_shards, zt_shards, labels, V_total, ignore_index=-100, shift=False,
+                reduction="mean"):
+    """(loss, lse, n_valid, status) from the stacked shard outputs [shards, B*T]."""
+    torch = _torch()
+    lse_shards = lse_shards.to(torch.float32).contiguous()
+    zt_shards = zt_shards.to(torch.float32).contiguous()
+    if labels.dim() == 2:
+        B, T = labels.shape
+    else:
+        B, T = 1, labels.shape[0]
+    dev = labels.device
+    nbytes = flce_shard_merge_workspace_size(B, T)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    loss = torch.empty((B * T,) if reduction == "none" else (), dtype=torch.float32,
+                       device=dev)
+    lse = torch.empty(B * T, dtype=torch.float32, device=dev)
+    n_valid = torch.empty((), dtype=torch.int64, device=dev)
+    status = torch.empty((), dtype=torch.int32, device=dev)
+    rc = flce_shard_merge(lse_shards.data_ptr(), zt_shards.data_ptr(), lse_shards.shape[0],
+                          labels.contiguous().data_ptr(), int(B), int(T), int(V_total),
+                          int(ignore_index), shift, _reduction_code(reduction),
+                          loss.data_ptr(), lse.data_ptr(), n_valid.data_ptr(),
+                          status.data_ptr(), ws.data_ptr(), nbytes, _stream_handle(dev))
+    if rc != FLCE_OK:
+        raise FlceError(rc, "flce_shard_merge")
+    return loss, lse, n_valid, status
+
+
+def shard_backward(hidden, weight_shard, labels, lse, v_begin, V_total, grad_scale=None,
+                   ignore_index=-100, shift=False, reduction="mean", grad_dtype=None,
+                   ws=None, dW=None, accumulate=False):
+    """(dX_partial fp32, dW_shard, status) of one vocabulary shard."""
+    torch = _torch()
+    _check_tensors(hidden, weight_shard, labels)
+    B, T, H, V = _shape(hidden, weight_shard, labels)
+    dt = _dtype_code(hidden)
+    gd = dt if grad_dtype is None else _dtype_code(torch.empty(0, dtype=grad_dtype))
+    out_dtype = torch.float32 if gd == FLCE_DTYPE_F32 else hidden.dtype
+    dev = hidden.device
+    if ws is None:
+        ws, nbytes = workspace(B, T, H, V, dt, dev)
+    else:
+        nbytes = ws.numel()
+    dXp = torch.empty(hidden.shape, dtype=torch.float32, device=dev)
+    dW = _dw_out(dW, weight_shard, out_dtype, accumulate)
+    status = torch.empty((), dtype=torch.int32, device=dev)
+    gs = 0
+    if grad_scale is not None:
+        grad_scale = grad_scale.to(device=dev, dtype=torch.float32).contiguous()
+        gs = grad_scale.data_ptr()
+    lse = lse.to(device=dev, dtype=torch.float32).contiguous()
+    rc = flce_shard_backward(hidden.data_ptr(), weight_shard.data_ptr(), labels.data_ptr(), B,
+                             T, H, V, int(v_begin), int(V_total), dt, int(ignore_index),
+                             _reduction_code(reduction), shift, lse.data_ptr(), gs,
+                             dXp.data_ptr(), dW.data_ptr(), gd, accumulate,
+                             status.data_ptr(), ws.data_ptr(), nbytes, _stream_handle(dev))
+    if rc != FLCE_OK:
+        raise FlceError(rc, "flce_shard_backward")
+    return dXp, dW, status
 
 
 def chunked_workspace(B, T, H, V, dtype_code, device, chunk_rows=0):

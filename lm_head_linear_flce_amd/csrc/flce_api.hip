@@ -156,11 +156,17 @@ struct Timed {
   }
 };
 
+// The calls' W may be a vocabulary shard: rows [v_begin, v_begin + V) of a
+// vocabulary of V_total entries (labels index the whole vocabulary).
+struct Shard {
+  int64_t v_begin, V_total;
+};
+
 template <class E>
-int forward_impl(const Plan& pl, const void* X, const void* W, const int64_t* labels,
-                 int64_t B, int64_t T, int64_t ignore_index, int reduction, int shift,
-                 float* loss, float* lse, int64_t* n_valid, int32_t* status,
-                 char* ws, hipStream_t stream) {
+int forward_impl(const Plan& pl, const Shard& sh, const void* X, const void* W,
+                 const int64_t* labels, int64_t B, int64_t T, int64_t ignore_index,
+                 int reduction, int shift, float* loss, float* lse, int64_t* n_valid,
+                 int32_t* status, float* zt_out, char* ws, hipStream_t stream) {
   Launch L{stream};
   Counters* ctr = (Counters*)(ws + pl.o_ctr);
   int* idx = (int*)(ws + pl.o_idx);
@@ -175,8 +181,9 @@ int forward_impl(const Plan& pl, const void* X, const void* W, const int64_t* la
   const bool none = reduction == FLCE_REDUCTION_NONE;
 
   hipLaunchKernelGGL(k_prep, dim3(1), dim3(1024), 0, stream, labels, (int)B, (int)T,
-                     ignore_index, pl.V, shift, reduction, (const float*)nullptr,
-                     cu_count(), (int)pl.fwd_items, idx, tgt, rowpos, ctr, status);
+                     ignore_index, sh.V_total, shift, reduction, (const float*)nullptr,
+                     cu_count(), (int)pl.fwd_items, sh.v_begin, pl.V, idx, tgt, rowpos, ctr,
+                     status);
   L.check();
   hipLaunchKernelGGL(k_gather, dim3((unsigned)cdiv(rows_pad, 4)), dim3(256), 0, stream,
                      (const char*)X, row_bytes, (const int*)idx, (const Counters*)ctr,
@@ -185,7 +192,7 @@ int forward_impl(const Plan& pl, const void* X, const void* W, const int64_t* la
   L.check();
   hipLaunchKernelGGL(k_target<E>, dim3((unsigned)cdiv(rows_pad, 4)), dim3(256), 0, stream,
                      (const char*)xc, (const char*)W, (int)pl.H, (const int*)tgt,
-                     (const Counters*)ctr, zt);
+                     (const Counters*)ctr, zt, (int)pl.V);
   L.check();
   FwdArgs fa;
   fa.W = (const char*)W;
@@ -206,7 +213,7 @@ int forward_impl(const Plan& pl, const void* X, const void* W, const int64_t* la
   const int nb = (int)cdiv(pl.N, 256);
   hipLaunchKernelGGL(k_merge, dim3(nb), dim3(256), 0, stream, (const float2*)part,
                      (const Counters*)ctr, (const int*)rowpos, (const float*)zt,
-                     (int)pl.N, lse, bsum, none ? loss : (float*)nullptr);
+                     (int)pl.N, lse, bsum, none ? loss : (float*)nullptr, zt_out);
   L.check();
   hipLaunchKernelGGL(k_loss, dim3(1), dim3(256), 0, stream, (const float*)bsum, nb,
                      (const Counters*)ctr, reduction, none ? (float*)nullptr : loss, n_valid);
@@ -215,10 +222,11 @@ int forward_impl(const Plan& pl, const void* X, const void* W, const int64_t* la
 }
 
 template <class E>
-int backward_impl(const Plan& pl, const void* X, const void* W, const int64_t* labels,
-                  int64_t B, int64_t T, int64_t ignore_index, int reduction, int shift,
-                  const float* lse, const float* grad_scale, void* dX, void* dW,
-                  int grad_f32, int dw_acc, int32_t* status, char* ws, hipStream_t stream) {
+int backward_impl(const Plan& pl, const Shard& sh, const void* X, const void* W,
+                  const int64_t* labels, int64_t B, int64_t T, int64_t ignore_index,
+                  int reduction, int shift, const float* lse, const float* grad_scale,
+                  void* dX, void* dW, int dx_f32, int grad_f32, int dw_acc, int32_t* status,
+                  char* ws, hipStream_t stream) {
   Launch L{stream};
   Counters* ctr = (Counters*)(ws + pl.o_ctr);
   int* idx = (int*)(ws + pl.o_idx);
@@ -235,8 +243,9 @@ int backward_impl(const Plan& pl, const void* X, const void* W, const int64_t* l
   const bool none = reduction == FLCE_REDUCTION_NONE;
   float* rs = none && grad_scale ? (float*)(ws + pl.o_rs) : nullptr;
   hipLaunchKernelGGL(k_prep, dim3(1), dim3(1024), 0, stream, labels, (int)B, (int)T,
-                     ignore_index, pl.V, shift, reduction, none ? nullptr : grad_scale,
-                     cu_count(), (int)pl.fwd_items, idx, tgt, rowpos, ctr, status);
+                     ignore_index, sh.V_total, shift, reduction, none ? nullptr : grad_scale,
+                     cu_count(), (int)pl.fwd_items, sh.v_begin, pl.V, idx, tgt, rowpos, ctr,
+                     status);
   L.check();
   hipLaunchKernelGGL(k_gather, dim3((unsigned)cdiv(rows_pad, 4)), dim3(256), 0, stream,
                      (const char*)X, row_bytes, (const int*)idx, (const Counters*)ctr,
@@ -295,7 +304,7 @@ int backward_impl(const Plan& pl, const void* X, const void* W, const int64_t* l
   }
   hipLaunchKernelGGL(k_dx_final, dim3((unsigned)cdiv(pl.N, 4)), dim3(256), 0, stream,
                      (const float*)dx32, (const int*)rowpos, (int)pl.N, (int)pl.H,
-                     (char*)dX, grad_f32);
+                     (char*)dX, dx_f32);
   L.check();
   return L.err == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }
@@ -409,7 +418,7 @@ int chunked_impl(const ChunkPlan& pl, const void* X, const void* W, const int64_
 
   hipLaunchKernelGGL(k_prep, dim3(1), dim3(1024), 0, stream, labels, (int)B, (int)T,
                      ignore_index, pl.V, shift, reduction, none ? nullptr : grad_scale,
-                     cu_count(), 1, idx, tgt, rowpos, ctr, status);
+                     cu_count(), 1, (int64_t)0, pl.V, idx, tgt, rowpos, ctr, status);
   L.check();
   hipLaunchKernelGGL(k_gather, dim3((unsigned)cdiv(rows_pad, 4)), dim3(256), 0, stream,
                      (const char*)X, row_bytes, (const int*)idx, (const Counters*)ctr, xc,
@@ -418,7 +427,7 @@ int chunked_impl(const ChunkPlan& pl, const void* X, const void* W, const int64_
   L.check();
   hipLaunchKernelGGL(k_target<E>, dim3((unsigned)cdiv(rows_pad, 4)), dim3(256), 0, stream,
                      (const char*)xc, (const char*)W, (int)pl.H, (const int*)tgt,
-                     (const Counters*)ctr, zt);
+                     (const Counters*)ctr, zt, (int)pl.V);
   L.check();
   if (L.err == hipSuccess) L.err = allow_big_lds(k_chunk_z<E>);
   if (L.err == hipSuccess) L.err = allow_big_lds(k_bwd<E>);
@@ -549,10 +558,10 @@ int flce_forward(const void* X, const void* W, const int64_t* labels, int64_t B,
   if ((int64_t)workspace_bytes < p.total || !aligned16(workspace))
     return FLCE_ERR_WORKSPACE;
   if (dtype == FLCE_DTYPE_BF16)
-    return forward_impl<BF16>(p, X, W, labels, B, T, ignore_index, reduction, shift,
-                              loss, lse, n_valid, status, (char*)workspace, s);
-  return forward_impl<F32>(p, X, W, labels, B, T, ignore_index, reduction, shift, loss,
-                           lse, n_valid, status, (char*)workspace, s);
+    return forward_impl<BF16>(p, Shard{0, V}, X, W, labels, B, T, ignore_index, reduction,
+                              shift, loss, lse, n_valid, status, nullptr, (char*)workspace, s);
+  return forward_impl<F32>(p, Shard{0, V}, X, W, labels, B, T, ignore_index, reduction, shift,
+                           loss, lse, n_valid, status, nullptr, (char*)workspace, s);
 }
 
 int flce_backward(const void* X, const void* W, const int64_t* labels, int64_t B,
@@ -590,11 +599,154 @@ int flce_backward(const void* X, const void* W, const int64_t* labels, int64_t B
     return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
   }
   if (dtype == FLCE_DTYPE_BF16)
-    return backward_impl<BF16>(p, X, W, labels, B, T, ignore_index, reduction, shift, lse,
-                               grad_scale, dX, dW, gf32, dW_accumulate ? 1 : 0, status,
-                               (char*)workspace, s);
-  return backward_impl<F32>(p, X, W, labels, B, T, ignore_index, reduction, shift, lse,
-                            grad_scale, dX, dW, gf32, dW_accumulate ? 1 : 0, status,
+    return backward_impl<BF16>(p, Shard{0, V}, X, W, labels, B, T, ignore_index, reduction,
+                               shift, lse, grad_scale, dX, dW, gf32, gf32,
+                               dW_accumulate ? 1 : 0, status, (char*)workspace, s);
+  return backward_impl<F32>(p, Shard{0, V}, X, W, labels, B, T, ignore_index, reduction, shift,
+                            lse, grad_scale, dX, dW, gf32, gf32, dW_accumulate ? 1 : 0, status,
+                            (char*)workspace, s);
+}
+
+int flce_shard_forward(const void* X, const void* W, const int64_t* labels, int64_t B,
+                       int64_t T, int64_t H, int64_t V, int64_t v_begin, int64_t V_total,
+                       int dtype, int64_t ignore_index, int shift, float* lse, float* zt,
+                       int32_t* status, void* workspace, size_t workspace_bytes,
+                       void* stream) {
+  Plan p;
+  int rc = make_plan(B, T, H, V, dtype, &p);
+  if (rc != FLCE_OK) return rc;
+  if (v_begin < 0 || V_total < V || v_begin > V_total - V || V_total > kMaxI32 - 512)
+    return FLCE_ERR_SHAPE;
+  hipStream_t s = (hipStream_t)stream;
+  if (p.N == 0) {
+    hipLaunchKernelGGL(k_empty, dim3(1), dim3(1), 0, s, (float*)nullptr, (int64_t*)nullptr,
+                       status);
+    return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
+  }
+  if (X == nullptr || W == nullptr || labels == nullptr || lse == nullptr || zt == nullptr)
+    return FLCE_ERR_NULL;
+  if (!aligned16(X) || !aligned16(W) || ((uintptr_t)labels & 7u) || ((uintptr_t)lse & 3u) ||
+      ((uintptr_t)zt & 3u))
+    return FLCE_ERR_ALIGN;
+  if (workspace == nullptr) return FLCE_ERR_WORKSPACE;
+  if ((int64_t)workspace_bytes < p.total || !aligned16(workspace)) return FLCE_ERR_WORKSPACE;
+  const Shard sh{v_begin, V_total};
+  if (dtype == FLCE_DTYPE_BF16)
+    return forward_impl<BF16>(p, sh, X, W, labels, B, T, ignore_index, FLCE_REDUCTION_SUM,
+                              shift, nullptr, lse, nullptr, status, zt, (char*)workspace, s);
+  return forward_impl<F32>(p, sh, X, W, labels, B, T, ignore_index, FLCE_REDUCTION_SUM, shift,
+                           nullptr, lse, nullptr, status, zt, (char*)workspace, s);
+}
+
+int flce_shard_merge_workspace_size(int64_t B, int64_t T, size_t* bytes) {
+  if (bytes == nullptr) return FLCE_ERR_NULL;
+  if (B < 0 || T < 0 || B > kMaxI32 || T > kMaxI32 || B * T > (1ll << 24)) return FLCE_ERR_SHAPE;
+  const int64_t rows_pad = round_up(B * T > 0 ? B * T : 1, kTile);
+  *bytes = (size_t)(round_up(sizeof(Counters), kAlign) + 3 * round_up(4 * rows_pad, kAlign) +
+                    round_up(4 * cdiv(rows_pad, 256), kAlign));
+  return FLCE_OK;
+}
+
+int flce_shard_merge(const float* lse_shards, const float* zt_shards, int shards,
+                     const int64_t* labels, int64_t B, int64_t T, int64_t V_total,
+                     int64_t ignore_index, int shift, int reduction, float* loss, float* lse,
+                     int64_t* n_valid, int32_t* status, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  size_t need = 0;
+  int rc = flce_shard_merge_workspace_size(B, T, &need);
+  if (rc != FLCE_OK) return rc;
+  if (shards <= 0 || V_total <= 0 || V_total > kMaxI32 - 512) return FLCE_ERR_SHAPE;
+  if (reduction != FLCE_REDUCTION_MEAN && reduction != FLCE_REDUCTION_SUM &&
+      reduction != FLCE_REDUCTION_NONE)
+    return FLCE_ERR_REDUCTION;
+  if (loss == nullptr) return FLCE_ERR_NULL;
+  const int64_t N = B * T;
+  hipStream_t s = (hipStream_t)stream;
+  if (N == 0) {
+    hipLaunchKernelGGL(k_empty, dim3(1), dim3(1), 0, s,
+                       reduction == FLCE_REDUCTION_NONE ? (float*)nullptr : loss, n_valid,
+                       status);
+    return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
+  }
+  if (lse_shards == nullptr || zt_shards == nullptr || labels == nullptr || lse == nullptr)
+    return FLCE_ERR_NULL;
+  if (((uintptr_t)labels & 7u) || ((uintptr_t)lse & 3u) || ((uintptr_t)loss & 3u))
+    return FLCE_ERR_ALIGN;
+  if (workspace == nullptr || workspace_bytes < need || !aligned16(workspace))
+    return FLCE_ERR_WORKSPACE;
+  const int64_t rows_pad = round_up(N, kTile);
+  char* ws = (char*)workspace;
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) {
+    const int64_t o = off;
+    off = round_up(off + bytes, kAlign);
+    return o;
+  };
+  Counters* ctr = (Counters*)(ws + take(sizeof(Counters)));
+  int* idx = (int*)(ws + take(4 * rows_pad));
+  int* tgt = (int*)(ws + take(4 * rows_pad));
+  int* rowpos = (int*)(ws + take(4 * rows_pad));
+  float* bsum = (float*)(ws + take(4 * cdiv(rows_pad, 256)));
+  const bool none = reduction == FLCE_REDUCTION_NONE;
+  Launch L{s};
+  hipLaunchKernelGGL(k_prep, dim3(1), dim3(1024), 0, s, labels, (int)B, (int)T, ignore_index,
+                     V_total, shift, reduction, (const float*)nullptr, cu_count(), 1,
+                     (int64_t)0, V_total, idx, tgt, rowpos, ctr, status);
+  L.check();
+  const int nb = (int)cdiv(N, 256);
+  hipLaunchKernelGGL(k_shard_merge, dim3((unsigned)nb), dim3(256), 0, s, lse_shards, zt_shards,
+                     shards, (int)N, (const int*)rowpos, (const Counters*)ctr, lse, bsum,
+                     none ? loss : (float*)nullptr);
+  L.check();
+  hipLaunchKernelGGL(k_loss, dim3(1), dim3(256), 0, s, (const float*)bsum, nb,
+                     (const Counters*)ctr, reduction, none ? (float*)nullptr : loss, n_valid);
+  L.check();
+  return L.err == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
+}
+
+int flce_shard_backward(const void* X, const void* W, const int64_t* labels, int64_t B,
+                        int64_t T, int64_t H, int64_t V, int64_t v_begin, int64_t V_total,
+                        int dtype, int64_t ignore_index, int reduction, int shift,
+                        const float* lse, const float* grad_scale, float* dX_partial, void* dW,
+                        int grad_dtype, int dW_accumulate, int32_t* status, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  Plan p;
+  int rc = make_plan(B, T, H, V, dtype, &p);
+  if (rc != FLCE_OK) return rc;
+  if (v_begin < 0 || V_total < V || v_begin > V_total - V || V_total > kMaxI32 - 512)
+    return FLCE_ERR_SHAPE;
+  if (reduction != FLCE_REDUCTION_MEAN && reduction != FLCE_REDUCTION_SUM &&
+      reduction != FLCE_REDUCTION_NONE)
+    return FLCE_ERR_REDUCTION;
+  if (grad_dtype != dtype && grad_dtype != FLCE_DTYPE_F32) return FLCE_ERR_DTYPE;
+  if (W == nullptr || dW == nullptr) return FLCE_ERR_NULL;
+  if (p.N > 0 && (X == nullptr || labels == nullptr || lse == nullptr || dX_partial == nullptr))
+    return FLCE_ERR_NULL;
+  const int64_t ges = grad_dtype == FLCE_DTYPE_F32 ? 4 : 2;
+  if (!aligned16(W) || !aligned16(dW) ||
+      (p.N > 0 && (!aligned16(X) || !aligned16(dX_partial))) || ((uintptr_t)labels & 7u) ||
+      ((uintptr_t)lse & 3u))
+    return FLCE_ERR_ALIGN;
+  if (overlaps(dW, p.V * p.H * ges, W, p.V * p.H * p.es)) return FLCE_ERR_ALIAS;
+  if (p.N > 0 && overlaps(dX_partial, p.N * p.H * 4, X, p.N * p.H * p.es)) return FLCE_ERR_ALIAS;
+  if (workspace == nullptr) return FLCE_ERR_WORKSPACE;
+  if ((int64_t)workspace_bytes < p.total || !aligned16(workspace)) return FLCE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  const int gf32 = grad_dtype == FLCE_DTYPE_F32 ? 1 : 0;
+  if (p.N == 0) {
+    if (!dW_accumulate) zero_fill(dW, p.V * p.H * ges, s);
+    if (status != nullptr)
+      hipLaunchKernelGGL(k_empty, dim3(1), dim3(1), 0, s, (float*)nullptr, (int64_t*)nullptr,
+                         status);
+    return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
+  }
+  const Shard sh{v_begin, V_total};
+  if (dtype == FLCE_DTYPE_BF16)
+    return backward_impl<BF16>(p, sh, X, W, labels, B, T, ignore_index, reduction, shift, lse,
+                               grad_scale, dX_partial, dW, 1, gf32, dW_accumulate ? 1 : 0,
+                               status, (char*)workspace, s);
+  return backward_impl<F32>(p, sh, X, W, labels, B, T, ignore_index, reduction, shift, lse,
+                            grad_scale, dX_partial, dW, 1, gf32, dW_accumulate ? 1 : 0, status,
                             (char*)workspace, s);
 }
 

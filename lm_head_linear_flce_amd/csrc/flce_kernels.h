@@ -42,13 +42,17 @@ constexpr int kStatusLabelRange = 8;
 
 // ---------------------------------------------------------------------------
 // k_prep: one workgroup of 1024 threads walks the rows in order, so the
-// compacted order is the row order (deterministic).
+// compacted order is the row order (deterministic).  Labels are checked
+// against V (the whole vocabulary); targets are stored relative to v_begin,
+// the first vocabulary row of this call's W (V_local rows; a vocabulary
+// shard), so a target outside the shard has an index outside [0, V_local).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void k_prep(
     const int64_t* __restrict__ labels, int B, int T, int64_t ignore,
     int64_t V, int shift, int reduction, const float* __restrict__ grad_scale,
-    int ncu, int max_items, int* __restrict__ idx, int* __restrict__ tgt, int* __restrict__ rowpos,
-    Counters* __restrict__ ctr, int32_t* __restrict__ status_out) {
+    int ncu, int max_items, int64_t v_begin, int64_t V_local, int* __restrict__ idx,
+    int* __restrict__ tgt, int* __restrict__ rowpos, Counters* __restrict__ ctr,
+    int32_t* __restrict__ status_out) {
   __shared__ int wsum[16];
   __shared__ int base_s;
   __shared__ int bad_s;
@@ -86,7 +90,7 @@ __global__ __launch_bounds__(1024) void k_prep(
       rowpos[i] = valid ? pos : -1;
       if (valid) {
         idx[pos] = i;
-        tgt[pos] = (int)y;
+        tgt[pos] = (int)(y - v_begin);   // index into this call's W rows
       }
     }
     __syncthreads();
@@ -103,7 +107,7 @@ __global__ __launch_bounds__(1024) void k_prep(
   // waves(P) * ceil(VT / P) tiles; thread t prices P = t + 1 and the
   // cheapest (then the smallest) P wins.
   const int n = base_s;
-  const int64_t VT = (V + kTile - 1) / kTile;
+  const int64_t VT = (V_local + kTile - 1) / kTile;
   const int64_t TTn = n > 0 ? (n + kTile - 1) / kTile : 1;
   if (tid == 0) best_s = ~0ull;
   __syncthreads();
@@ -167,10 +171,14 @@ template <class E>
 __global__ __launch_bounds__(256) void k_target(
     const char* __restrict__ Xc, const char* __restrict__ W, int H,
     const int* __restrict__ tgt, const Counters* __restrict__ ctr,
-    float* __restrict__ zt) {
+    float* __restrict__ zt, int V_local) {
   const int k = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (k >= ctr->n) return;
+  if (tgt[k] < 0 || tgt[k] >= V_local) {   // target in another vocabulary shard
+    if (lane == 0) zt[k] = 0.f;
+    return;
+  }
   const int row_bytes = H * E::kBytes;
   const i32x4* x = (const i32x4*)(Xc + (int64_t)k * row_bytes);
   const i32x4* w = (const i32x4*)(W + (int64_t)tgt[k] * row_bytes);
@@ -326,7 +334,8 @@ void k_fwd_lse(FwdArgs a) {
 __global__ __launch_bounds__(256) void k_merge(
     const float2* __restrict__ part, const Counters* __restrict__ ctr,
     const int* __restrict__ rowpos, const float* __restrict__ zt, int N,
-    float* __restrict__ lse_out, float* __restrict__ blocksum, float* __restrict__ rloss_out) {
+    float* __restrict__ lse_out, float* __restrict__ blocksum, float* __restrict__ rloss_out,
+    float* __restrict__ zt_out) {
   __shared__ float red[256];
   const int i = blockIdx.x * 256 + threadIdx.x;
   const int P = ctr->fwd_p, TTn = (ctr->n + kTile - 1) / kTile;
@@ -350,6 +359,8 @@ __global__ __launch_bounds__(256) void k_merge(
     lse_out[i] = lse;
     // per-row losses (reduction "none"): 0 on ignored rows, NaN after a bad label
     if (rloss_out) rloss_out[i] = ctr->status ? __builtin_nanf("") : li;
+    // a vocabulary shard's target logits (0 where the target is elsewhere)
+    if (zt_out) zt_out[i] = k >= 0 ? zt[k] : 0.f;
   }
   red[threadIdx.x] = li;
   __syncthreads();
@@ -967,6 +978,41 @@ __global__ __launch_bounds__(256) void k_scale_grads(char* __restrict__ p, int64
     }
     *q = u;
   }
+}
+
+// Vocabulary shards: row i's lse is the log-sum-exp of the shards' lse and its
+// target logit the sum of the shards' (exactly one holds it); one thread per
+// original row, fixed-order block sums of the row losses.
+__global__ __launch_bounds__(256) void k_shard_merge(
+    const float* __restrict__ lse_g, const float* __restrict__ zt_g, int shards, int N,
+    const int* __restrict__ rowpos, const Counters* __restrict__ ctr,
+    float* __restrict__ lse_out, float* __restrict__ blocksum, float* __restrict__ rloss_out) {
+  __shared__ float red[256];
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  float li = 0.f;
+  if (i < N) {
+    float lse = 0.f;
+    if (rowpos[i] >= 0) {
+      float M = -INFINITY, z = 0.f;
+      for (int g = 0; g < shards; ++g) M = fmaxf(M, lse_g[(int64_t)g * N + i]);
+      float S = 0.f;
+      for (int g = 0; g < shards; ++g) {
+        S += expf(lse_g[(int64_t)g * N + i] - M);
+        z += zt_g[(int64_t)g * N + i];
+      }
+      lse = M + logf(S);
+      li = lse - z;
+    }
+    lse_out[i] = lse;
+    if (rloss_out) rloss_out[i] = ctr->status ? __builtin_nanf("") : li;
+  }
+  red[threadIdx.x] = li;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if (threadIdx.x < w) red[threadIdx.x] += red[threadIdx.x + w];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) blocksum[blockIdx.x] = red[0];
 }
 
 __global__ __launch_bounds__(256) void k_dx_final(

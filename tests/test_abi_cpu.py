@@ -188,3 +188,55 @@ def test_chunk_rows_parameter():
     # at most the padded row count
     assert (F.flce_chunked_workspace_size(1, 1000, H, V, F.FLCE_DTYPE_BF16, 1 << 20)
             == F.flce_chunked_workspace_size(1, 1000, H, V, F.FLCE_DTYPE_BF16, 1024))
+
+
+def sfwd(**kw):
+    a = dict(X=P, W=2 * P, labels=3 * P, B=1, T=16, H=128, V=50, v_begin=10, V_total=100,
+             dtype=F.FLCE_DTYPE_BF16, ignore_index=-100, shift=0, lse=5 * P, zt=4 * P,
+             status=0, workspace=6 * P, workspace_bytes=1 << 30, stream=0)
+    a.update(kw)
+    return F.flce_shard_forward(*a.values())
+
+
+def sbwd(**kw):
+    a = dict(X=P, W=2 * P, labels=3 * P, B=1, T=16, H=128, V=50, v_begin=10, V_total=100,
+             dtype=F.FLCE_DTYPE_BF16, ignore_index=-100, reduction=F.FLCE_REDUCTION_MEAN,
+             shift=0, lse=5 * P, grad_scale=0, dX_partial=7 * P, dW=8 * P,
+             grad_dtype=F.FLCE_DTYPE_BF16, dW_accumulate=0, status=0, workspace=6 * P,
+             workspace_bytes=1 << 30, stream=0)
+    a.update(kw)
+    return F.flce_shard_backward(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(v_begin=60), F.FLCE_ERR_SHAPE), (dict(v_begin=-1), F.FLCE_ERR_SHAPE),
+    (dict(V_total=40), F.FLCE_ERR_SHAPE), (dict(zt=0), F.FLCE_ERR_NULL),
+    (dict(lse=0), F.FLCE_ERR_NULL), (dict(H=100), F.FLCE_ERR_ALIGN),
+    (dict(workspace_bytes=64), F.FLCE_ERR_WORKSPACE),
+])
+def test_shard_forward_host_checks(kw, code):
+    assert sfwd(**kw) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(v_begin=51), F.FLCE_ERR_SHAPE), (dict(dX_partial=0), F.FLCE_ERR_NULL),
+    (dict(dW=0), F.FLCE_ERR_NULL), (dict(reduction=3), F.FLCE_ERR_REDUCTION),
+    (dict(dX_partial=P), F.FLCE_ERR_ALIAS), (dict(grad_dtype=5), F.FLCE_ERR_DTYPE),
+    (dict(workspace=0), F.FLCE_ERR_WORKSPACE),
+])
+def test_shard_backward_host_checks(kw, code):
+    assert sbwd(**kw) == code
+
+
+def test_shard_merge_host_checks():
+    ws = F.flce_shard_merge_workspace_size(2, 1000)
+    args = dict(lse_shards=P, zt_shards=2 * P, shards=3, labels=3 * P, B=2, T=1000,
+                V_total=100, ignore_index=-100, shift=1, reduction=F.FLCE_REDUCTION_MEAN,
+                loss=4 * P, lse=5 * P, n_valid=0, status=0, workspace=6 * P,
+                workspace_bytes=ws, stream=0)
+    for kw, code in ((dict(shards=0), F.FLCE_ERR_SHAPE), (dict(lse_shards=0), F.FLCE_ERR_NULL),
+                     (dict(reduction=7), F.FLCE_ERR_REDUCTION),
+                     (dict(workspace_bytes=ws - 1), F.FLCE_ERR_WORKSPACE)):
+        a = dict(args)
+        a.update(kw)
+        assert F.flce_shard_merge(*a.values()) == code

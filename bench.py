@@ -39,12 +39,20 @@ PROFILES = os.path.join(ROOT, "profiles")
 # run from /tmp with TMPDIR=/tmp)
 PROFILE_COMMANDS = (
     "rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof_trace -o flce "
-    "-- python $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+    "-- python $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-chunked",
     "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/prof_fetch -o flce "
-    "-- python $R/bench.py --steps 1 --warmup 0 --no-cpu-baseline --copy-calibration",
+    "-- python $R/bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-chunked "
+    "--copy-calibration",
     "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof_write -o flce "
-    "-- python $R/bench.py --steps 1 --warmup 0 --no-cpu-baseline --copy-calibration",
+    "-- python $R/bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-chunked "
+    "--copy-calibration",
     "python $R/bench.py --summarize $R/gpurun_out",
+)
+# the chunked mode's own kernel trace (profiles/flce_qwen2_7b_head_chunked_kernels.md)
+CHUNKED_PROFILE_COMMANDS = (
+    "rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof_chunk -o flce "
+    "-- python $R/bench.py --steps 3 --warmup 1 --chunked-only",
+    "python $R/bench.py --summarize-chunked $R/gpurun_out",
 )
 TRAFFIC = os.path.join(PROFILES, "traffic_qwen2_7b_head.json")
 METRIC = "fused linear-CE fwd+bwd tokens/sec and % bf16 MFMA peak; peak extra HBM bytes"
@@ -59,6 +67,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-chunked", action="store_true",
                     help="skip the chunked-mode measurement")
+    ap.add_argument("--chunked-only", action="store_true",
+                    help="measure only the chunked mode and print its figures (for "
+                         "CHUNKED_PROFILE_COMMANDS)")
+    ap.add_argument("--summarize-chunked", metavar="DIR",
+                    help="summarise DIR/prof_chunk of CHUNKED_PROFILE_COMMANDS into profiles/")
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--summarize", metavar="DIR",
                     help="summarise the rocprofv3 output of PROFILE_COMMANDS under DIR "
@@ -162,16 +175,20 @@ def _short(name):
     return name.replace("flce::", "")
 
 
-def summarize(prof_dir, command):
+def summarize(prof_dir, command, trace="prof_trace", out="flce_qwen2_7b_head_kernels.md",
+              title="Kernel time and HBM traffic: Qwen2-7B-like LM head (forward + "
+                    "backward)"):
     """Kernel-trace statistics and calibrated HBM traffic -> profiles/."""
     import csv
     import glob
-    stats = glob.glob(os.path.join(prof_dir, "prof_trace", "**", "*kernel_stats.csv"),
+    stats = glob.glob(os.path.join(prof_dir, trace, "**", "*kernel_stats.csv"),
                       recursive=True)
-    pmcs = [p for sub in ("prof_fetch", "prof_write") for p in glob.glob(
-        os.path.join(prof_dir, sub, "**", "*counter_collection.csv"), recursive=True)]
-    lines = ["# Kernel time and HBM traffic: Qwen2-7B-like LM head, N=8192 H=3584 "
-             "V=152064 bf16", "", f"kernel source hash: `{source_hash()}`", "",
+    pmcs = [] if trace != "prof_trace" else [p for sub in ("prof_fetch", "prof_write")
+                                             for p in glob.glob(os.path.join(
+                                                 prof_dir, sub, "**", "*counter_collection.csv"),
+                                                 recursive=True)]
+    lines = [f"# {title}, N=8192 H=3584 V=152064 bf16", "",
+             f"kernel source hash: `{source_hash()}`", "",
              "Commands (run from /tmp with TMPDIR=/tmp; $R = repository root):", "",
              "```", *command, "```", ""]
     rows = []
@@ -221,7 +238,14 @@ def summarize(prof_dir, command):
         lines.append(f"| {n} | {d['FETCH_SIZE'][1]} | {fe / 1e6:.1f} | {wr / 1e6:.1f} | "
                      f"{(fe + wr) / 1e6:.1f} |")
     os.makedirs(PROFILES, exist_ok=True)
-    md = os.path.join(PROFILES, "flce_qwen2_7b_head_kernels.md")
+    md = os.path.join(PROFILES, out)
+    if not pmcs:
+        os.makedirs(PROFILES, exist_ok=True)
+        with open(md, "w") as f:
+            f.write("\n".join(lines[:lines.index("## HBM traffic (rocprofv3 --pmc FETCH_SIZE, "
+                                                   "then --pmc WRITE_SIZE)")]) + "\n")
+        print(md)
+        return
     with open(md, "w") as f:
         f.write("\n".join(lines) + "\n")
     with open(TRAFFIC, "w") as f:
@@ -271,6 +295,11 @@ def main():
     if args.summarize:
         summarize(args.summarize, PROFILE_COMMANDS)
         return
+    if args.summarize_chunked:
+        summarize(args.summarize_chunked, CHUNKED_PROFILE_COMMANDS, trace="prof_chunk",
+                  out="flce_qwen2_7b_head_chunked_kernels.md",
+                  title="Kernel time: Qwen2-7B-like LM head, chunked mode (flce_chunked)")
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path "
               "has no multi-GPU mode", file=sys.stderr)
@@ -290,6 +319,11 @@ def main():
     lab = torch.from_numpy(w.labels).to(dev)
     dcode = F.FLCE_DTYPE_BF16 if w.dtype == "bf16" else F.FLCE_DTYPE_F32
     n_valid = int(((lab[:, 1:] if w.shift else lab) != w.ignore_index).sum())
+    peak = BF16_PEAK if w.dtype == "bf16" else F32_PEAK
+    if args.chunked_only:
+        print(json.dumps({"chunked_mode": chunked_mode(F, X, W, lab, w, dcode, dev, args,
+                                                       peak)}), flush=True)
+        return
     ws, ws_bytes = F.workspace(w.B, w.T, w.H, w.V, dcode, dev)
     torch.cuda.synchronize()
 

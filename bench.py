@@ -67,6 +67,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-chunked", action="store_true",
                     help="skip the chunked-mode measurement")
+    ap.add_argument("--chunk-rows", type=int, default=0,
+                    help="rows per chunk of the chunked mode (0 = 1 GiB slab budget)")
     ap.add_argument("--chunked-only", action="store_true",
                     help="measure only the chunked mode and print its figures (for "
                          "CHUNKED_PROFILE_COMMANDS)")
@@ -263,11 +265,11 @@ def chunked_mode(F, X, W, lab, w, dcode, dev, args, peak):
     torch.cuda.empty_cache()
     torch.cuda.reset_peak_memory_stats()
     base = torch.cuda.memory_allocated()
-    ws, ws_bytes = F.chunked_workspace(w.B, w.T, w.H, w.V, dcode, dev)
+    ws, ws_bytes = F.chunked_workspace(w.B, w.T, w.H, w.V, dcode, dev, args.chunk_rows)
 
     def step():
         return F.chunked(X, W, lab, ignore_index=w.ignore_index, shift=w.shift,
-                         reduction=w.reduction, ws=ws)
+                         reduction=w.reduction, ws=ws, chunk_rows=args.chunk_rows)
 
     out = step()
     torch.cuda.synchronize()
@@ -283,7 +285,7 @@ def chunked_mode(F, X, W, lab, w, dcode, dev, args, peak):
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
     N, H, V = w.N, w.H, w.V
     print(f"[bench] chunked mode: {ms:.3f} ms/step", file=sys.stderr, flush=True)
-    return {"ms_per_step": ms, "tokens_per_s": N / (ms / 1e3),
+    return {"ms_per_step": ms, "tokens_per_s": N / (ms / 1e3), "chunk_rows": args.chunk_rows,
             "mfma_frac_model": 6.0 * N * H * V / (ms / 1e3) / peak,
             "workspace_bytes": int(ws_bytes), "peak_extra_bytes": int(peak_extra),
             "note": "flce_chunked: gradients formed with the logits over row chunks "

@@ -146,13 +146,12 @@ struct Timed {
   Timed(const char* kernel, hipStream_t stream) : s(stream) {
     on = g_timing.events != nullptr && g_timing.count != nullptr &&
          *g_timing.count < g_timing.capacity && strcmp(kernel, g_timing.name) == 0;
-    if (on) hipEventRecord(g_timing.events[2 * *g_timing.count], s);
+    // a launch whose events cannot be recorded is left out of the count
+    if (on) on = hipEventRecord(g_timing.events[2 * *g_timing.count], s) == hipSuccess;
   }
   ~Timed() {
-    if (on) {
-      hipEventRecord(g_timing.events[2 * *g_timing.count + 1], s);
+    if (on && hipEventRecord(g_timing.events[2 * *g_timing.count + 1], s) == hipSuccess)
       ++*g_timing.count;
-    }
   }
 };
 

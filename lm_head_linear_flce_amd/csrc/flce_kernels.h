@@ -288,12 +288,13 @@ void k_fwd_lse(FwdArgs a) {
   B.ldb = ldb;
   B.kbytes = ldb;
 
-  float m[4], s[4];
+  // The running (max, sum) of the lane's 4 token columns live in LDS between
+  // tiles (each thread owns its slots): held in registers they would be live
+  // across the K loop, which needs every register, and be spilled.
+  __shared__ float2 ms_s[4][kThreads];
+  const int t = threadIdx.x;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    m[j] = -INFINITY;
-    s[j] = 0.f;
-  }
+  for (int j = 0; j < 4; ++j) ms_s[j][t] = make_float2(-INFINITY, 0.f);
   f32x16 acc[4][4];
   for (int vt = vt0; vt < vt1; ++vt) {
     Opnd A;
@@ -302,12 +303,20 @@ void k_fwd_lse(FwdArgs a) {
     A.ldb = ldb;
     A.kbytes = ldb;
     zero_acc(acc);
-    gemm_tile<E, LoadDirect, LoadDirect>(A, B, steps, smem, wm, wn,
-                                         acc);
+    gemm_tile<E, LoadDirect, LoadDirect>(A, B, steps, smem, wm, wn, acc, opaque_tid());
     // rows at or past V (last tile only) take no part in the reduction
     const int vlim = a.V - vt * kTile;
+    float m[4], s[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float2 v = ms_s[j][t];
+      m[j] = v.x;
+      s[j] = v.y;
+    }
     if (vlim >= kTile) lse_update<false>(acc, m, s, 0);
     else lse_update<true>(acc, m, s, vlim - wm * 128 - 4 * (lane >> 5));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ms_s[j][t] = make_float2(m[j], s[j]);
   }
   // combine the two lane halves and the two waves that share tokens
   typedef __attribute__((address_space(3))) float lf;
@@ -315,11 +324,11 @@ void k_fwd_lse(FwdArgs a) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = ((wm * 2 + (lane >> 5)) * kTile + acc_col(wn, j, lane)) * 2;
-    st[e] = m[j];
-    st[e + 1] = s[j];
+    const float2 v = ms_s[j][t];
+    st[e] = v.x;
+    st[e + 1] = v.y;
   }
   __syncthreads();
-  const int t = threadIdx.x;
   float M = -INFINITY, S = 0.f;
 #pragma unroll
   for (int q = 0; q < 4; ++q) lse_merge(M, S, st[(q * kTile + t) * 2], st[(q * kTile + t) * 2 + 1]);

@@ -126,8 +126,9 @@ struct LoadDirect {
   // the descriptor covers at most the tile's 256 rows (< 2^31 bytes, as H is
   // bounded), so the offset 2^31 is always out of range.
   template <class E>
-  __device__ __forceinline__ void issue_part(const Opnd& o, int s, int part, bool live) {
-    const int c = threadIdx.x & 7, rr = threadIdx.x >> 3;
+  __device__ __forceinline__ void issue_part(const Opnd& o, int s, int part, bool live,
+                                             int tid) {
+    const int c = tid & 7, rr = tid >> 3;
     const int64_t span = (int64_t)kTile * o.ldb;
     const rsrc_t r = make_rsrc(o.base, live ? (o.bytes < span ? o.bytes : span) : 0);
     const int kb = s * kRowBytes + c * 16;
@@ -137,20 +138,20 @@ struct LoadDirect {
       v[i] = bload128(r, ok ? (rr + 32 * i) * o.ldb + kb : (int)0x80000000u);
   }
   template <class E>
-  __device__ __forceinline__ void issue(const Opnd& o, int s, bool live) {
+  __device__ __forceinline__ void issue(const Opnd& o, int s, bool live, int tid) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) issue_part<E>(o, s, q, live);
+    for (int q = 0; q < 4; ++q) issue_part<E>(o, s, q, live, tid);
   }
   // quarter `part` (0..3) of the stores: register rows 2*part, 2*part+1
-  __device__ __forceinline__ void commit_part(lds_t* slab, int part) const {
-    const int c = threadIdx.x & 7, rr = threadIdx.x >> 3;
+  __device__ __forceinline__ void commit_part(lds_t* slab, int part, int tid) const {
+    const int c = tid & 7, rr = tid >> 3;
 #pragma unroll
     for (int i = 2 * part; i < 2 * part + 2; ++i)
       *(__attribute__((address_space(3))) i32x4*)(slab + swz(rr + 32 * i, c)) = v[i];
   }
-  __device__ __forceinline__ void commit(lds_t* slab) const {
+  __device__ __forceinline__ void commit(lds_t* slab, int tid) const {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) commit_part(slab, q);
+    for (int q = 0; q < 4; ++q) commit_part(slab, q, tid);
   }
 };
 
@@ -162,8 +163,8 @@ typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 // Fragment reader of a K-major slab: one ds_read_b128 per 32-row block.
 struct LoadDirect::Frag {
   int off[4];   // per chunk pair p
-  __device__ __forceinline__ explicit Frag(int row_base) {
-    const int lane = threadIdx.x & 63, r32 = lane & 31, h = lane >> 5;
+  __device__ __forceinline__ Frag(int row_base, int lane) {
+    const int r32 = lane & 31, h = lane >> 5;
 #pragma unroll
     for (int p = 0; p < 4; ++p) off[p] = swz(row_base + r32, 2 * p + h);
   }
@@ -188,28 +189,29 @@ struct LoadMN<BF16> {
   static constexpr bool kTransposed = true;
   i32x4 v[8];
   template <class E>
-  __device__ __forceinline__ void issue_part(const Opnd& o, int s, int part, bool live) {
-    const int c = threadIdx.x & 31, kr = threadIdx.x >> 5;
+  __device__ __forceinline__ void issue_part(const Opnd& o, int s, int part, bool live,
+                                             int tid) {
+    const int c = tid & 31, kr = tid >> 5;
     const int64_t k0 = (int64_t)s * BF16::kKStep;
     const rsrc_t r = make_rsrc(o.base + k0 * o.ldb, live ? o.bytes - k0 * o.ldb : 0);
 #pragma unroll
     for (int i = 2 * part; i < 2 * part + 2; ++i) v[i] = bload128(r, (kr + 8 * i) * o.ldb + c * 16);
   }
   template <class E>
-  __device__ __forceinline__ void issue(const Opnd& o, int s, bool live) {
+  __device__ __forceinline__ void issue(const Opnd& o, int s, bool live, int tid) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) issue_part<E>(o, s, q, live);
+    for (int q = 0; q < 4; ++q) issue_part<E>(o, s, q, live, tid);
   }
-  __device__ __forceinline__ void commit_part(lds_t* slab, int part) const {
-    const int c = threadIdx.x & 31, kr = threadIdx.x >> 5;
+  __device__ __forceinline__ void commit_part(lds_t* slab, int part, int tid) const {
+    const int c = tid & 31, kr = tid >> 5;
     const int base = kr * 512 + ((c ^ (4 * (kr & 3))) << 4);
 #pragma unroll
     for (int i = 2 * part; i < 2 * part + 2; ++i)
       *(__attribute__((address_space(3))) i32x4*)(slab + base + i * 4096) = v[i];
   }
-  __device__ __forceinline__ void commit(lds_t* slab) const {
+  __device__ __forceinline__ void commit(lds_t* slab, int tid) const {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) commit_part(slab, q);
+    for (int q = 0; q < 4; ++q) commit_part(slab, q, tid);
   }
   // Lane l = 16 G + j of a wave: the group of 16 reads K rows 8(G/2) + j/4
   // (+ 16 p + 4 r), columns cb + 16 (G&1) + 4 (j&3) .. +3; ds_read_b64_tr_b16
@@ -217,8 +219,8 @@ struct LoadMN<BF16> {
   // first four of its eight, r = 1 the last four.
   struct Frag {
     int off[4];   // per 32-column block i
-    __device__ __forceinline__ explicit Frag(int col_base) {
-      const int lane = threadIdx.x & 63, G = lane >> 4, j = lane & 15;
+    __device__ __forceinline__ Frag(int col_base, int lane) {
+      const int G = lane >> 4, j = lane & 15;
       const int k = 8 * (G >> 1) + (j >> 2);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -243,33 +245,33 @@ struct LoadMN<F32> {
   static constexpr bool kTransposed = true;
   i32x4 v[8];
   template <class E>
-  __device__ __forceinline__ void issue_part(const Opnd& o, int s, int part, bool live) {
-    const int c = threadIdx.x & 63, kr = threadIdx.x >> 6;
+  __device__ __forceinline__ void issue_part(const Opnd& o, int s, int part, bool live,
+                                             int tid) {
+    const int c = tid & 63, kr = tid >> 6;
     const int64_t k0 = (int64_t)s * F32::kKStep;
     const rsrc_t r = make_rsrc(o.base + k0 * o.ldb, live ? o.bytes - k0 * o.ldb : 0);
 #pragma unroll
     for (int i = 2 * part; i < 2 * part + 2; ++i) v[i] = bload128(r, (kr + 4 * i) * o.ldb + c * 16);
   }
   template <class E>
-  __device__ __forceinline__ void issue(const Opnd& o, int s, bool live) {
+  __device__ __forceinline__ void issue(const Opnd& o, int s, bool live, int tid) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) issue_part<E>(o, s, q, live);
+    for (int q = 0; q < 4; ++q) issue_part<E>(o, s, q, live, tid);
   }
-  __device__ __forceinline__ void commit_part(lds_t* slab, int part) const {
-    const int c = threadIdx.x & 63, kr = threadIdx.x >> 6;
+  __device__ __forceinline__ void commit_part(lds_t* slab, int part, int tid) const {
+    const int c = tid & 63, kr = tid >> 6;
 #pragma unroll
     for (int i = 2 * part; i < 2 * part + 2; ++i)
       *(__attribute__((address_space(3))) i32x4*)(slab + (kr + 4 * i) * 1024 + c * 16) = v[i];
   }
-  __device__ __forceinline__ void commit(lds_t* slab) const {
+  __device__ __forceinline__ void commit(lds_t* slab, int tid) const {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) commit_part(slab, q);
+    for (int q = 0; q < 4; ++q) commit_part(slab, q, tid);
   }
   // lane (column l%32, half h) takes k = 8p + 4h + e, e = 0..3
   struct Frag {
     int off;
-    __device__ __forceinline__ explicit Frag(int col_base) {
-      const int lane = threadIdx.x & 63;
+    __device__ __forceinline__ Frag(int col_base, int lane) {
       off = 4 * (lane >> 5) * 1024 + (col_base + (lane & 31)) * 4;
     }
     __device__ __forceinline__ i32x4 read(const lds_t* slab, int p, int i) const {
@@ -394,15 +396,17 @@ struct TilePipe {
   const Opnd& A;
   const Opnd& B;
   int steps;
+  int tid;
   lds_t* sa;
   lds_t* sb;
   typename LA::Frag fa;
   typename LB::Frag fb;
 
+  // `t`: the thread index (see gemm_tile)
   __device__ __forceinline__ TilePipe(const Opnd& a, const Opnd& b, int n, lds_t* smem,
-                                      int wm, int wn)
-      : A(a), B(b), steps(n), sa(smem), sb(smem + 2 * kSlab), fa(wm * 128),
-        fb(wn * 128) {}
+                                      int wm, int wn, int t)
+      : A(a), B(b), steps(n), tid(t), sa(smem), sb(smem + 2 * kSlab),
+        fa(wm * 128, t & 63), fb(wn * 128, t & 63) {}
 
   // one step s with s % 2 == k: MFMAs on slab k, the loads of step s + 1 go to
   // slab k ^ 1, the loads of step s + 2 are issued into registers k.  Steps
@@ -412,21 +416,21 @@ struct TilePipe {
   __device__ __forceinline__ void step(int s, f32x16 (&acc)[4][4]) {
     const bool live = s + 2 < steps;
     mma_slab<E>(sa + k * kSlab, sb + k * kSlab, fa, fb, acc, [&](int part) {
-      la[k ^ 1].commit_part(sa + (k ^ 1) * kSlab, part);
-      lb[k ^ 1].commit_part(sb + (k ^ 1) * kSlab, part);
-      la[k].template issue_part<E>(A, s + 2, part, live);
-      lb[k].template issue_part<E>(B, s + 2, part, live);
+      la[k ^ 1].commit_part(sa + (k ^ 1) * kSlab, part, tid);
+      lb[k ^ 1].commit_part(sb + (k ^ 1) * kSlab, part, tid);
+      la[k].template issue_part<E>(A, s + 2, part, live, tid);
+      lb[k].template issue_part<E>(B, s + 2, part, live, tid);
     });
     __syncthreads();
   }
   __device__ __forceinline__ void run(f32x16 (&acc)[4][4]) {
     if (steps <= 0) return;
-    la[0].template issue<E>(A, 0, true);
-    lb[0].template issue<E>(B, 0, true);
-    la[1].template issue<E>(A, 1, steps > 1);
-    lb[1].template issue<E>(B, 1, steps > 1);
-    la[0].commit(sa);
-    lb[0].commit(sb);
+    la[0].template issue<E>(A, 0, true, tid);
+    lb[0].template issue<E>(B, 0, true, tid);
+    la[1].template issue<E>(A, 1, steps > 1, tid);
+    lb[1].template issue<E>(B, 1, steps > 1, tid);
+    la[0].commit(sa, tid);
+    lb[0].commit(sb, tid);
     __syncthreads();
     for (int s = 0; s < steps; s += 2) {
       step<0>(s, acc);
@@ -435,12 +439,23 @@ struct TilePipe {
   }
 };
 
+// One tile.  A kernel that runs several tiles in a loop passes the thread
+// index through opaque_tid(), so that the loaders' address arithmetic is
+// redone per tile instead of being hoisted out of that loop (where it would
+// stay live across the loop's epilogue and be spilled).
 template <class E, class LA, class LB>
 __device__ __forceinline__ void gemm_tile(const Opnd& A, const Opnd& B, int steps,
                                           lds_t* smem, int wm, int wn,
-                                          f32x16 (&acc)[4][4]) {
-  TilePipe<E, LA, LB> pipe(A, B, steps, smem, wm, wn);
+                                          f32x16 (&acc)[4][4], int tid = threadIdx.x) {
+  TilePipe<E, LA, LB> pipe(A, B, steps, smem, wm, wn, tid);
   pipe.run(acc);
+}
+
+__device__ __forceinline__ int opaque_tid() {
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  __builtin_assume(tid >= 0 && tid < kThreads);
+  return tid;
 }
 
 // Accumulator element (i, j, r) of lane `lane` in wave (wm, wn) sits at tile

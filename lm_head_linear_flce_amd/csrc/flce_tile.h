@@ -427,8 +427,16 @@ struct TilePipe {
     if (steps <= 0) return;
     la[0].template issue<E>(A, 0, true, tid);
     lb[0].template issue<E>(B, 0, true, tid);
-    la[1].template issue<E>(A, 1, steps > 1, tid);
-    lb[1].template issue<E>(B, 1, steps > 1, tid);
+    // step 1 in the loop's order (A then B, quarter by quarter): the wait
+    // before each of the loop's stores is the same on the first pass as on
+    // every later one, instead of the deeper wait a different order here
+    // would impose on all passes
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      la[1].template issue_part<E>(A, 1, q, steps > 1, tid);
+      lb[1].template issue_part<E>(B, 1, q, steps > 1, tid);
+      __builtin_amdgcn_sched_barrier(0);
+    }
     la[0].commit(sa, tid);
     lb[0].commit(sb, tid);
     __syncthreads();

@@ -328,10 +328,12 @@ __device__ __forceinline__ void mma_slab(const lds_t* sa, const lds_t* sb, const
                                          const FB& fb, f32x16 (&acc)[4][4], Mid&& mid) {
   constexpr int kDsr = 4 * (FA::kReads + FB::kReads);
   Frags f[2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) f[0].a[i] = fa.read(sa, 0, i);
+  // pair 0: A block 0 and all B blocks first, the order the first MFMAs use
+  f[0].a[0] = fa.read(sa, 0, 0);
 #pragma unroll
   for (int j = 0; j < 4; ++j) f[0].b[j] = fb.read(sb, 0, j);
+#pragma unroll
+  for (int i = 1; i < 4; ++i) f[0].a[i] = fa.read(sa, 0, i);
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     if (p + 1 < 4) {
@@ -347,6 +349,8 @@ __device__ __forceinline__ void mma_slab(const lds_t* sa, const lds_t* sb, const
       for (int j = 0; j < 4; ++j) mma<E>(c.a[i], c.b[j], acc[i][j]);
     mid(p);
     if constexpr (E::kBytes == 2) {
+      // all of pair 0's fragment reads go out before its first MFMA
+      if (p == 0) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kDsr, 0);
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);

@@ -192,10 +192,13 @@ struct LoadMN<BF16> {
   __device__ __forceinline__ void issue_part(const Opnd& o, int s, int part, bool live,
                                              int tid) {
     const int c = tid & 31, kr = tid >> 5;
-    const int64_t k0 = (int64_t)s * BF16::kKStep;
-    const rsrc_t r = make_rsrc(o.base + k0 * o.ldb, live ? o.bytes - k0 * o.ldb : 0);
+    // one descriptor for the whole operand (offsets stay below 2^31: the
+    // callers bound K * ldb); a step that is not `live` reads at 2^31 and up,
+    // past the descriptor's end, so it loads zeros
+    const rsrc_t r = make_rsrc(o.base, o.bytes < 0x7FFFFFFF ? o.bytes : 0x7FFFFFFF);
+    const int off = live ? (s * BF16::kKStep + kr) * o.ldb + c * 16 : (int)0x80000000u;
 #pragma unroll
-    for (int i = 2 * part; i < 2 * part + 2; ++i) v[i] = bload128(r, (kr + 8 * i) * o.ldb + c * 16);
+    for (int i = 2 * part; i < 2 * part + 2; ++i) v[i] = bload128(r, off + 8 * i * o.ldb);
   }
   template <class E>
   __device__ __forceinline__ void issue(const Opnd& o, int s, bool live, int tid) {
@@ -248,10 +251,11 @@ struct LoadMN<F32> {
   __device__ __forceinline__ void issue_part(const Opnd& o, int s, int part, bool live,
                                              int tid) {
     const int c = tid & 63, kr = tid >> 6;
-    const int64_t k0 = (int64_t)s * F32::kKStep;
-    const rsrc_t r = make_rsrc(o.base + k0 * o.ldb, live ? o.bytes - k0 * o.ldb : 0);
+    // one descriptor per operand, as for bf16
+    const rsrc_t r = make_rsrc(o.base, o.bytes < 0x7FFFFFFF ? o.bytes : 0x7FFFFFFF);
+    const int off = live ? (s * F32::kKStep + kr) * o.ldb + c * 16 : (int)0x80000000u;
 #pragma unroll
-    for (int i = 2 * part; i < 2 * part + 2; ++i) v[i] = bload128(r, (kr + 4 * i) * o.ldb + c * 16);
+    for (int i = 2 * part; i < 2 * part + 2; ++i) v[i] = bload128(r, off + 4 * i * o.ldb);
   }
   template <class E>
   __device__ __forceinline__ void issue(const Opnd& o, int s, bool live, int tid) {
@@ -321,8 +325,10 @@ constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100,
 
 // The fragment reads of chunk pair p+1 are issued before the 16 MFMAs of pair
 // p.  `mid(p)` then adds a quarter of the next step's LDS stores and of the
-// step after's global loads; the scheduling groups put one or two memory
-// instructions between consecutive MFMAs, fragment reads first.
+// step after's global loads.  The scheduling groups interleave them with the
+// MFMAs: fragment reads over the first eight MFMAs, so that even the
+// transposing loaders' two reads per fragment have half a pair to land, and
+// stores and loads alternating over the last eight.
 template <class E, class FA, class FB, class Mid>
 __device__ __forceinline__ void mma_slab(const lds_t* sa, const lds_t* sb, const FA& fa,
                                          const FB& fb, f32x16 (&acc)[4][4], Mid&& mid) {
@@ -354,15 +360,12 @@ __device__ __forceinline__ void mma_slab(const lds_t* sa, const lds_t* sb, const
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-        if (p + 1 < 4 && q < kDsr) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-        if (kDsr <= 8) {
-          // fragment reads in the first half, stores and loads in the second
-          if (q >= 8 && (q & 1) == 0) __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 1, 0);
-          if (q >= 8 && (q & 1) == 1) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
-        } else {
-          if ((q & 3) == 1) __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 1, 0);
-          if ((q & 3) == 3) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
-        }
+        // the next pair's fragment reads in the first half (two per MFMA when
+        // there are more than 8), the stores and loads in the second
+        constexpr int kPer = (kDsr + 7) / 8;
+        if (p + 1 < 4 && q < 8) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, kPer, 0);
+        if (q >= 8 && (q & 1) == 0) __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 1, 0);
+        if (q >= 8 && (q & 1) == 1) __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
       }
     }
     __builtin_amdgcn_sched_barrier(0);

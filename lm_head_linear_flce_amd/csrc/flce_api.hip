@@ -455,7 +455,7 @@ int chunked_impl(const ChunkPlan& pl, const void* X, const void* W, const int64_
       const int nb = (int)pad8(pl.VT * TTc);
       Timed t("k_chunk_z", stream);
       hipLaunchKernelGGL(k_chunk_z<E>, dim3((unsigned)nb), dim3(kThreads), kLdsBytes, stream,
-                         ca, nb);
+                         ca);
       L.check();
     }
     hipLaunchKernelGGL(k_chunk_lse, dim3((unsigned)(C / 4)), dim3(256), 0, stream, ca);

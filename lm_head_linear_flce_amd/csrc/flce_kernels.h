@@ -476,12 +476,13 @@ __device__ __forceinline__ void g_store(const BwdArgs& a, const f32x16 (&acc)[4]
 // recomputed (A = W rows, B = Xc rows, K = H) and turned into G on the way
 // out; zero outside the vocabulary and on padding rows.
 template <class E>
-__device__ __forceinline__ void g_tile(const BwdArgs& a, int item, lds_t* smem) {
-  if (item >= a.VTb * a.TT) return;
-  int vt, tau;
-  grouped(item, a.VTb, a.TT, vt, tau);
+__device__ __forceinline__ void g_tile(const BwdArgs& a, int b, lds_t* smem) {
   const int n = a.ctr->n;
-  if (tau * kTile >= n) return;
+  const int TTn = (n + kTile - 1) / kTile;
+  const int item = live_item(b, a.VTb * TTn);
+  if (item < 0) return;
+  int vt, tau;
+  grouped(item, a.VTb, TTn, vt, tau);
   const float c = a.ctr->c;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -621,8 +622,9 @@ __device__ __forceinline__ void dw_store(const BwdArgs& a, const f32x16 (&acc)[4
 // tile) of the block: A = Xc, B = G, both stored with K (rows) outer; K runs
 // over the valid rows rounded up to one step (G and Xc are zero past n).
 template <class E>
-__device__ __forceinline__ void dw_tile(const BwdArgs& a, int item, lds_t* smem) {
-  if (item >= a.HT * a.VTb) return;
+__device__ __forceinline__ void dw_tile(const BwdArgs& a, int b, lds_t* smem) {
+  const int item = live_item(b, a.HT * a.VTb);
+  if (item < 0) return;
   int ht, vt;
   grouped(item, a.HT, a.VTb, ht, vt);
   const int n = a.ctr->n;
@@ -682,12 +684,13 @@ __device__ __forceinline__ void dx_add(const BwdArgs& a, const f32x16 (&acc)[4][
 // (K contiguous).  Past the block's end G is zero (last block) or the step
 // count stops at the block (others).
 template <class E>
-__device__ __forceinline__ void dx_tile(const BwdArgs& a, int item, lds_t* smem) {
-  if (item >= a.HT * a.TT) return;
-  int ht, tau;
-  grouped(item, a.HT, a.TT, ht, tau);
+__device__ __forceinline__ void dx_tile(const BwdArgs& a, int b, lds_t* smem) {
   const int n = a.ctr->n;
-  if (tau * kTile >= n) return;
+  const int TTn = (n + kTile - 1) / kTile;
+  const int item = live_item(b, a.HT * TTn);
+  if (item < 0) return;
+  int ht, tau;
+  grouped(item, a.HT, TTn, ht, tau);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int es = E::kBytes;
@@ -721,16 +724,16 @@ void k_bwd(BwdArgs cur, BwdArgs nxt, int nb_dx, int nb_dw, int nb_g) {
   lds_t* smem = (lds_t*)smem_;
   int b = blockIdx.x;
   if (b < nb_dx) {
-    dx_tile<E>(cur, xcd_item(b, nb_dx), smem);
+    dx_tile<E>(cur, b, smem);
     return;
   }
   b -= nb_dx;
   if (b < nb_dw) {
-    dw_tile<E>(cur, xcd_item(b, nb_dw), smem);
+    dw_tile<E>(cur, b, smem);
     return;
   }
   b -= nb_dw;
-  if (b < nb_g) g_tile<E>(nxt, xcd_item(b, nb_g), smem);
+  if (b < nb_g) g_tile<E>(nxt, b, smem);
 }
 
 // ---------------------------------------------------------------------------
@@ -770,11 +773,12 @@ __device__ __forceinline__ int chunk_rows(const ChunkArgs& a) {
 
 // Logits tile (vocabulary tile vt x token tile tau of the chunk).
 template <class E>
-__device__ __forceinline__ void z_tile(const ChunkArgs& a, int item, lds_t* smem) {
-  if (item >= a.VT * a.TTc) return;
+__device__ __forceinline__ void z_tile(const ChunkArgs& a, int b, lds_t* smem) {
+  const int TTn = (chunk_rows(a) + kTile - 1) / kTile;
+  const int item = live_item(b, a.VT * TTn);
+  if (item < 0) return;
   int vt, tau;
-  grouped(item, a.VT, a.TTc, vt, tau);
-  if (tau * kTile >= chunk_rows(a)) return;
+  grouped(item, a.VT, TTn, vt, tau);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int ldb = a.H * E::kBytes;
@@ -847,9 +851,9 @@ __device__ __forceinline__ void z_tile(const ChunkArgs& a, int item, lds_t* smem
 
 template <class E>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void k_chunk_z(ChunkArgs a, int nblocks) {
+void k_chunk_z(ChunkArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem_[];
-  z_tile<E>(a, xcd_item(blockIdx.x, nblocks), (lds_t*)smem_);
+  z_tile<E>(a, blockIdx.x, (lds_t*)smem_);
 }
 
 // One wave per row of the chunk: lse from the row's 2 VT partials (each lane

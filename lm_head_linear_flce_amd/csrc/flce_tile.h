@@ -572,6 +572,18 @@ __device__ __forceinline__ int xcd_item(int b, int nblocks) {
   return (b & 7) * (nblocks >> 3) + (b >> 3);
 }
 
+// Work item of block b (counted from the first block of its kind, which
+// starts on XCD 0) when only `real` of the launched blocks have work, a count
+// the device learns at run time (the launch is sized for the bound): the
+// items go to the first real rounded up to 8 blocks, XCD by XCD, so every XCD
+// gets the same share.  -1: no work.
+__device__ __forceinline__ int live_item(int b, int real) {
+  const int real8 = (real + 7) & ~7;
+  if (b >= real8) return -1;
+  const int item = xcd_item(b, real8);
+  return item < real ? item : -1;
+}
+
 // Grouped tile order over an R x C item grid: items run through groups of
 // kGroup consecutive rows, column by column inside a group.  The 32 workgroups
 // an XCD runs at once then cover a 4 x 8 block of tiles, so each of the 4 row

@@ -77,3 +77,31 @@ def check(w, got, ref, dx_rows=None, dw_rows=None, what=""):
             assert m <= tol["maxabs"] * np.abs(r).max(), f"{what} {name} max abs {m}"
         out[name] = cos
     return out
+
+
+def soft_parts(w, dX, dW, n):
+    """The softmax parts of the gradients, P W and P^T X, rebuilt from dX and
+    dW by removing the one-hot term: dX_i / c + W_{y_i} and dW / c + the sum
+    of X_i over the rows whose target is v (mean: c = 1 / n)."""
+    y, valid = oracle.targets(w.labels, w.shift, w.ignore_index)
+    c = 1.0 / n if w.reduction == "mean" else 1.0
+    X = w.X.reshape(w.N, w.H).astype(np.float64)
+    Wt = w.W.astype(np.float64)
+    sx = dX[valid] / c + Wt[y[valid]]
+    sw = dW / c
+    np.add.at(sw, y[valid], X[valid])
+    return sx, sw
+
+
+def soft_tolerance(w):
+    """(minimum cosine, norm-ratio tolerance) of the softmax parts.  With fp32
+    inputs G is fp32 and the soft parts match to rounding.  With bf16 inputs
+    the MFMA consumes G in bf16, and at the target column G holds c (p - 1):
+    its rounding error (up to 2^-9 c) is of the order of a tenth of a row's
+    whole softmax part when p is diffuse (p_max ~ 1e-3 here), so the rebuilt
+    soft part carries that much noise: cosine ~0.996 at these shapes, the
+    norm within a few parts per thousand.  A missing or misplaced softmax term
+    gives a cosine near 0, a wrong scale a norm ratio far from 1."""
+    if w.dtype == "f32":
+        return 0.99999, 1e-4
+    return 0.99, 0.02

@@ -14,7 +14,7 @@ import torch
 import lm_head_linear_flce_amd as F
 import oracle
 import synth
-from gpu_util import DEV, check, run, run_chunked, to_device
+from gpu_util import DEV, check, run, run_chunked, soft_parts, soft_tolerance, to_device
 from test_gpu_parity import GOLDEN, SMALL, _ids
 
 pytestmark = pytest.mark.gpu
@@ -31,6 +31,28 @@ def test_chunked_small_parity(case):
     check(w, got, ref, what="chunked " + name)
     _, valid = oracle.targets(w.labels, w.shift, w.ignore_index)
     assert np.all(got["dX"][~valid] == 0.0)
+
+
+@pytest.mark.parametrize("case", SMALL[:5], ids=[_ids(p) for p in SMALL[:5]])
+def test_chunked_softmax_part_of_the_gradients(case):
+    """As for the recompute path: the softmax parts P W and P^T X, rebuilt from
+    the FP32 gradient outputs, in direction and size."""
+    name, ov = case
+    w = synth.workload(name, **ov)
+    ref = oracle.flce(w.X, w.W, w.labels, ignore_index=w.ignore_index,
+                      reduction=w.reduction, shift=w.shift, mode="rows", chunk=1024)
+    got = run_chunked(w, grad_dtype=torch.float32)
+    n = ref["n_valid"]
+    gx, gw = soft_parts(w, got["dX"], got["dW"], n)
+    rx, rw = soft_parts(w, ref["dX"], ref["dW"], n)
+    cx, cw = oracle.cosine(gx, rx), oracle.cosine(gw, rw)
+    print(f"[chunked soft part] {name}: cos P.W {cx:.7f}  cos P^T.X {cw:.7f}", flush=True)
+    rnx = np.linalg.norm(gx) / np.linalg.norm(rx)
+    rnw = np.linalg.norm(gw) / np.linalg.norm(rw)
+    # fp32 G: the soft parts to rounding; bf16 G: see soft_tolerance
+    cmin, rtol = soft_tolerance(w)
+    assert cx >= cmin and cw >= cmin, (cx, cw)
+    assert abs(rnx - 1) <= rtol and abs(rnw - 1) <= rtol, (rnx, rnw)
 
 
 def test_chunked_several_chunks():

@@ -14,7 +14,7 @@ import torch
 import lm_head_linear_flce_amd as F
 import oracle
 import synth
-from gpu_util import DEV, check, run, to_device
+from gpu_util import DEV, check, run, soft_parts, soft_tolerance, to_device
 
 pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -62,6 +62,30 @@ def test_fp32_gradient_outputs(case):
     got = run(w, grad_dtype=torch.float32)
     cos = check(w, got, ref, what=name)
     assert cos["dX"] > 0.99999 and cos["dW"] > 0.99999
+
+
+@pytest.mark.parametrize("case", SMALL[:5], ids=[_ids(p) for p in SMALL[:5]])
+def test_softmax_part_of_the_gradients(case):
+    """The contract's tolerances are dominated by the one-hot term (the
+    softmax is diffuse at these shapes), so the softmax part alone is compared
+    too, with the FP32 gradient outputs: its direction (cosine) and its size
+    (norm ratio), for both gradients."""
+    name, ov = case
+    w = synth.workload(name, **ov)
+    ref = oracle.flce(w.X, w.W, w.labels, ignore_index=w.ignore_index,
+                      reduction=w.reduction, shift=w.shift, mode="rows", chunk=1024)
+    got = run(w, grad_dtype=torch.float32)
+    n = ref["n_valid"]
+    gx, gw = soft_parts(w, got["dX"], got["dW"], n)
+    rx, rw = soft_parts(w, ref["dX"], ref["dW"], n)
+    cx, cw = oracle.cosine(gx, rx), oracle.cosine(gw, rw)
+    print(f"[soft part] {name}: cos P.W {cx:.7f}  cos P^T.X {cw:.7f}", flush=True)
+    rnx = np.linalg.norm(gx) / np.linalg.norm(rx)
+    rnw = np.linalg.norm(gw) / np.linalg.norm(rw)
+    # fp32 G: the soft parts to rounding; bf16 G: see soft_tolerance
+    cmin, rtol = soft_tolerance(w)
+    assert cx >= cmin and cw >= cmin, (cx, cw)
+    assert abs(rnx - 1) <= rtol and abs(rnw - 1) <= rtol, (rnx, rnw)
 
 
 def test_grad_scale_and_autograd():

@@ -15,7 +15,7 @@ namespace {
 
 constexpr int64_t kAlign = 256;
 #ifndef FLCE_SLAB_MIB
-#define FLCE_SLAB_MIB 256
+#define FLCE_SLAB_MIB 512
 #endif
 // backward: both softmax-gradient slabs together hold at most this many bytes
 // (unless a single 256-wide vocabulary tile per row already needs more)
@@ -58,8 +58,10 @@ int make_plan(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, Plan* p) {
   q.fwd_items = std::max<int64_t>(2048, q.TT);
   // backward: the vocabulary block is as wide as the slab budget allows for
   // this many rows, whatever V is (and narrow enough for 32-bit offsets)
-  int64_t vb = std::min<int64_t>(kSlabBudget / (2 * q.rows_pad * q.es),
-                                 kMaxI32 / (q.rows_pad * q.es));
+  // (the dX tiles address a whole block of W rows, and the dW tiles the
+  // whole slab, from one descriptor each: both below 2^31 bytes)
+  int64_t vb = std::min<int64_t>({kSlabBudget / (2 * q.rows_pad * q.es),
+                                  kMaxI32 / (q.rows_pad * q.es), kMaxI32 / (H * q.es)});
   vb = std::max<int64_t>(kTile, vb / kTile * kTile);
   vb = std::min<int64_t>(vb, round_up(V, kTile));
   q.Vb = vb;
@@ -326,11 +328,15 @@ void zero_fill(void* p, int64_t bytes, hipStream_t s) {
 // bytes (unless one 256-row tile of it already needs more)
 constexpr int64_t kChunkBudget = (int64_t)FLCE_CHUNK_MIB << 20;
 // vocabulary block of the dX / dW launches inside a chunk
-constexpr int64_t kChunkVocabBlock = 16384;
+#ifndef FLCE_CHUNK_VB
+#define FLCE_CHUNK_VB 32768
+#endif
+constexpr int64_t kChunkVocabBlock = FLCE_CHUNK_VB;
 
 struct ChunkPlan {
   int64_t N, rows_pad, H, V, Vp, es, TT, VT;
   int64_t C, nchunks;       // chunk rows (multiple of 256), chunks covering rows_pad
+  int64_t VB;               // vocabulary block of the dX / dW launches
   int64_t o_ctr, o_idx, o_tgt, o_rowpos, o_xc, o_zt, o_lse_c, o_lse2, o_rloss, o_bsum, o_cctr;
   int64_t o_rs;
   int64_t o_part, o_slab, o_dx32;
@@ -362,6 +368,10 @@ int make_chunk_plan(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, int64
   q.C = std::min(c, q.rows_pad);
   if (q.C * q.Vp * q.es > kMaxI32) return FLCE_ERR_SHAPE;
   q.nchunks = cdiv(q.rows_pad, q.C);
+  // vocabulary block of the dX / dW launches: its W rows stay below 2^31
+  // bytes (one descriptor per dX tile operand)
+  q.VB = std::max<int64_t>(kTile, std::min<int64_t>(kChunkVocabBlock, kMaxI32 / (H * q.es)) /
+                                      kTile * kTile);
   int64_t off = 0;
   auto take = [&](int64_t bytes) {
     const int64_t o = off;
@@ -482,9 +492,9 @@ int chunked_impl(const ChunkPlan& pl, const void* X, const void* W, const int64_
     b.HT = HT;
     b.dw_f32 = grad_f32;
     b.dw_acc = ch > 0 || dw_acc;
-    for (int64_t v0 = 0; v0 < pl.V && L.err == hipSuccess; v0 += kChunkVocabBlock) {
+    for (int64_t v0 = 0; v0 < pl.V && L.err == hipSuccess; v0 += pl.VB) {
       b.v0 = (int)v0;
-      b.vb = (int)std::min<int64_t>(kChunkVocabBlock, pl.V - v0);
+      b.vb = (int)std::min<int64_t>(pl.VB, pl.V - v0);
       b.VTb = (int)cdiv(b.vb, kTile);
       b.G = slab + v0 * E::kBytes;
       const int nb_dx = (int)pad8((int64_t)HT * TTc), nb_dw = (int)pad8((int64_t)HT * b.VTb);

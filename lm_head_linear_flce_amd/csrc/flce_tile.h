@@ -192,13 +192,16 @@ struct LoadMN<BF16> {
   __device__ __forceinline__ void issue_part(const Opnd& o, int s, int part, bool live,
                                              int tid) {
     const int c = tid & 31, kr = tid >> 5;
-    // one descriptor for the whole operand (offsets stay below 2^31: the
-    // callers bound K * ldb); a step that is not `live` reads at 2^31 and up,
-    // past the descriptor's end, so it loads zeros
+    // one descriptor for the whole operand: the plans keep K * ldb below
+    // 2^31, so live offsets do too; a step that is not `live` reads at 2^31
+    // and up (below 2^32: the rows it adds are within the tile), past the
+    // descriptor's end, so it loads zeros
     const rsrc_t r = make_rsrc(o.base, o.bytes < 0x7FFFFFFF ? o.bytes : 0x7FFFFFFF);
-    const int off = live ? (s * BF16::kKStep + kr) * o.ldb + c * 16 : (int)0x80000000u;
+    const uint32_t off = live ? (uint32_t)(s * BF16::kKStep + kr) * (uint32_t)o.ldb + c * 16
+                              : 0x80000000u;
 #pragma unroll
-    for (int i = 2 * part; i < 2 * part + 2; ++i) v[i] = bload128(r, off + 8 * i * o.ldb);
+    for (int i = 2 * part; i < 2 * part + 2; ++i)
+      v[i] = bload128(r, (int)(off + (uint32_t)(8 * i) * (uint32_t)o.ldb));
   }
   template <class E>
   __device__ __forceinline__ void issue(const Opnd& o, int s, bool live, int tid) {
@@ -253,9 +256,11 @@ struct LoadMN<F32> {
     const int c = tid & 63, kr = tid >> 6;
     // one descriptor per operand, as for bf16
     const rsrc_t r = make_rsrc(o.base, o.bytes < 0x7FFFFFFF ? o.bytes : 0x7FFFFFFF);
-    const int off = live ? (s * F32::kKStep + kr) * o.ldb + c * 16 : (int)0x80000000u;
+    const uint32_t off = live ? (uint32_t)(s * F32::kKStep + kr) * (uint32_t)o.ldb + c * 16
+                              : 0x80000000u;
 #pragma unroll
-    for (int i = 2 * part; i < 2 * part + 2; ++i) v[i] = bload128(r, off + 4 * i * o.ldb);
+    for (int i = 2 * part; i < 2 * part + 2; ++i)
+      v[i] = bload128(r, (int)(off + (uint32_t)(4 * i) * (uint32_t)o.ldb));
   }
   template <class E>
   __device__ __forceinline__ void issue(const Opnd& o, int s, bool live, int tid) {

@@ -193,7 +193,13 @@ def test_zero_weight_gives_log_vocab():
 
 
 def test_peak_memory_never_holds_logits():
-    w = synth.workload("long_context", T=4096, H=128, V=262144, seed=151)
+    # the device memory a call takes beyond its inputs is the caller's
+    # workspace plus the outputs; the workspace is linear in N and does not
+    # grow with V (the gradient slabs are a fixed budget); at this shape the
+    # logits would be 4.3 GB
+    w = synth.workload("long_context", T=8192, H=128, V=262144, seed=151)
+    ws_v = [F.flce_workspace_size(w.B, w.T, w.H, v, F.FLCE_DTYPE_BF16) for v in (w.V, 4 * w.V)]
+    assert ws_v[0] == ws_v[1], ws_v
     X, W, lab = to_device(w)
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()

@@ -214,6 +214,39 @@ def test_peak_memory_never_holds_logits():
     assert peak < w.N * w.V * 2 / 4
 
 
+@pytest.mark.parametrize("dtype,V", [("bf16", 16640), ("f32", 8448)])
+def test_widest_hidden_size(dtype, V):
+    """H = 65536, the widest the ABI takes.  A block of W rows then reaches the
+    2^31 bytes one buffer descriptor addresses, so both modes narrow their
+    vocabulary blocks (two blocks here, the second one ragged); loss, lse and
+    dX in full and sampled dW rows against the oracle."""
+    w = synth.workload("tiny_f32", B=1, T=8, H=65536, V=V, dtype=dtype, seed=171, mask_arg=2)
+    print(f"[widest] N={w.N} H={w.H} V={w.V} {dtype}", flush=True)
+    ref = oracle.flce(w.X, w.W, w.labels, ignore_index=w.ignore_index,
+                      reduction=w.reduction, shift=w.shift, mode="rows", chunk=8)
+    y, valid = oracle.targets(w.labels, w.shift, w.ignore_index)
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([y[valid], rng.integers(0, w.V, 48), [w.V - 1]]))
+    X, W, lab = to_device(w)
+    for mode in ("recompute", "chunked"):
+        if mode == "recompute":
+            loss, lse, n_valid, status = F.forward(X, W, lab, w.ignore_index, w.shift,
+                                                   w.reduction)
+            dX, dW, bstatus = F.backward(X, W, lab, lse, ignore_index=w.ignore_index,
+                                         shift=w.shift, reduction=w.reduction)
+        else:
+            loss, lse, n_valid, dX, dW, status = F.chunked(
+                X, W, lab, ignore_index=w.ignore_index, shift=w.shift, reduction=w.reduction)
+            bstatus = status
+        torch.cuda.synchronize()
+        got = dict(loss=float(loss), lse=lse.double().cpu().numpy(), n_valid=int(n_valid),
+                   status=int(status), bstatus=int(bstatus),
+                   dX=dX.reshape(w.N, w.H).double().cpu().numpy(),
+                   dW=dW[torch.from_numpy(rows).to(DEV)].double().cpu().numpy())
+        del dX, dW
+        check(w, got, dict(ref, dW=ref["dW"][rows]), what=f"widest {mode} {dtype}")
+
+
 # ---------------------------------------------------------------------------
 # full sizes
 # ---------------------------------------------------------------------------

@@ -470,9 +470,12 @@ int chunked_impl(const ChunkPlan& pl, const void* X, const void* W, const int64_
     }
     hipLaunchKernelGGL(k_chunk_lse, dim3((unsigned)(C / 4)), dim3(256), 0, stream, ca);
     L.check();
+    // rows strided over at most 1024 workgroup rows: the chunk past the valid
+    // rows (the host does not know n) exits at once
     constexpr int per = 16 / E::kBytes;
-    hipLaunchKernelGGL(k_chunk_scale<E>, dim3((unsigned)cdiv(pl.Vp, 256 * per), (unsigned)C),
-                       dim3(256), 0, stream, ca);
+    hipLaunchKernelGGL(k_chunk_scale<E>,
+                       dim3((unsigned)cdiv(pl.Vp, 256 * per), (unsigned)std::min(C, 1024)),
+                       dim3(256), 0, stream, ca, 0, (int)pl.Vp);
     L.check();
     // dX and dW tiles of the chunk, one vocabulary block per launch
     BwdArgs b;

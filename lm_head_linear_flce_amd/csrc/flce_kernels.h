@@ -911,28 +911,18 @@ __global__ __launch_bounds__(256) void k_block_sums(const float* __restrict__ rl
   if (threadIdx.x == 0) bsum[blockIdx.x] = red[0];
 }
 
-// G = c e 2^(M - lse2) - c [v = y] in place; 16 bytes per thread, grid
-// (Vp / (256 * per), rows).  Rows from the chunk's row count up to the next
-// multiple of 64 (the last K step of the dW tiles) are zeroed; rows past that
-// are left alone.
+// G = c e 2^(M - lse2) - c [v = y] for one 16-byte piece u of the slab (row
+// kl of the chunk, columns v .. v + 16 / es - 1); rows from the chunk's row
+// count up to the next multiple of 64 (the last K step of the dW tiles) become
+// zero.
 template <class E>
-__global__ __launch_bounds__(256) void k_chunk_scale(ChunkArgs a) {
-  constexpr int per = 16 / E::kBytes;
-  const int kl = blockIdx.y;
-  const int nc = chunk_rows(a);
-  if (kl >= ((nc + 63) & ~63)) return;
-  const int v = (blockIdx.x * 256 + threadIdx.x) * per;
-  if (v >= a.Vp) return;
-  i32x4* p = (i32x4*)(a.E + ((int64_t)kl * a.Vp + v) * E::kBytes);
-  if (kl >= nc) {
-    *p = i32x4{0, 0, 0, 0};
-    return;
-  }
+__device__ __forceinline__ i32x4 scale_piece(const ChunkArgs& a, int kl, int v, int nc,
+                                             i32x4 u) {
+  if (kl >= nc) return i32x4{0, 0, 0, 0};
   const int k = a.row0 + kl;
   const float c = a.rs ? a.ctr->c * a.rs[k] : a.ctr->c;
   const float f = c * exp2f(a.part[(int64_t)kl * (2 * a.VT) + (v >> 7)].x - a.lse2[k]);
   const int y = a.tgt[k] - v;
-  const i32x4 u = *p;
   if constexpr (E::kBytes == 2) {
     float g[8];
 #pragma unroll
@@ -943,8 +933,8 @@ __global__ __launch_bounds__(256) void k_chunk_scale(ChunkArgs a) {
 #pragma unroll
     for (int q = 0; q < 8; ++q)
       if (y == q) g[q] -= c;
-    *p = i32x4{pack_bf16(g[0], g[1]), pack_bf16(g[2], g[3]), pack_bf16(g[4], g[5]),
-               pack_bf16(g[6], g[7])};
+    return i32x4{pack_bf16(g[0], g[1]), pack_bf16(g[2], g[3]), pack_bf16(g[4], g[5]),
+                 pack_bf16(g[6], g[7])};
   } else {
     f32x4 g = __builtin_bit_cast(f32x4, u);
 #pragma unroll
@@ -952,7 +942,28 @@ __global__ __launch_bounds__(256) void k_chunk_scale(ChunkArgs a) {
       g[q] *= f;
       if (y == q) g[q] -= c;
     }
-    *p = __builtin_bit_cast(i32x4, g);
+    return __builtin_bit_cast(i32x4, g);
+  }
+}
+
+__device__ __forceinline__ i32x4* slab_piece(const ChunkArgs& a, int kl, int v, int es) {
+  return (i32x4*)(a.E + ((int64_t)kl * a.Vp + v) * es);
+}
+
+// Slab columns [v_begin, v_end) (multiples of 256) in place, rows below the
+// chunk's row count rounded up to 64; 16 bytes per thread, grid
+// ((v_end - v_begin) / (256 * per), any row count), rows strided by gridDim.y
+// (so a chunk past the valid rows costs one early exit per workgroup).
+template <class E>
+__global__ __launch_bounds__(256) void k_chunk_scale(ChunkArgs a, int v_begin, int v_end) {
+  constexpr int per = 16 / E::kBytes;
+  const int nc = chunk_rows(a);
+  const int rows = (nc + 63) & ~63;
+  const int v = v_begin + (blockIdx.x * 256 + threadIdx.x) * per;
+  if (v >= v_end) return;
+  for (int kl = blockIdx.y; kl < rows; kl += gridDim.y) {
+    i32x4* p = slab_piece(a, kl, v, E::kBytes);
+    *p = scale_piece<E>(a, kl, v, nc, *p);
   }
 }
 

@@ -594,7 +594,10 @@ __device__ __forceinline__ int live_item(int b, int real) {
 // an XCD runs at once then cover a 4 x 8 block of tiles, so each of the 4 row
 // panels and each of the 8 column panels is fetched once into that XCD's L2
 // and reused by the other tiles of the block.
-constexpr int kGroup = 4;
+#ifndef FLCE_GROUP
+#define FLCE_GROUP 4
+#endif
+constexpr int kGroup = FLCE_GROUP;
 __device__ __forceinline__ void grouped(int item, int R, int C, int& r, int& c) {
   const int group = item / (kGroup * C);
   const int r0 = group * kGroup;

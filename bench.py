@@ -54,6 +54,30 @@ CHUNKED_PROFILE_COMMANDS = (
     "-- python $R/bench.py --steps 3 --warmup 1 --chunked-only",
     "python $R/bench.py --summarize-chunked $R/gpurun_out",
 )
+# matrix-core busy cycles, bf16 MFMA work and the shader clock per kernel
+# (profiles/flce_qwen2_7b_head_mfma.md); each counter run holds 3 SQ and 1 GRBM
+# counters, with the kernel trace for the durations
+MFMA_COUNTERS = "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_CYCLES GRBM_GUI_ACTIVE"
+MFMA_PROFILE_COMMANDS = (
+    f"rocprofv3 --pmc {MFMA_COUNTERS} --kernel-trace --output-format csv "
+    "-d $R/gpurun_out/prof_mfma -o flce -- python $R/bench.py --steps 1 --warmup 0 "
+    "--no-cpu-baseline --no-chunked",
+    f"rocprofv3 --pmc {MFMA_COUNTERS} --kernel-trace --output-format csv "
+    "-d $R/gpurun_out/prof_mfma_chunk -o flce -- python $R/bench.py --steps 1 --warmup 0 "
+    "--chunked-only",
+    *(f"rocprofv3 --pmc {c} --kernel-trace --output-format csv -d $R/gpurun_out/stall{i + 1} "
+      "-o flce -- python $R/bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-chunked"
+      for i, c in enumerate((
+          "SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_WAIT_INST_LDS SQ_INSTS_VMEM_RD "
+          "SQ_LDS_DATA_FIFO_FULL SQ_LDS_CMD_FIFO_FULL GRBM_GUI_ACTIVE",
+          "SQ_WAVE_CYCLES SQ_INSTS_LDS SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_VMEM SQ_LDS_BANK_CONFLICT "
+          "SQ_ACTIVE_INST_ANY SQ_ACTIVE_INST_VALU GRBM_GUI_ACTIVE",
+          "SQ_WAVE_CYCLES SQ_INSTS_MFMA SQ_INSTS_VALU SQ_INSTS_SALU SQ_ACTIVE_INST_SCA "
+          "SQ_VMEM_TA_ADDR_FIFO_FULL SQ_VMEM_TA_CMD_FIFO_FULL GRBM_GUI_ACTIVE"))),
+    "python $R/bench.py --summarize-mfma $R/gpurun_out",
+)
+SIMDS = 256 * 4           # MI355X: 256 compute units x 4 SIMDs
+XCDS = 8                  # GRBM_GUI_ACTIVE comes summed over the 8 XCDs
 TRAFFIC = os.path.join(PROFILES, "traffic_qwen2_7b_head.json")
 METRIC = "fused linear-CE fwd+bwd tokens/sec and % bf16 MFMA peak; peak extra HBM bytes"
 
@@ -74,6 +98,9 @@ def parse():
                          "CHUNKED_PROFILE_COMMANDS)")
     ap.add_argument("--summarize-chunked", metavar="DIR",
                     help="summarise DIR/prof_chunk of CHUNKED_PROFILE_COMMANDS into profiles/")
+    ap.add_argument("--summarize-mfma", metavar="DIR",
+                    help="summarise DIR/prof_mfma and DIR/prof_mfma_chunk of "
+                         "MFMA_PROFILE_COMMANDS into profiles/")
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--summarize", metavar="DIR",
                     help="summarise the rocprofv3 output of PROFILE_COMMANDS under DIR "
@@ -256,6 +283,114 @@ def summarize(prof_dir, command, trace="prof_trace", out="flce_qwen2_7b_head_ker
     print(md)
 
 
+def summarize_mfma(prof_dir):
+    """Per kernel and dispatch: matrix-core busy fraction (SQ_VALU_MFMA_BUSY_CYCLES
+    over GRBM_GUI_ACTIVE x SIMDs), bf16 MFMA flops counted by the hardware
+    (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512), the shader clock (GRBM_GUI_ACTIVE over
+    the dispatch's duration) and the achieved rate -> profiles/."""
+    import csv
+    import glob
+    out = ["# MFMA utilisation and shader clock: Qwen2-7B-like LM head, N=8192 H=3584 "
+           "V=152064 bf16", "", f"kernel source hash: `{source_hash()}`", "",
+           "Commands (run from /tmp with TMPDIR=/tmp; $R = repository root):", "",
+           "```", *MFMA_PROFILE_COMMANDS, "```", "",
+           "Per dispatch: GRBM_GUI_ACTIVE is reported summed over the 8 XCDs, so one "
+           "XCD's busy cycles are a = GRBM_GUI_ACTIVE / 8 (the memory-bound bf16 copy "
+           "kernel's row reads 2.40 GHz, the top clock); MFMA busy = "
+           "SQ_VALU_MFMA_BUSY_CYCLES / (a x 1024 SIMDs); MFMA flop = "
+           "SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 (the padded tiles' work: rows rounded up "
+           "to 256); clock = a / duration; rate = MFMA flop / duration; the peak at the "
+           "measured clock is 2.5 PFLOP/s x clock / 2.4 GHz. Dispatches under 50 us are "
+           "left out.", ""]
+    for sub, title in (("prof_mfma", "recompute path (flce_forward + flce_backward)"),
+                       ("prof_mfma_chunk", "chunked mode (flce_chunked)")):
+        cc = glob.glob(os.path.join(prof_dir, sub, "**", "*counter_collection.csv"),
+                       recursive=True)
+        kt = glob.glob(os.path.join(prof_dir, sub, "**", "*kernel_trace.csv"), recursive=True)
+        if not cc or not kt:
+            continue
+        dur = {}
+        for path in kt:
+            for r in csv.DictReader(open(path)):
+                dur[r["Dispatch_Id"]] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        per = {}
+        for path in cc:
+            for r in csv.DictReader(open(path)):
+                d = per.setdefault(r["Dispatch_Id"], {"name": _short(r["Kernel_Name"])})
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        agg = {}
+        for did, d in per.items():
+            ns = dur.get(did)
+            if not ns or ns < 50_000 or "GRBM_GUI_ACTIVE" not in d:
+                continue
+            a = agg.setdefault(d["name"], [])
+            a.append((ns, d["GRBM_GUI_ACTIVE"] / XCDS, d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0),
+                      d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) * 512))
+        out += [f"## {title}", "",
+                "| kernel | dispatches | avg us | MFMA busy | clock GHz | MFMA TFLOP/launch "
+                "| TFLOP/s | % of 2.5 PF | % of peak at measured clock |",
+                "|---|---|---|---|---|---|---|---|---|"]
+        for name, a in sorted(agg.items(), key=lambda kv: -sum(x[0] for x in kv[1])):
+            ns = sum(x[0] for x in a) / len(a)
+            gui = sum(x[1] for x in a) / len(a)
+            busy = sum(x[2] for x in a) / len(a) / (gui * SIMDS)
+            fl = sum(x[3] for x in a) / len(a)
+            clk = gui / ns
+            rate = fl / (ns * 1e-9)
+            out.append(f"| {name} | {len(a)} | {ns / 1e3:.1f} | {100 * busy:.1f} % | {clk:.2f} | "
+                       f"{fl / 1e12:.3f} | {rate / 1e12:.0f} | {100 * rate / BF16_PEAK:.1f} | "
+                       f"{100 * rate / (BF16_PEAK * clk / 2.4):.1f} |")
+        out.append("")
+    # where the waves' time goes (the stall runs): SQ_WAVE_CYCLES, SQ_WAIT_* and
+    # SQ_ACTIVE_INST_* all count wave-cycles in the same units, so their ratios are
+    # fractions of the waves' lifetime
+    stall = {}
+    for i in (1, 2, 3):
+        for path in glob.glob(os.path.join(prof_dir, f"stall{i}", "**", "*counter_collection.csv"),
+                              recursive=True):
+            per = {}
+            for r in csv.DictReader(open(path)):
+                name = _short(r["Kernel_Name"])
+                if not any(k in name for k in KERNELS):
+                    continue
+                d = per.setdefault(r["Dispatch_Id"], {"name": name})
+                d["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+                d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            for d in per.values():
+                if d["ns"] < 50_000 or not d.get("SQ_WAVE_CYCLES"):
+                    continue
+                acc = stall.setdefault(d["name"], {})
+                for c, v in d.items():
+                    if c.startswith("SQ_"):
+                        acc.setdefault(c, []).append(v / d["SQ_WAVE_CYCLES"] if c != "SQ_WAVE_CYCLES"
+                                                     else v)
+    if stall:
+        rows = (("SQ_WAIT_ANY", "waiting on s_waitcnt / barrier"),
+                ("SQ_WAIT_INST_ANY", "waiting to issue (includes the MFMA pipe's back-pressure)"),
+                ("SQ_WAIT_INST_LDS", "waiting to issue an LDS instruction"),
+                ("SQ_ACTIVE_INST_LDS", "LDS instructions active"),
+                ("SQ_ACTIVE_INST_VALU", "VALU instructions active (the counter's issue-side count)"),
+                ("SQ_ACTIVE_INST_VMEM", "global load / store instructions active"),
+                ("SQ_ACTIVE_INST_SCA", "scalar instructions active"))
+        names = sorted(stall)
+        out += ["## Where the waves' time goes (recompute path; fractions of SQ_WAVE_CYCLES)", "",
+                "| counter | meaning | " + " | ".join(names) + " |",
+                "|---|---|" + "---|" * len(names)]
+        for c, what in rows:
+            vals = [stall[n].get(c) for n in names]
+            out.append(f"| {c} | {what} | " + " | ".join(
+                f"{100 * sum(v) / len(v):.1f} %" if v else "-" for v in vals) + " |")
+        for c in ("SQ_LDS_BANK_CONFLICT",):
+            vals = [stall[n].get(c) for n in names]
+            out.append(f"| {c} | LDS bank-conflict cycles (relative) | " + " | ".join(
+                f"{sum(v) / len(v):.4f}" if v else "-" for v in vals) + " |")
+        out.append("")
+    md = os.path.join(PROFILES, "flce_qwen2_7b_head_mfma.md")
+    with open(md, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print(md)
+
+
 def chunked_mode(F, X, W, lab, w, dcode, dev, args, peak):
     """The same workload through flce_chunked (one call: loss, lse, dX, dW over
     row chunks; 6 n H V executed flop instead of 8), timed like the main step;
@@ -296,6 +431,9 @@ def main():
     args = parse()
     if args.summarize:
         summarize(args.summarize, PROFILE_COMMANDS)
+        return
+    if args.summarize_mfma:
+        summarize_mfma(args.summarize_mfma)
         return
     if args.summarize_chunked:
         summarize(args.summarize_chunked, CHUNKED_PROFILE_COMMANDS, trace="prof_chunk",

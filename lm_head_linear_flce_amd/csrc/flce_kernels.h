@@ -771,34 +771,17 @@ __device__ __forceinline__ int chunk_rows(const ChunkArgs& a) {
   return r < 0 ? 0 : (r < a.C ? r : a.C);
 }
 
-// Logits tile (vocabulary tile vt x token tile tau of the chunk).
-template <class E>
-__device__ __forceinline__ void z_tile(const ChunkArgs& a, int b, lds_t* smem) {
-  const int TTn = (chunk_rows(a) + kTile - 1) / kTile;
-  const int item = live_item(b, a.VT * TTn);
-  if (item < 0) return;
-  int vt, tau;
-  grouped(item, a.VT, TTn, vt, tau);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int ldb = a.H * E::kBytes;
-  const int steps = (ldb + kRowBytes - 1) / kRowBytes;
-  Opnd A, B;
-  A.base = a.W + (int64_t)vt * kTile * ldb;
-  A.bytes = (int64_t)(a.V - vt * kTile) * ldb;
-  A.ldb = ldb;
-  A.kbytes = ldb;
-  B.base = a.Xc + (int64_t)tau * kTile * ldb;
-  B.bytes = (int64_t)(a.C - tau * kTile) * ldb;
-  B.ldb = ldb;
-  B.kbytes = ldb;
-  f32x16 acc[4][4];
-  zero_acc(acc);
-  gemm_tile<E, LoadDirect, LoadDirect>(A, B, steps, smem, wm, wn, acc);
-
-  // vocabulary rows 32i + 8g + q < vlim lie inside V; lanes l and l ^ 32 hold
-  // the two halves of the 64 rows a wave keeps per token column
-  const int vlim = a.V - vt * kTile - wm * 128 - 4 * (lane >> 5);
+// Epilogue of a logits tile of the chunked mode: per (token, 128-row half of
+// the tile) the max M of z log2e and s = sum 2^(z log2e - M), and
+// e = 2^(z log2e - M) into the slab.  kMasked: vocabulary rows
+// 32i + 8g + q >= vlim (the lane's offset already in vlim) lie past V and
+// count as absent; full tiles skip the test.
+template <class E, bool kMasked>
+__device__ __forceinline__ void z_store(const ChunkArgs& a, const f32x16 (&acc)[4][4], int vt,
+                                        int tau, int wm, int wn, int lane, int vlim,
+                                        lds_t* smem) {
+  // lanes l and l ^ 32 hold the two halves of the 64 rows a wave keeps per
+  // token column
   float m2[4], sum[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -807,18 +790,19 @@ __device__ __forceinline__ void z_tile(const ChunkArgs& a, int b, lds_t* smem) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r)
-        if (32 * i + 8 * (r >> 2) + (r & 3) < vlim) mx = fmaxf(mx, acc[i][j][r]);
+        if (!kMasked || 32 * i + 8 * (r >> 2) + (r & 3) < vlim) mx = fmaxf(mx, acc[i][j][r]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     m2[j] = mx == -INFINITY ? 0.f : mx * kLog2e;
     sum[j] = 0.f;
   }
   auto val = [&](int i, int j, int r) {
-    const bool ok = 32 * i + 8 * (r >> 2) + (r & 3) < vlim;
-    const float e = ok ? __builtin_amdgcn_exp2f(fmaf(acc[i][j][r], kLog2e, -m2[j])) : 0.f;
-    sum[j] += e;
-    return e;
+    const float e = __builtin_amdgcn_exp2f(fmaf(acc[i][j][r], kLog2e, -m2[j]));
+    const float v = (!kMasked || 32 * i + 8 * (r >> 2) + (r & 3) < vlim) ? e : 0.f;
+    sum[j] += v;
+    return v;
   };
   const rsrc_t er = make_rsrc(a.E, (int64_t)a.C * a.Vp * E::kBytes);
+  const int wave = threadIdx.x >> 6;
   if constexpr (E::kBytes == 2) {
     const int tok0 = tau * kTile + wn * 128, voc0 = vt * kTile + wm * 128;
     store_quarter_bf16(smem + wave * 32768, lane, val, [&](int o, int x0, i32x4 v) {
@@ -847,6 +831,36 @@ __device__ __forceinline__ void z_tile(const ChunkArgs& a, int b, lds_t* smem) {
       a.part[(int64_t)(tau * kTile + acc_col(wn, j, lane)) * (2 * a.VT) + 2 * vt + wm] =
           make_float2(m2[j], s2);
   }
+}
+
+// Logits tile (vocabulary tile vt x token tile tau of the chunk).
+template <class E>
+__device__ __forceinline__ void z_tile(const ChunkArgs& a, int b, lds_t* smem) {
+  const int TTn = (chunk_rows(a) + kTile - 1) / kTile;
+  const int item = live_item(b, a.VT * TTn);
+  if (item < 0) return;
+  int vt, tau;
+  grouped(item, a.VT, TTn, vt, tau);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int ldb = a.H * E::kBytes;
+  const int steps = (ldb + kRowBytes - 1) / kRowBytes;
+  Opnd A, B;
+  A.base = a.W + (int64_t)vt * kTile * ldb;
+  A.bytes = (int64_t)(a.V - vt * kTile) * ldb;
+  A.ldb = ldb;
+  A.kbytes = ldb;
+  B.base = a.Xc + (int64_t)tau * kTile * ldb;
+  B.bytes = (int64_t)(a.C - tau * kTile) * ldb;
+  B.ldb = ldb;
+  B.kbytes = ldb;
+  f32x16 acc[4][4];
+  zero_acc(acc);
+  gemm_tile<E, LoadDirect, LoadDirect>(A, B, steps, smem, wm, wn, acc);
+
+  const int vlim = a.V - vt * kTile;
+  if (vlim >= kTile) z_store<E, false>(a, acc, vt, tau, wm, wn, lane, 0, smem);
+  else z_store<E, true>(a, acc, vt, tau, wm, wn, lane, vlim - wm * 128 - 4 * (lane >> 5), smem);
 }
 
 template <class E>

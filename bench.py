@@ -39,12 +39,12 @@ PROFILES = os.path.join(ROOT, "profiles")
 # run from /tmp with TMPDIR=/tmp)
 PROFILE_COMMANDS = (
     "rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof_trace -o flce "
-    "-- python $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-chunked",
+    "-- python $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-chunked --no-vendor-gemm --no-torch-reference",
     "rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/prof_fetch -o flce "
-    "-- python $R/bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-chunked "
+    "-- python $R/bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-chunked --no-vendor-gemm --no-torch-reference "
     "--copy-calibration",
     "rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof_write -o flce "
-    "-- python $R/bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-chunked "
+    "-- python $R/bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-chunked --no-vendor-gemm --no-torch-reference "
     "--copy-calibration",
     "python $R/bench.py --summarize $R/gpurun_out",
 )
@@ -61,12 +61,12 @@ MFMA_COUNTERS = "SQ_VALU_MFMA_BUSY_CYCLES SQ_INSTS_VALU_MFMA_MOPS_BF16 SQ_BUSY_C
 MFMA_PROFILE_COMMANDS = (
     f"rocprofv3 --pmc {MFMA_COUNTERS} --kernel-trace --output-format csv "
     "-d $R/gpurun_out/prof_mfma -o flce -- python $R/bench.py --steps 1 --warmup 0 "
-    "--no-cpu-baseline --no-chunked",
+    "--no-cpu-baseline --no-chunked --no-vendor-gemm --no-torch-reference",
     f"rocprofv3 --pmc {MFMA_COUNTERS} --kernel-trace --output-format csv "
     "-d $R/gpurun_out/prof_mfma_chunk -o flce -- python $R/bench.py --steps 1 --warmup 0 "
     "--chunked-only",
     *(f"rocprofv3 --pmc {c} --kernel-trace --output-format csv -d $R/gpurun_out/stall{i + 1} "
-      "-o flce -- python $R/bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-chunked"
+      "-o flce -- python $R/bench.py --steps 1 --warmup 0 --no-cpu-baseline --no-chunked --no-vendor-gemm --no-torch-reference"
       for i, c in enumerate((
           "SQ_WAVE_CYCLES SQ_WAIT_ANY SQ_WAIT_INST_ANY SQ_WAIT_INST_LDS SQ_INSTS_VMEM_RD "
           "SQ_LDS_DATA_FIFO_FULL SQ_LDS_CMD_FIFO_FULL GRBM_GUI_ACTIVE",
@@ -74,6 +74,9 @@ MFMA_PROFILE_COMMANDS = (
           "SQ_ACTIVE_INST_ANY SQ_ACTIVE_INST_VALU GRBM_GUI_ACTIVE",
           "SQ_WAVE_CYCLES SQ_INSTS_MFMA SQ_INSTS_VALU SQ_INSTS_SALU SQ_ACTIVE_INST_SCA "
           "SQ_VMEM_TA_ADDR_FIFO_FULL SQ_VMEM_TA_CMD_FIFO_FULL GRBM_GUI_ACTIVE"))),
+    f"rocprofv3 --pmc {MFMA_COUNTERS} --kernel-trace --output-format csv "
+    "-d $R/gpurun_out/prof_mfma_vendor -o flce -- python $R/bench.py --steps 2 --warmup 1 "
+    "--vendor-gemm-only",
     "python $R/bench.py --summarize-mfma $R/gpurun_out",
 )
 SIMDS = 256 * 4           # MI355X: 256 compute units x 4 SIMDs
@@ -101,6 +104,13 @@ def parse():
     ap.add_argument("--summarize-mfma", metavar="DIR",
                     help="summarise DIR/prof_mfma and DIR/prof_mfma_chunk of "
                          "MFMA_PROFILE_COMMANDS into profiles/")
+    ap.add_argument("--no-vendor-gemm", action="store_true",
+                    help="skip timing hipBLASLt on the forward's logits GEMM")
+    ap.add_argument("--vendor-gemm-only", action="store_true",
+                    help="time only hipBLASLt on the forward's logits GEMM (for the "
+                         "counter runs)")
+    ap.add_argument("--no-torch-reference", action="store_true",
+                    help="skip timing the same loss in PyTorch eager")
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--summarize", metavar="DIR",
                     help="summarise the rocprofv3 output of PROFILE_COMMANDS under DIR "
@@ -303,7 +313,10 @@ def summarize_mfma(prof_dir):
            "measured clock is 2.5 PFLOP/s x clock / 2.4 GHz. Dispatches under 50 us are "
            "left out.", ""]
     for sub, title in (("prof_mfma", "recompute path (flce_forward + flce_backward)"),
-                       ("prof_mfma_chunk", "chunked mode (flce_chunked)")):
+                       ("prof_mfma_chunk", "chunked mode (flce_chunked)"),
+                       ("prof_mfma_vendor", "reference point: hipBLASLt on the forward's "
+                                            "logits GEMM alone (torch.matmul, [n, V] "
+                                            "logits materialised)")):
         cc = glob.glob(os.path.join(prof_dir, sub, "**", "*counter_collection.csv"),
                        recursive=True)
         kt = glob.glob(os.path.join(prof_dir, sub, "**", "*kernel_trace.csv"), recursive=True)
@@ -391,6 +404,75 @@ def summarize_mfma(prof_dir):
     print(md)
 
 
+def vendor_gemm(X, W, n, args, peak):
+    """Reference point, not part of the path: the forward's contraction alone,
+    the [n, V] logits of the valid rows materialised by torch.matmul
+    (hipBLASLt), 2 n H V flop per call, no softmax."""
+    import torch
+    Xv = X[:n].contiguous()
+    Wt = W.t()
+    out = torch.empty(n, W.shape[0], dtype=X.dtype, device=X.device)
+    for _ in range(max(args.warmup, 1)):
+        torch.matmul(Xv, Wt, out=out)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        torch.matmul(Xv, Wt, out=out)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    fl = 2.0 * n * X.shape[1] * W.shape[0]
+    del out
+    torch.cuda.empty_cache()
+    print(f"[bench] hipBLASLt logits GEMM: {ms:.3f} ms", file=sys.stderr, flush=True)
+    return {"ms": ms, "tflops": fl / (ms / 1e3) / 1e12, "frac": fl / (ms / 1e3) / peak,
+            "note": "torch.matmul (hipBLASLt) of the valid rows' [n, V] logits alone: the "
+                    "forward's contraction without the softmax, logits materialised"}
+
+
+def torch_eager(X, W, lab, w, args, peak):
+    """Reference point, not part of the path: the same loss and gradients in
+    PyTorch eager (F.linear + F.cross_entropy with autograd, bf16, the [N, V]
+    logits and their gradient materialised), timed like the main step."""
+    import torch
+    import torch.nn.functional as tF
+    y = lab.clone()
+    if w.shift:
+        y = torch.cat([y[:, 1:], torch.full_like(y[:, :1], w.ignore_index)], dim=1)
+    y = y.reshape(-1)
+    Xr = X.detach().requires_grad_(True)
+    Wr = W.detach().requires_grad_(True)
+
+    def step():
+        loss = tF.cross_entropy(tF.linear(Xr, Wr).float(), y, ignore_index=w.ignore_index,
+                                reduction=w.reduction)
+        dX, dW = torch.autograd.grad(loss, (Xr, Wr))
+        return loss, dX, dW
+
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
+    out = step()
+    torch.cuda.synchronize()
+    peak_extra = torch.cuda.max_memory_allocated() - base
+    del out
+    for _ in range(max(args.warmup, 1)):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    torch.cuda.empty_cache()
+    print(f"[bench] torch eager: {ms:.3f} ms/step", file=sys.stderr, flush=True)
+    return {"ms_per_step": ms, "tokens_per_s": w.N / (ms / 1e3),
+            "mfma_frac_model": 6.0 * w.N * w.H * w.V / (ms / 1e3) / peak,
+            "peak_extra_bytes": int(peak_extra),
+            "note": "PyTorch eager F.linear + F.cross_entropy (fp32 logits for the loss) with "
+                    "autograd: logits and their gradient materialised"}
+
+
 def chunked_mode(F, X, W, lab, w, dcode, dev, args, peak):
     """The same workload through flce_chunked (one call: loss, lse, dX, dW over
     row chunks; 6 n H V executed flop instead of 8), timed like the main step;
@@ -460,6 +542,9 @@ def main():
     dcode = F.FLCE_DTYPE_BF16 if w.dtype == "bf16" else F.FLCE_DTYPE_F32
     n_valid = int(((lab[:, 1:] if w.shift else lab) != w.ignore_index).sum())
     peak = BF16_PEAK if w.dtype == "bf16" else F32_PEAK
+    if args.vendor_gemm_only:
+        print(json.dumps({"vendor_gemm": vendor_gemm(X, W, n_valid, args, peak)}), flush=True)
+        return
     if args.chunked_only:
         print(json.dumps({"chunked_mode": chunked_mode(F, X, W, lab, w, dcode, dev, args,
                                                        peak)}), flush=True)
@@ -577,6 +662,11 @@ def main():
     }
     if not args.no_chunked:
         result["chunked_mode"] = chunked_mode(F, X, W, lab, w, dcode, dev, args, peak)
+    if not args.no_vendor_gemm and w.dtype == "bf16":
+        del ws
+        result["vendor_gemm"] = vendor_gemm(X, W, n_valid, args, peak)
+    if not args.no_torch_reference and w.dtype == "bf16":
+        result["torch_eager"] = torch_eager(X, W, lab, w, args, peak)
     if not args.no_cpu_baseline:
         print("[bench] oracle on the host", file=sys.stderr, flush=True)
         result["cpu_baseline"] = oracle_baseline(w, args.cpu_rows)

@@ -79,6 +79,11 @@ MFMA_PROFILE_COMMANDS = (
     "--vendor-gemm-only",
     "python $R/bench.py --summarize-mfma $R/gpurun_out",
 )
+# every bf16 workload through the bench (profiles/flce_workloads_bench.md)
+BENCH_WORKLOADS = ("qwen2_7b_head", "qwen3_sft_batch", "long_context", "ragged_vocab")
+WORKLOAD_BENCH_COMMANDS = tuple(
+    f"python $R/bench.py --workload {name} --steps 5 --warmup 2 > $R/gpurun_out/bench_{name}.json"
+    for name in BENCH_WORKLOADS) + ("python $R/bench.py --summarize-workloads $R/gpurun_out",)
 SIMDS = 256 * 4           # MI355X: 256 compute units x 4 SIMDs
 XCDS = 8                  # GRBM_GUI_ACTIVE comes summed over the 8 XCDs
 TRAFFIC = os.path.join(PROFILES, "traffic_qwen2_7b_head.json")
@@ -111,6 +116,9 @@ def parse():
                          "counter runs)")
     ap.add_argument("--no-torch-reference", action="store_true",
                     help="skip timing the same loss in PyTorch eager")
+    ap.add_argument("--summarize-workloads", metavar="DIR",
+                    help="summarise DIR/bench_<workload>.json of WORKLOAD_BENCH_COMMANDS into "
+                         "profiles/")
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--summarize", metavar="DIR",
                     help="summarise the rocprofv3 output of PROFILE_COMMANDS under DIR "
@@ -404,6 +412,46 @@ def summarize_mfma(prof_dir):
     print(md)
 
 
+def summarize_workloads(prof_dir):
+    """One table over the bench lines of every workload -> profiles/."""
+    rows = []
+    for name in BENCH_WORKLOADS:
+        path = os.path.join(prof_dir, f"bench_{name}.json")
+        if not os.path.exists(path):
+            continue
+        lines = [l for l in open(path) if l.startswith("{")]
+        if not lines:
+            continue
+        rows.append((name, json.loads(lines[-1])))
+    gb = 1e9
+    out = ["# Every bf16 workload through bench.py (MI355X, one GPU)", "",
+           "Commands ($R = repository root):", "", "```", *WORKLOAD_BENCH_COMMANDS, "```", "",
+           "Model basis: 6 N H V flop over all N rows; the recompute path executes 8 n H V "
+           "(n valid rows), the chunked mode 6 n H V. PyTorch eager and hipBLASLt are "
+           "context, not part of the path.", "",
+           "| workload | recompute ms | tokens/s | % bf16 peak (model) | peak extra GB | "
+           "chunked ms | chunked % | PyTorch eager ms | eager peak extra GB | hipBLASLt logits "
+           "GEMM ms | oracle tokens/s (host) |",
+           "|---|---|---|---|---|---|---|---|---|---|---|"]
+    for name, d in rows:
+        ch = d.get("chunked_mode") or {}
+        te = d.get("torch_eager") or {}
+        vg = d.get("vendor_gemm") or {}
+        cb = d.get("cpu_baseline") or {}
+        out.append(
+            f"| {d['config']['workload']} | {d['ms_per_step']:.2f} | {d['value']:.3g} | "
+            f"{100 * d['mfma_frac_model']:.1f} | {d['peak_extra_bytes'] / gb:.2f} | "
+            f"{ch.get('ms_per_step', float('nan')):.2f} | "
+            f"{100 * ch.get('mfma_frac_model', float('nan')):.1f} | "
+            f"{te.get('ms_per_step', float('nan')):.2f} | "
+            f"{te.get('peak_extra_bytes', float('nan')) / gb:.1f} | "
+            f"{vg.get('ms', float('nan')):.2f} | {cb.get('value', float('nan')):.0f} |")
+    md = os.path.join(PROFILES, "flce_workloads_bench.md")
+    with open(md, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print(md)
+
+
 def vendor_gemm(X, W, n, args, peak):
     """Reference point, not part of the path: the forward's contraction alone,
     the [n, V] logits of the valid rows materialised by torch.matmul
@@ -513,6 +561,9 @@ def main():
     args = parse()
     if args.summarize:
         summarize(args.summarize, PROFILE_COMMANDS)
+        return
+    if args.summarize_workloads:
+        summarize_workloads(args.summarize_workloads)
         return
     if args.summarize_mfma:
         summarize_mfma(args.summarize_mfma)

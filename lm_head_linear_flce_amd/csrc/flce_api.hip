@@ -31,12 +31,34 @@ struct Plan {
   int64_t TT, VT;           // token tiles (upper bound), vocabulary tiles
   int64_t fwd_items;        // forward work items (range x token tile), at most
   int64_t Vb;               // backward vocabulary block (multiple of 256)
+  int64_t dx_split;         // dX tiles per (token tile, hidden tile) and block
   // workspace offsets (bytes)
   int64_t o_ctr, o_idx, o_tgt, o_rowpos, o_xc;
   int64_t o_part, o_zt, o_bsum;            // forward region
   int64_t o_lse2, o_rs, o_g, o_dx32;       // backward region
   int64_t total;
 };
+
+// The dX tiles of a launch number (token tiles) x (hidden tiles), each with a
+// K loop over the whole vocabulary block.  Where that count is small (narrow
+// H, few rows) a launch would last as long as one dX tile while most compute
+// units idle, so the block's vocabulary range is cut into parts, each with its
+// own FP32 accumulator, until about `target` dX tiles are in flight (at most
+// kMaxDxSplit parts).  The recompute path's launches also carry the G tiles
+// (three tile kinds of equal total work, the chunked mode's two), and its
+// token-tile count is a bound that the valid rows may not reach, hence the
+// larger target.
+#ifndef FLCE_DX_TILES
+#define FLCE_DX_TILES 256
+#endif
+#ifndef FLCE_DX_TILES_CHUNKED
+#define FLCE_DX_TILES_CHUNKED 176
+#endif
+constexpr int64_t kMaxDxSplit = 8;
+int64_t dx_split_for(int64_t hidden_tiles, int64_t token_tiles, int64_t target) {
+  return std::min<int64_t>(kMaxDxSplit,
+                           std::max<int64_t>(1, cdiv(target, hidden_tiles * token_tiles)));
+}
 
 int make_plan(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, Plan* p) {
   if (B < 0 || T < 0 || H <= 0 || V <= 0) return FLCE_ERR_SHAPE;
@@ -65,6 +87,7 @@ int make_plan(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, Plan* p) {
   vb = std::max<int64_t>(kTile, vb / kTile * kTile);
   vb = std::min<int64_t>(vb, round_up(V, kTile));
   q.Vb = vb;
+  q.dx_split = dx_split_for(cdiv(H, kTile), q.TT, FLCE_DX_TILES);
   // 32-bit offsets inside the kernels
   if (q.rows_pad * q.Vb * q.es > kMaxI32 || q.rows_pad * H * 4 > kMaxI32 ||
       (int64_t)kTile * H * q.es * 2 > kMaxI32)
@@ -90,7 +113,7 @@ int make_plan(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, Plan* p) {
   q.o_lse2 = take(4 * q.rows_pad);
   q.o_rs = take(4 * q.rows_pad);
   q.o_g = take(2 * q.rows_pad * q.Vb * q.es);   // two slabs, alternating blocks
-  q.o_dx32 = take(4 * q.rows_pad * H);
+  q.o_dx32 = take(4 * q.dx_split * q.rows_pad * H);
   const int64_t bwd_end = off;
   q.total = std::max(fwd_end, bwd_end);
   *p = q;
@@ -189,7 +212,7 @@ int forward_impl(const Plan& pl, const Shard& sh, const void* X, const void* W,
   hipLaunchKernelGGL(k_gather, dim3((unsigned)cdiv(rows_pad, 4)), dim3(256), 0, stream,
                      (const char*)X, row_bytes, (const int*)idx, (const Counters*)ctr,
                      xc, rows_pad, (const float*)nullptr, (float*)nullptr,
-                     (float*)nullptr, 0, (const float*)nullptr, (float*)nullptr);
+                     (float*)nullptr, 0, 0, (int64_t)0, (const float*)nullptr, (float*)nullptr);
   L.check();
   hipLaunchKernelGGL(k_target<E>, dim3((unsigned)cdiv(rows_pad, 4)), dim3(256), 0, stream,
                      (const char*)xc, (const char*)W, (int)pl.H, (const int*)tgt,
@@ -250,7 +273,8 @@ int backward_impl(const Plan& pl, const Shard& sh, const void* X, const void* W,
   L.check();
   hipLaunchKernelGGL(k_gather, dim3((unsigned)cdiv(rows_pad, 4)), dim3(256), 0, stream,
                      (const char*)X, row_bytes, (const int*)idx, (const Counters*)ctr,
-                     xc, rows_pad, lse, lse2, dx32, (int)(pl.H * 4), grad_scale, rs);
+                     xc, rows_pad, lse, lse2, dx32, (int)(pl.H * 4), (int)pl.dx_split,
+                     (int64_t)pl.rows_pad * pl.H, grad_scale, rs);
   L.check();
 
   BwdArgs a;
@@ -261,6 +285,9 @@ int backward_impl(const Plan& pl, const Shard& sh, const void* X, const void* W,
   a.rs = rs;
   a.tgt = tgt;
   a.dx32 = dx32;
+  a.dx32p = dx32 + (int64_t)pl.rows_pad * pl.H;
+  a.dx_stride = (int64_t)pl.rows_pad * pl.H;
+  a.dx_split = (int)pl.dx_split;
   a.dW = (char*)dW;
   a.ctr = ctr;
   a.H = (int)pl.H;
@@ -288,7 +315,7 @@ int backward_impl(const Plan& pl, const Shard& sh, const void* X, const void* W,
   for (int64_t b = -1; b < nblk && L.err == hipSuccess; ++b) {
     const BwdArgs cur = b >= 0 ? block(b) : a;
     const BwdArgs nxt = b + 1 < nblk ? block(b + 1) : a;
-    const int nb_dx = b >= 0 ? (int)pad8((int64_t)a.HT * a.TT) : 0;
+    const int nb_dx = b >= 0 ? (int)pad8((int64_t)a.dx_split * a.HT * a.TT) : 0;
     const int nb_dw = b >= 0 ? (int)pad8((int64_t)a.HT * cur.VTb) : 0;
     const int nb_g = b + 1 < nblk ? (int)pad8((int64_t)nxt.VTb * a.TT) : 0;
     {
@@ -304,8 +331,8 @@ int backward_impl(const Plan& pl, const Shard& sh, const void* X, const void* W,
     }
   }
   hipLaunchKernelGGL(k_dx_final, dim3((unsigned)cdiv(pl.N, 4)), dim3(256), 0, stream,
-                     (const float*)dx32, (const int*)rowpos, (int)pl.N, (int)pl.H,
-                     (char*)dX, dx_f32);
+                     (const float*)dx32, (int)pl.dx_split, (int64_t)pl.rows_pad * pl.H,
+                     (const int*)rowpos, (int)pl.N, (int)pl.H, (char*)dX, dx_f32);
   L.check();
   return L.err == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }
@@ -337,9 +364,10 @@ struct ChunkPlan {
   int64_t N, rows_pad, H, V, Vp, es, TT, VT;
   int64_t C, nchunks;       // chunk rows (multiple of 256), chunks covering rows_pad
   int64_t VB;               // vocabulary block of the dX / dW launches
+  int64_t dx_split;         // dX tiles per (token tile, hidden tile) and block
   int64_t o_ctr, o_idx, o_tgt, o_rowpos, o_xc, o_zt, o_lse_c, o_lse2, o_rloss, o_bsum, o_cctr;
   int64_t o_rs;
-  int64_t o_part, o_slab, o_dx32;
+  int64_t o_part, o_slab, o_dx32, o_dx32p;
   int64_t total;
 };
 
@@ -392,7 +420,11 @@ int make_chunk_plan(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, int64
   q.o_cctr = take(sizeof(Counters) * q.nchunks);
   q.o_part = take(8 * 2 * q.VT * q.C);
   q.o_slab = take(q.C * q.Vp * q.es);
+  q.dx_split = dx_split_for(cdiv(H, kTile), q.C / kTile, FLCE_DX_TILES_CHUNKED);
   q.o_dx32 = take(4 * q.rows_pad * H);
+  // the extra vocabulary parts of dX cover one chunk's rows; they are folded
+  // into the main FP32 sum after each chunk
+  q.o_dx32p = take(4 * (q.dx_split - 1) * q.C * H);
   q.total = off;
   *p = q;
   return FLCE_OK;
@@ -419,6 +451,7 @@ int chunked_impl(const ChunkPlan& pl, const void* X, const void* W, const int64_
   float2* part = (float2*)(ws + pl.o_part);
   char* slab = ws + pl.o_slab;
   float* dx32 = (float*)(ws + pl.o_dx32);
+  float* dx32p = (float*)(ws + pl.o_dx32p);
   const int rows_pad = (int)pl.rows_pad;
   const int row_bytes = (int)(pl.H * E::kBytes);
   const int C = (int)pl.C, TTc = C / kTile, HT = (int)cdiv(pl.H, kTile);
@@ -432,7 +465,7 @@ int chunked_impl(const ChunkPlan& pl, const void* X, const void* W, const int64_
   hipLaunchKernelGGL(k_gather, dim3((unsigned)cdiv(rows_pad, 4)), dim3(256), 0, stream,
                      (const char*)X, row_bytes, (const int*)idx, (const Counters*)ctr, xc,
                      rows_pad, (const float*)nullptr, (float*)nullptr, dx32,
-                     (int)(pl.H * 4), grad_scale, rs);
+                     (int)(pl.H * 4), 1, (int64_t)0, grad_scale, rs);
   L.check();
   hipLaunchKernelGGL(k_target<E>, dim3((unsigned)cdiv(rows_pad, 4)), dim3(256), 0, stream,
                      (const char*)xc, (const char*)W, (int)pl.H, (const int*)tgt,
@@ -485,6 +518,10 @@ int chunked_impl(const ChunkPlan& pl, const void* X, const void* W, const int64_
     b.rs = rs;
     b.tgt = tgt;
     b.dx32 = dx32 + (int64_t)ca.row0 * pl.H;
+    b.dx32p = dx32p;
+    b.dx_stride = (int64_t)C * pl.H;
+    b.dx_split = (int)pl.dx_split;
+    if (pl.dx_split > 1) zero_fill(dx32p, 4 * (pl.dx_split - 1) * C * pl.H, stream);
     b.dW = (char*)dW;
     b.ctr = cctr + ch;
     b.H = (int)pl.H;
@@ -500,10 +537,21 @@ int chunked_impl(const ChunkPlan& pl, const void* X, const void* W, const int64_
       b.vb = (int)std::min<int64_t>(pl.VB, pl.V - v0);
       b.VTb = (int)cdiv(b.vb, kTile);
       b.G = slab + v0 * E::kBytes;
-      const int nb_dx = (int)pad8((int64_t)HT * TTc), nb_dw = (int)pad8((int64_t)HT * b.VTb);
+      const int nb_dx = (int)pad8((int64_t)pl.dx_split * HT * TTc);
+      const int nb_dw = (int)pad8((int64_t)HT * b.VTb);
       Timed t("k_chunk_dxdw", stream);
       hipLaunchKernelGGL(k_bwd<E>, dim3((unsigned)(nb_dx + nb_dw)), dim3(kThreads), kLdsBytes,
                          stream, b, b, nb_dx, nb_dw, 0);
+      L.check();
+    }
+    if (pl.dx_split > 1 && L.err == hipSuccess) {
+      // the chunk's extra vocabulary parts into the main sum, in part order
+      // (the last chunk may reach past rows_pad: only its rows inside it)
+      const int64_t rows = std::min<int64_t>(C, pl.rows_pad - ca.row0);
+      const int64_t count4 = rows * pl.H / 4;
+      hipLaunchKernelGGL(k_dx_fold, dim3((unsigned)std::min<int64_t>(cdiv(count4, 256), 4096)),
+                         dim3(256), 0, stream, b.dx32, (const float*)dx32p,
+                         (int)pl.dx_split - 1, (int64_t)C * pl.H, count4);
       L.check();
     }
   }
@@ -518,8 +566,8 @@ int chunked_impl(const ChunkPlan& pl, const void* X, const void* W, const int64_
                      (const Counters*)ctr, reduction, none ? (float*)nullptr : loss, n_valid);
   L.check();
   hipLaunchKernelGGL(k_dx_final, dim3((unsigned)cdiv(pl.N, 4)), dim3(256), 0, stream,
-                     (const float*)dx32, (const int*)rowpos, (int)pl.N, (int)pl.H,
-                     (char*)dX, grad_f32);
+                     (const float*)dx32, 1, (int64_t)0, (const int*)rowpos, (int)pl.N,
+                     (int)pl.H, (char*)dX, grad_f32);
   L.check();
   return L.err == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }

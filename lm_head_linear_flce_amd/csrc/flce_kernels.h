@@ -136,14 +136,15 @@ __global__ __launch_bounds__(1024) void k_prep(
 // ---------------------------------------------------------------------------
 // k_gather: one wave per compacted row k in [0, rows_pad).  Row k < n copies
 // X[idx[k]]; the rest is zero.  In the backward it also stages
-// lse2[k] = lse[idx[k]] * log2(e) and clears the FP32 dX accumulator row.
+// lse2[k] = lse[idx[k]] * log2(e) and clears row k of each of the dx_split
+// FP32 dX accumulators (dx_stride floats apart).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_gather(
     const char* __restrict__ X, int row_bytes, const int* __restrict__ idx,
     const Counters* __restrict__ ctr, char* __restrict__ Xc, int rows_pad,
     const float* __restrict__ lse, float* __restrict__ lse2,
-    float* __restrict__ dx32, int dx32_row_bytes, const float* __restrict__ rs_in,
-    float* __restrict__ rs_c) {
+    float* __restrict__ dx32, int dx32_row_bytes, int dx_split, int64_t dx_stride,
+    const float* __restrict__ rs_in, float* __restrict__ rs_c) {
   const int k = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (k >= rows_pad) return;
@@ -159,8 +160,10 @@ __global__ __launch_bounds__(256) void k_gather(
   if (lse2 != nullptr && lane == 0) lse2[k] = k < n ? lse[idx[k]] * kLog2e : 0.f;
   if (rs_c != nullptr && lane == 0) rs_c[k] = k < n ? rs_in[idx[k]] : 0.f;
   if (dx32 != nullptr) {
-    i32x4* d = (i32x4*)((char*)dx32 + (int64_t)k * dx32_row_bytes);
-    for (int c = lane; c < (dx32_row_bytes >> 4); c += 64) d[c] = i32x4{0, 0, 0, 0};
+    for (int sp = 0; sp < dx_split; ++sp) {
+      i32x4* d = (i32x4*)((char*)(dx32 + sp * dx_stride) + (int64_t)k * dx32_row_bytes);
+      for (int c = lane; c < (dx32_row_bytes >> 4); c += 64) d[c] = i32x4{0, 0, 0, 0};
+    }
   }
 }
 
@@ -419,7 +422,11 @@ struct BwdArgs {
   const float* lse2;   // [rows_pad] lse * log2(e)
   const float* rs;     // [rows_pad] per-row gradient factors (reduction "none") or NULL
   const int* tgt;      // [n]
-  float* dx32;         // [rows_pad, H]
+  float* dx32;         // [rows_pad, H]: the FP32 dX sum (vocabulary part 0)
+  float* dx32p;        // parts 1 .. dx_split - 1, [rows_pad, H] each, dx_stride
+  int64_t dx_stride;   //   floats apart
+  int dx_split;        // dX tiles per (token tile, hidden tile): the block's
+                       // vocabulary range cut into this many parts
   char* dW;            // [V, H] output (grad dtype)
   const Counters* ctr;
   int H, V, rows_pad, Vb;
@@ -661,9 +668,10 @@ __device__ __forceinline__ void dw_tile(const BwdArgs& a, int b, lds_t* smem) {
 // the load returns zeros and the store is dropped.
 template <bool kMasked>
 __device__ __forceinline__ void dx_add(const BwdArgs& a, const f32x16 (&acc)[4][4],
-                                       int tau, int ht, int wm, int wn, int lane,
+                                       int part, int tau, int ht, int wm, int wn, int lane,
                                        int nlim, int hlim, lds_t* smem) {
-  const rsrc_t xr = make_rsrc(a.dx32, (int64_t)a.rows_pad * a.H * 4);
+  float* base = part == 0 ? a.dx32 : a.dx32p + (part - 1) * a.dx_stride;
+  const rsrc_t xr = make_rsrc(base, (int64_t)a.rows_pad * a.H * 4);
   const int wave = threadIdx.x >> 6;
   auto offset = [&](int o, int x0) {
     const int tcol = wn * 128 + o, hc = wm * 128 + x0;
@@ -679,39 +687,52 @@ __device__ __forceinline__ void dx_add(const BwdArgs& a, const f32x16 (&acc)[4][
       });
 }
 
-// dX32[k, h] += sum_m W[v0 + m, h] G[k, m] over the whole block for one
-// (hidden tile, token tile): A = W (K = vocabulary rows outer), B = G rows
-// (K contiguous).  Past the block's end G is zero (last block) or the step
-// count stops at the block (others).
+// dX32_part[k, h] += sum_m W[v0 + m, h] G[k, m] for one (part, hidden tile,
+// token tile), m over part `part` of the block's vocabulary range (parts of
+// a multiple of 64 columns; the last may be shorter): A = W (K = vocabulary
+// rows outer), B = G rows (K contiguous).  G reads past the part's last
+// column are zero (kbytes), so the W rows a last partial step reaches add
+// nothing.  Each part has its own FP32 accumulator, so the parts of one tile
+// run in the same launch without sharing memory, and the final sum over the
+// parts is in fixed order (k_dx_final).
 template <class E>
 __device__ __forceinline__ void dx_tile(const BwdArgs& a, int b, lds_t* smem) {
   const int n = a.ctr->n;
   const int TTn = (n + kTile - 1) / kTile;
-  const int item = live_item(b, a.HT * TTn);
+  const int per_part = a.HT * TTn;
+  const int item = live_item(b, a.dx_split * per_part);
   if (item < 0) return;
+  const int part = item / per_part;
   int ht, tau;
-  grouped(item, a.HT, TTn, ht, tau);
+  grouped(item - part * per_part, a.HT, TTn, ht, tau);
+  const int pw = (((a.vb + a.dx_split - 1) / a.dx_split) + 63) & ~63;
+  const int m0 = part * pw;
+  if (m0 >= a.vb) return;
+  const int len = a.vb - m0 < pw ? a.vb - m0 : pw;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int es = E::kBytes;
-  const int steps = (a.vb + E::kKStep - 1) / E::kKStep;
+  const int steps = (len + E::kKStep - 1) / E::kKStep;
 
   Opnd A, B;
-  A.base = a.W + ((int64_t)a.v0 * a.H + (int64_t)ht * kTile) * es;
-  A.bytes = (int64_t)a.V * a.H * es - ((int64_t)a.v0 * a.H + (int64_t)ht * kTile) * es;
+  const int64_t aoff = ((int64_t)(a.v0 + m0) * a.H + (int64_t)ht * kTile) * es;
+  A.base = a.W + aoff;
+  A.bytes = (int64_t)a.V * a.H * es - aoff;
   A.ldb = a.H * es;
   A.kbytes = 0;
-  B.base = a.G + (int64_t)tau * kTile * a.Vb * es;
-  B.bytes = (int64_t)a.rows_pad * a.Vb * es - (int64_t)tau * kTile * a.Vb * es;
+  const int64_t boff = ((int64_t)tau * kTile * a.Vb + m0) * es;
+  B.base = a.G + boff;
+  B.bytes = (int64_t)a.rows_pad * a.Vb * es - boff;
   B.ldb = a.Vb * es;
-  B.kbytes = a.Vb * es;
+  B.kbytes = len * es;
   f32x16 acc[4][4];
   zero_acc(acc);
   gemm_tile<E, LoadMN<E>, LoadDirect>(A, B, steps, smem, wm, wn, acc);
 
   const int nlim = n - tau * kTile, hlim = a.H - ht * kTile;
-  if (nlim >= kTile && hlim >= kTile) dx_add<false>(a, acc, tau, ht, wm, wn, lane, 0, 0, smem);
-  else dx_add<true>(a, acc, tau, ht, wm, wn, lane, nlim, hlim, smem);
+  if (nlim >= kTile && hlim >= kTile)
+    dx_add<false>(a, acc, part, tau, ht, wm, wn, lane, 0, 0, smem);
+  else dx_add<true>(a, acc, part, tau, ht, wm, wn, lane, nlim, hlim, smem);
 }
 
 // One backward launch: nb_dx dX tiles and nb_dw dW tiles of block `cur`,
@@ -1054,8 +1075,8 @@ __global__ __launch_bounds__(256) void k_shard_merge(
 }
 
 __global__ __launch_bounds__(256) void k_dx_final(
-    const float* __restrict__ dx32, const int* __restrict__ rowpos, int N, int H,
-    char* __restrict__ dX, int out_f32) {
+    const float* __restrict__ dx32, int dx_split, int64_t dx_stride,
+    const int* __restrict__ rowpos, int N, int H, char* __restrict__ dX, int out_f32) {
   const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (i >= N) return;
@@ -1063,7 +1084,14 @@ __global__ __launch_bounds__(256) void k_dx_final(
   const int groups = H >> 2;  // 4 values per lane step
   for (int g = lane; g < groups; g += 64) {
     f32x4 v = {0.f, 0.f, 0.f, 0.f};
-    if (k >= 0) v = *(const f32x4*)(dx32 + (int64_t)k * H + 4 * g);
+    if (k >= 0) {
+      // the vocabulary parts' FP32 sums, added in part order
+      v = *(const f32x4*)(dx32 + (int64_t)k * H + 4 * g);
+      for (int sp = 1; sp < dx_split; ++sp) {
+        const f32x4 u = *(const f32x4*)(dx32 + sp * dx_stride + (int64_t)k * H + 4 * g);
+        v = f32x4{v[0] + u[0], v[1] + u[1], v[2] + u[2], v[3] + u[3]};
+      }
+    }
     if (out_f32) {
       *(f32x4*)((float*)dX + (int64_t)i * H + 4 * g) = v;
     } else {
@@ -1072,6 +1100,24 @@ __global__ __launch_bounds__(256) void k_dx_final(
       pk[1] = pack_bf16(v[2], v[3]);
       *(i32x2*)((uint16_t*)dX + (int64_t)i * H + 4 * g) = pk;
     }
+  }
+}
+
+// dst[k, :] += sum over p = 0 .. parts - 1 of src_p[k, :] (src_p = src + p *
+// stride floats), in that order, for rows k < rows of H floats: folds a row
+// chunk's extra vocabulary parts of dX into the main FP32 sum.  Grid-stride,
+// 4 floats per thread step.
+__global__ __launch_bounds__(256) void k_dx_fold(float* __restrict__ dst,
+                                                 const float* __restrict__ src, int parts,
+                                                 int64_t stride, int64_t count4) {
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < count4;
+       i += (int64_t)gridDim.x * 256) {
+    f32x4 v = *(const f32x4*)(dst + 4 * i);
+    for (int p = 0; p < parts; ++p) {
+      const f32x4 u = *(const f32x4*)(src + p * stride + 4 * i);
+      v = f32x4{v[0] + u[0], v[1] + u[1], v[2] + u[2], v[3] + u[3]};
+    }
+    *(f32x4*)(dst + 4 * i) = v;
   }
 }
 

@@ -312,6 +312,9 @@ int backward_impl(const Plan& pl, const Shard& sh, const void* X, const void* W,
   // launch b + 1 runs the dX / dW tiles of block b and the G tiles of block
   // b + 1 (dX first: its tiles are the longest)
   const int64_t nblk = cdiv(pl.V, pl.Vb);
+  // the dW tiles' K loop runs over the rows (bounded by rows_pad), the dX
+  // tiles' over a part of the block: the longer kind starts first
+  const int dw_first = pl.rows_pad > cdiv(pl.Vb, pl.dx_split) ? 1 : 0;
   for (int64_t b = -1; b < nblk && L.err == hipSuccess; ++b) {
     const BwdArgs cur = b >= 0 ? block(b) : a;
     const BwdArgs nxt = b + 1 < nblk ? block(b + 1) : a;
@@ -321,7 +324,7 @@ int backward_impl(const Plan& pl, const Shard& sh, const void* X, const void* W,
     {
       Timed t("k_bwd", stream);
       hipLaunchKernelGGL(k_bwd<E>, dim3((unsigned)(nb_dx + nb_dw + nb_g)), dim3(kThreads),
-                         kLdsBytes, stream, cur, nxt, nb_dx, nb_dw, nb_g);
+                         kLdsBytes, stream, cur, nxt, nb_dx, nb_dw, nb_g, dw_first);
       L.check();
     }
     if (b + 1 < nblk) {
@@ -541,7 +544,7 @@ int chunked_impl(const ChunkPlan& pl, const void* X, const void* W, const int64_
       const int nb_dw = (int)pad8((int64_t)HT * b.VTb);
       Timed t("k_chunk_dxdw", stream);
       hipLaunchKernelGGL(k_bwd<E>, dim3((unsigned)(nb_dx + nb_dw)), dim3(kThreads), kLdsBytes,
-                         stream, b, b, nb_dx, nb_dw, 0);
+                         stream, b, b, nb_dx, nb_dw, 0, C > cdiv(b.vb, pl.dx_split) ? 1 : 0);
       L.check();
     }
     if (pl.dx_split > 1 && L.err == hipSuccess) {

@@ -737,23 +737,25 @@ __device__ __forceinline__ void dx_tile(const BwdArgs& a, int b, lds_t* smem) {
 
 // One backward launch: nb_dx dX tiles and nb_dw dW tiles of block `cur`,
 // then nb_g G tiles of block `nxt` (each count a multiple of 8, so every
-// kind is spread over the XCDs on its own).
+// kind is spread over the XCDs on its own).  Workgroups start roughly in
+// index order, so the kind with the longer K loop goes first (dw_first: the
+// dW tiles, whose K runs over the rows, before the dX tiles, whose K runs
+// over the block), and the shorter tiles fill the launch's last wave.
 template <class E>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void k_bwd(BwdArgs cur, BwdArgs nxt, int nb_dx, int nb_dw, int nb_g) {
+void k_bwd(BwdArgs cur, BwdArgs nxt, int nb_dx, int nb_dw, int nb_g, int dw_first) {
   extern __shared__ __attribute__((aligned(16))) char smem_[];
   lds_t* smem = (lds_t*)smem_;
   int b = blockIdx.x;
-  if (b < nb_dx) {
-    dx_tile<E>(cur, b, smem);
+  const int n1 = dw_first ? nb_dw : nb_dx, n2 = dw_first ? nb_dx : nb_dw;
+  if (b < n1 + n2) {
+    const bool dw = dw_first ? b < n1 : b >= n1;
+    const int i = b < n1 ? b : b - n1;
+    if (dw) dw_tile<E>(cur, i, smem);
+    else dx_tile<E>(cur, i, smem);
     return;
   }
-  b -= nb_dx;
-  if (b < nb_dw) {
-    dw_tile<E>(cur, b, smem);
-    return;
-  }
-  b -= nb_dw;
+  b -= n1 + n2;
   if (b < nb_g) g_tile<E>(nxt, b, smem);
 }
 

@@ -83,8 +83,10 @@ extern "C" {
  * flce_backward need for this shape and dtype (one buffer serves both).
  * Host-only arithmetic, no HIP call.  The figure is the engine's whole extra
  * device memory: it grows linearly in N (per-row indices, a compacted copy of
- * the valid rows of X, an FP32 dX accumulator and two bounded slabs of
- * softmax gradients, each covering a fixed vocabulary block), never with N*V.
+ * the valid rows of X, FP32 dX accumulators -- one, or up to eight vocabulary
+ * parts when few hidden x row tiles would leave compute units idle -- and two
+ * bounded slabs of softmax gradients, each covering a fixed vocabulary
+ * block), never with N*V.
  *   B, T, H, V : problem sizes (B*T = N rows)
  *   dtype      : FLCE_DTYPE_*
  *   bytes      : out, host pointer

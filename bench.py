@@ -711,13 +711,25 @@ def main():
                      "peak": peak / 1e12, "unit": "TFLOP/s", "frac": ach / peak,
                      "traffic": measured_traffic(dom, w.name)},
     }
+    # the measurements beside the path: each one's failure is reported in its
+    # place and leaves the line intact
+    def beside(key, fn):
+        try:
+            result[key] = fn()
+        except Exception as e:  # noqa: BLE001  (reported, not swallowed)
+            print(f"[bench] {key} failed: {e!r}", file=sys.stderr, flush=True)
+            result[key] = {"error": repr(e)}
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+
     if not args.no_chunked:
-        result["chunked_mode"] = chunked_mode(F, X, W, lab, w, dcode, dev, args, peak)
+        beside("chunked_mode", lambda: chunked_mode(F, X, W, lab, w, dcode, dev, args, peak))
+    del ws
+    torch.cuda.empty_cache()
     if not args.no_vendor_gemm and w.dtype == "bf16":
-        del ws
-        result["vendor_gemm"] = vendor_gemm(X, W, n_valid, args, peak)
+        beside("vendor_gemm", lambda: vendor_gemm(X, W, n_valid, args, peak))
     if not args.no_torch_reference and w.dtype == "bf16":
-        result["torch_eager"] = torch_eager(X, W, lab, w, args, peak)
+        beside("torch_eager", lambda: torch_eager(X, W, lab, w, args, peak))
     if not args.no_cpu_baseline:
         print("[bench] oracle on the host", file=sys.stderr, flush=True)
         result["cpu_baseline"] = oracle_baseline(w, args.cpu_rows)

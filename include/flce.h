@@ -254,14 +254,17 @@ int flce_chunked(const void* X, const void* W, const int64_t* labels,
                  size_t workspace_bytes, void* stream);
 
 /*
- * flce_scale_grads -- dX[0:nx] *= *scale and dW[0:nw] *= *scale in place (the
+ * flce_scale_grads -- dX = *scale * dX_in and dW = *scale * dW_in (the
  * upstream gradient applied to gradients computed with grad_scale = 1, e.g.
- * by flce_chunked during an autograd forward).  nx, nw: element counts,
- * multiples of 8 (bf16) or 4 (fp32); grad_dtype FLCE_DTYPE_BF16 or _F32;
- * scale: float32 scalar, device.  Buffers 16-byte aligned.
+ * by flce_chunked during an autograd forward).  Each output may be its own
+ * input (in place) or must not overlap it (else FLCE_ERR_ALIAS); out of
+ * place, the inputs stay as they are, so the same saved gradients can be
+ * scaled again (a second backward through a retained graph).  nx, nw: element
+ * counts, multiples of 8 (bf16) or 4 (fp32); grad_dtype FLCE_DTYPE_BF16 or
+ * _F32; scale: float32 scalar, device.  Buffers 16-byte aligned.
  */
-int flce_scale_grads(void* dX, int64_t nx, void* dW, int64_t nw, int grad_dtype,
-                     const float* scale, void* stream);
+int flce_scale_grads(const void* dX_in, void* dX, int64_t nx, const void* dW_in, void* dW,
+                     int64_t nw, int grad_dtype, const float* scale, void* stream);
 
 /*
  * flce_set_timing -- measurement hook for benchmarks and profilers.  While set,

@@ -100,7 +100,7 @@ def _load() -> ctypes.CDLL:
     lib.flce_chunked.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, i64, i32, i32, i64,
                                  vp, vp, vp, vp, vp, vp, i32, i32, vp, vp, sz, vp]
     lib.flce_chunked.restype = i32
-    lib.flce_scale_grads.argtypes = [vp, i64, vp, i64, i32, vp, vp]
+    lib.flce_scale_grads.argtypes = [vp, vp, i64, vp, vp, i64, i32, vp, vp]
     lib.flce_scale_grads.restype = i32
     lib.flce_set_timing.argtypes = [ctypes.c_char_p, vp, i32, ctypes.POINTER(i32)]
     lib.flce_set_timing.restype = i32
@@ -213,10 +213,10 @@ def flce_chunked(X, W, labels, B, T, H, V, dtype, ignore_index, reduction, shift
                              stream or None)
 
 
-def flce_scale_grads(dX, nx, dW, nw, grad_dtype, scale, stream) -> int:
+def flce_scale_grads(dX_in, dX, nx, dW_in, dW, nw, grad_dtype, scale, stream) -> int:
     """Returns the status code (0 on success); raises nothing."""
-    return _LIB.flce_scale_grads(dX or None, nx, dW or None, nw, grad_dtype, scale or None,
-                                 stream or None)
+    return _LIB.flce_scale_grads(dX_in or None, dX or None, nx, dW_in or None, dW or None, nw,
+                                 grad_dtype, scale or None, stream or None)
 
 
 def flce_set_timing(kernel, events, capacity, count) -> int:
@@ -540,11 +540,15 @@ def _autograd_function():
             dX, dW = ctx.saved_tensors
             g = grad_out.reshape(()).to(dtype=torch.float32).contiguous()
             gd = _dtype_code(dX)
-            rc = flce_scale_grads(dX.data_ptr(), dX.numel(), dW.data_ptr(), dW.numel(), gd,
-                                  g.data_ptr(), _stream_handle(dX.device))
+            # out of place: the saved gradients stay unscaled, so a second
+            # backward (retain_graph=True) scales them afresh
+            gX, gW = torch.empty_like(dX), torch.empty_like(dW)
+            rc = flce_scale_grads(dX.data_ptr(), gX.data_ptr(), dX.numel(), dW.data_ptr(),
+                                  gW.data_ptr(), dW.numel(), gd, g.data_ptr(),
+                                  _stream_handle(dX.device))
             if rc != FLCE_OK:
                 raise FlceError(rc, "flce_scale_grads")
-            return dX, dW, None, None, None, None
+            return gX, gW, None, None, None, None
 
     return LinearCrossEntropy, LinearCrossEntropyChunked
 

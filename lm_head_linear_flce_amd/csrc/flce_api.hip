@@ -230,8 +230,10 @@ int forward_impl(const Plan& pl, const Shard& sh, const void* X, const void* W,
   if (L.err == hipSuccess) L.err = allow_big_lds(k_fwd_lse<E>);
   {
     Timed t("k_fwd_lse", stream);
-    hipLaunchKernelGGL(k_fwd_lse<E>, dim3((unsigned)pl.fwd_items), dim3(kThreads), kLdsBytes,
-                       stream, fa);
+    // k_fwd_lse hands its items out XCD by XCD over the first pad8(P * TTn)
+    // workgroups (P * TTn <= fwd_items), so the grid covers pad8(fwd_items)
+    hipLaunchKernelGGL(k_fwd_lse<E>, dim3((unsigned)pad8(pl.fwd_items)), dim3(kThreads),
+                       kLdsBytes, stream, fa);
     L.check();
   }
   const int nb = (int)cdiv(pl.N, 256);
@@ -866,14 +868,23 @@ int flce_chunked(const void* X, const void* W, const int64_t* labels, int64_t B,
                            (char*)workspace, s);
 }
 
-int flce_scale_grads(void* dX, int64_t nx, void* dW, int64_t nw, int grad_dtype,
-                     const float* scale, void* stream) {
+int flce_scale_grads(const void* dX_in, void* dX, int64_t nx, const void* dW_in, void* dW,
+                     int64_t nw, int grad_dtype, const float* scale, void* stream) {
   if (scale == nullptr) return FLCE_ERR_NULL;
   if (grad_dtype != FLCE_DTYPE_F32 && grad_dtype != FLCE_DTYPE_BF16) return FLCE_ERR_DTYPE;
   const int per = grad_dtype == FLCE_DTYPE_F32 ? 4 : 8;
+  const int64_t es = grad_dtype == FLCE_DTYPE_F32 ? 4 : 2;
   if (nx < 0 || nw < 0 || nx % per || nw % per) return FLCE_ERR_SHAPE;
-  if ((nx > 0 && dX == nullptr) || (nw > 0 && dW == nullptr)) return FLCE_ERR_NULL;
-  if ((nx > 0 && !aligned16(dX)) || (nw > 0 && !aligned16(dW))) return FLCE_ERR_ALIGN;
+  if ((nx > 0 && (dX == nullptr || dX_in == nullptr)) ||
+      (nw > 0 && (dW == nullptr || dW_in == nullptr)))
+    return FLCE_ERR_NULL;
+  if ((nx > 0 && (!aligned16(dX) || !aligned16(dX_in))) ||
+      (nw > 0 && (!aligned16(dW) || !aligned16(dW_in))))
+    return FLCE_ERR_ALIGN;
+  // each output is its input (in place) or lies apart from it
+  if ((nx > 0 && dX != dX_in && overlaps(dX, nx * es, dX_in, nx * es)) ||
+      (nw > 0 && dW != dW_in && overlaps(dW, nw * es, dW_in, nw * es)))
+    return FLCE_ERR_ALIAS;
   hipStream_t s = (hipStream_t)stream;
   const int f32 = grad_dtype == FLCE_DTYPE_F32;
   for (int t = 0; t < 2; ++t) {
@@ -881,7 +892,8 @@ int flce_scale_grads(void* dX, int64_t nx, void* dW, int64_t nw, int grad_dtype,
     if (chunks == 0) continue;
     const int64_t blocks = std::min<int64_t>(cdiv(chunks, 256), 8192);
     hipLaunchKernelGGL(k_scale_grads, dim3((unsigned)blocks), dim3(256), 0, s,
-                       (char*)(t == 0 ? dX : dW), chunks, f32, scale);
+                       (const char*)(t == 0 ? dX_in : dW_in), (char*)(t == 0 ? dX : dW),
+                       chunks, f32, scale);
   }
   return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }

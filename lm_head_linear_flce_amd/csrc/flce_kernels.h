@@ -1019,14 +1019,15 @@ __global__ __launch_bounds__(256) void k_lse_out(const float* __restrict__ lse_c
   if (rloss_out) rloss_out[i] = ctr->status ? __builtin_nanf("") : (k >= 0 ? rloss[k] : 0.f);
 }
 
-// dX *= s, dW *= s (s a device scalar): gradients computed with grad_scale 1
-// rescaled by the upstream gradient.  Grid-stride, 16 bytes per thread step.
-__global__ __launch_bounds__(256) void k_scale_grads(char* __restrict__ p, int64_t chunks,
-                                                     int f32, const float* __restrict__ s) {
+// out = s * in (s a device scalar; out may be in itself): gradients computed
+// with grad_scale 1, rescaled by the upstream gradient.  Grid-stride, 16
+// bytes per thread step.
+__global__ __launch_bounds__(256) void k_scale_grads(const char* src, char* dst,
+                                                     int64_t chunks, int f32,
+                                                     const float* __restrict__ s) {
   const float k = *s;
   for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < chunks; i += (int64_t)gridDim.x * 256) {
-    i32x4* q = (i32x4*)p + i;
-    i32x4 u = *q;
+    i32x4 u = ((const i32x4*)src)[i];
     if (f32) {
       f32x4 g = __builtin_bit_cast(f32x4, u);
 #pragma unroll
@@ -1037,7 +1038,7 @@ __global__ __launch_bounds__(256) void k_scale_grads(char* __restrict__ p, int64
       for (int e = 0; e < 4; ++e)
         u[e] = pack_bf16(bf2f((uint32_t)u[e] & 0xFFFFu) * k, bf2f((uint32_t)u[e] >> 16) * k);
     }
-    *q = u;
+    ((i32x4*)dst)[i] = u;
   }
 }
 

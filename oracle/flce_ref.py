@@ -333,6 +333,12 @@ def logits_bytes(N, V, elem_bytes):
 
 
 def cosine(a, b):
+    """Cosine similarity <a, b> / (|a| |b|) of the two arrays taken as flat
+    vectors, in float64: the figure the ms-swift PR, section "Mathematical
+    Equivalence", quotes for the chunked gradients against the global ones.
+    Convention for zero vectors (the pages fix none): two zero vectors are
+    identical (1.0); a zero vector against a nonzero one shares no direction
+    (0.0)."""
     a = _as_f64(a).ravel()
     b = _as_f64(b).ravel()
     na = math.sqrt(float(a @ a))

@@ -153,12 +153,16 @@ def test_chunked_host_checks(kw, code):
 
 
 @pytest.mark.parametrize("args,code", [
-    ((P, 64, 2 * P, 64, F.FLCE_DTYPE_BF16, 0, 0), F.FLCE_ERR_NULL),
-    ((P, 63, 2 * P, 64, F.FLCE_DTYPE_F32, 3 * P, 0), F.FLCE_ERR_SHAPE),
-    ((P, 64, 2 * P, 60, F.FLCE_DTYPE_BF16, 3 * P, 0), F.FLCE_ERR_SHAPE),
-    ((P, 64, 2 * P, 64, 7, 3 * P, 0), F.FLCE_ERR_DTYPE),
-    ((0, 64, 2 * P, 64, F.FLCE_DTYPE_BF16, 3 * P, 0), F.FLCE_ERR_NULL),
-    ((P + 4, 64, 2 * P, 64, F.FLCE_DTYPE_BF16, 3 * P, 0), F.FLCE_ERR_ALIGN),
+    ((P, P, 64, 2 * P, 2 * P, 64, F.FLCE_DTYPE_BF16, 0, 0), F.FLCE_ERR_NULL),
+    ((P, P, 63, 2 * P, 2 * P, 64, F.FLCE_DTYPE_F32, 3 * P, 0), F.FLCE_ERR_SHAPE),
+    ((P, P, 64, 2 * P, 2 * P, 60, F.FLCE_DTYPE_BF16, 3 * P, 0), F.FLCE_ERR_SHAPE),
+    ((P, P, 64, 2 * P, 2 * P, 64, 7, 3 * P, 0), F.FLCE_ERR_DTYPE),
+    ((0, P, 64, 2 * P, 2 * P, 64, F.FLCE_DTYPE_BF16, 3 * P, 0), F.FLCE_ERR_NULL),
+    ((P, 0, 64, 2 * P, 2 * P, 64, F.FLCE_DTYPE_BF16, 3 * P, 0), F.FLCE_ERR_NULL),
+    ((P + 4, P + 4, 64, 2 * P, 2 * P, 64, F.FLCE_DTYPE_BF16, 3 * P, 0), F.FLCE_ERR_ALIGN),
+    # an output overlapping its input without being it
+    ((P, P + 16, 64, 2 * P, 2 * P, 64, F.FLCE_DTYPE_BF16, 3 * P, 0), F.FLCE_ERR_ALIAS),
+    ((P, P, 64, 2 * P, 2 * P - 16, 64, F.FLCE_DTYPE_F32, 3 * P, 0), F.FLCE_ERR_ALIAS),
 ])
 def test_scale_grads_host_checks(args, code):
     assert F.flce_scale_grads(*args) == code

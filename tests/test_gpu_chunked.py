@@ -113,6 +113,26 @@ def test_chunked_autograd_and_grad_scale():
     assert oracle.cosine(got["dW"], ref["dW"]) >= 0.9999
 
 
+def test_chunked_autograd_second_backward():
+    """A second backward through a retained graph gets the same gradients: the
+    saved unit-scale gradients are scaled out of place, not in place."""
+    w = synth.workload("qwen2_7b_head", T=300, H=128, V=700, seed=73)
+    X, W, lab = to_device(w)
+    Xr = X.detach().clone().requires_grad_(True)
+    Wr = W.detach().clone().requires_grad_(True)
+    loss = F.linear_cross_entropy(Xr, Wr, lab, ignore_index=-100, shift=True,
+                                  reduction="mean", mode="chunked")
+    g1 = torch.autograd.grad(2.0 * loss, (Xr, Wr), retain_graph=True)
+    g2 = torch.autograd.grad(2.0 * loss, (Xr, Wr))
+    ref = oracle.flce(w.X, w.W, w.labels, shift=True, grad_scale=2.0)
+    for g in (g1, g2):
+        assert oracle.cosine(g[0].reshape(w.N, w.H).double().cpu().numpy(), ref["dX"]) >= 0.9999
+        assert oracle.cosine(g[1].double().cpu().numpy(), ref["dW"]) >= 0.9999
+        rx = np.linalg.norm(g[1].double().cpu().numpy()) / np.linalg.norm(ref["dW"])
+        assert abs(rx - 1.0) <= 1e-2
+    assert torch.equal(g1[0], g2[0]) and torch.equal(g1[1], g2[1])
+
+
 def test_chunked_no_valid_rows_and_bad_label():
     w = synth.workload("long_context", T=500, H=64, V=300, seed=101)
     w.labels[:] = -100

@@ -1,0 +1,65 @@
+"""CPU model of how the GEMM kernels hand work items to workgroups.
+
+A launch is sized from the padded row count (the host does not know the number
+of valid rows); the kernels learn it on the device and map workgroup b to an
+item XCD by XCD: the first pad8(real) workgroups cover the `real` items, each
+XCD (b % 8) taking a contiguous range of them.  These tests check, for the
+grid sizes the host code uses, that every item is computed exactly once --
+including the forward's single-range case with more than 2048 token tiles,
+whose grid once fell short of the padded item count and skipped items."""
+import pytest
+
+
+def pad8(n):
+    return (n + 7) // 8 * 8
+
+
+def xcd_item(b, nblocks):
+    return (b % 8) * (nblocks // 8) + b // 8
+
+
+def live_item(b, real):
+    real8 = pad8(real)
+    if b >= real8:
+        return -1
+    item = xcd_item(b, real8)
+    return item if item < real else -1
+
+
+def covered(grid, real):
+    items = [live_item(b, real) for b in range(grid)]
+    got = sorted(i for i in items if i >= 0)
+    return got == list(range(real))
+
+
+def fwd_grid(TT):
+    # host: fwd_items = max(2048, TT); the launch covers pad8(fwd_items)
+    return pad8(max(2048, TT))
+
+
+@pytest.mark.parametrize("TT", [1, 7, 26, 2047, 2048, 2049, 2051, 2053, 3907, 65536])
+def test_forward_items_single_range(TT):
+    # P = 1: one vocabulary range per token tile, TTn = TT when every row is valid
+    assert covered(fwd_grid(TT), TT)
+
+
+@pytest.mark.parametrize("TT,P", [(26, 9), (26, 78), (100, 20), (2051, 1), (3907, 1)])
+def test_forward_items_split(TT, P):
+    # the device picks P with P * TTn <= max(2048, TT)
+    assert P * TT <= max(2048, TT)
+    assert covered(fwd_grid(TT), P * TT)
+
+
+def test_short_grid_misses_items():
+    # the grid of fwd_items workgroups (not rounded up) leaves items out when
+    # the item count is not a multiple of 8: the case the rounding fixes
+    assert not covered(2051, 2051)
+    assert not covered(3907, 3907)
+
+
+@pytest.mark.parametrize("TT,TTn", [(26, 26), (26, 13), (32, 1), (2051, 2049)])
+@pytest.mark.parametrize("tiles_per_row", [1, 14, 64])
+def test_backward_items(TT, TTn, tiles_per_row):
+    # G / dX / dW tiles: grid pad8(kinds x TT) sized for the bound, real items
+    # over the valid rows' TTn token tiles
+    assert covered(pad8(tiles_per_row * TT), tiles_per_row * TTn)

@@ -410,3 +410,49 @@ def test_uniform_per_row_weights_equal_mean():
     r = oracle.flce(X, W, lab, reduction="none", grad_scale=np.full(X.shape[0], 0.8 / n))
     np.testing.assert_allclose(r["dX"], m["dX"], rtol=1e-12, atol=1e-15)
     np.testing.assert_allclose(r["dW"], m["dW"], rtol=1e-12, atol=1e-15)
+
+
+# --- the cosine metric every gradient-parity check uses ------------------
+
+def test_cosine_hand_values():
+    """oracle.cosine against values fixed by plane geometry, not by its own
+    formula: orthogonal, antiparallel and 45-degree vectors, invariance under
+    positive scaling and under reshaping, sign under negation, an asymmetric
+    pair (a formula that divided by |a|^2 would fail it), and the zero-vector
+    convention."""
+    assert oracle.cosine([1.0, 0.0], [0.0, 1.0]) == 0.0
+    assert oracle.cosine([1.0, 0.0], [-3.0, 0.0]) == pytest.approx(-1.0, abs=1e-15)
+    assert oracle.cosine([1.0, 0.0], [1.0, 1.0]) == pytest.approx(1.0 / math.sqrt(2.0),
+                                                                  rel=1e-15)
+    # 3-4-5 and 5-12-13 right triangles: cos = (3*5 + 4*12) / (5 * 13) = 63/65
+    assert oracle.cosine([3.0, 4.0], [5.0, 12.0]) == pytest.approx(63.0 / 65.0, rel=1e-15)
+    assert oracle.cosine([3.0, 4.0], [50.0, 120.0]) == pytest.approx(63.0 / 65.0, rel=1e-15)
+    assert oracle.cosine([-3.0, -4.0], [5.0, 12.0]) == pytest.approx(-63.0 / 65.0, rel=1e-15)
+    # the arrays are compared as flat vectors, whatever their shape
+    a = np.array([[3.0, 0.0], [0.0, 4.0]])
+    b = np.array([[5.0, 0.0], [0.0, 12.0]])
+    assert oracle.cosine(a, b) == pytest.approx(63.0 / 65.0, rel=1e-15)
+    # nearly parallel vectors: 1 - cos = 1 - 1/sqrt(1 + e^2) ~ e^2 / 2, resolved
+    e = 1e-4
+    assert 1.0 - oracle.cosine([1.0, 0.0], [1.0, e]) == pytest.approx(e * e / 2, rel=1e-6)
+    # zero vectors: identical when both are zero, no direction shared otherwise
+    assert oracle.cosine([0.0, 0.0], [0.0, 0.0]) == 1.0
+    assert oracle.cosine([0.0, 0.0], [1.0, 2.0]) == 0.0
+    assert oracle.cosine([1.0, 2.0], [0.0, 0.0]) == 0.0
+
+
+def test_cosine_detects_a_wrong_softmax_part():
+    """The gradient checks rest on the cosine telling a correct gradient from
+    one whose softmax part is missing: with the softmax term dropped the dW
+    cosine falls measurably (here below 0.9999999), and a gradient with the
+    opposite sign gives -1."""
+    X, W, lab = _problem(21, B=2, T=40, H=8, V=30, w_std=1.0)
+    r = oracle.flce(X, W, lab)
+    y, valid = oracle.targets(lab, False, -100)
+    onehot_only = np.zeros_like(r["dW"])
+    c = 1.0 / r["n_valid"]
+    for i in np.flatnonzero(valid):
+        onehot_only[y[i]] -= c * X[i]
+    assert oracle.cosine(r["dW"], onehot_only) < 0.9999999
+    assert oracle.cosine(r["dW"], -r["dW"]) == pytest.approx(-1.0, abs=1e-15)
+    assert oracle.cosine(r["dW"], 3.0 * r["dW"]) == pytest.approx(1.0, abs=1e-15)

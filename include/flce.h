@@ -65,6 +65,10 @@ extern "C" {
 #define FLCE_ERR_HIP 7         /* a HIP launch or query failed              */
 #define FLCE_ERR_LABEL_RANGE 8 /* device: a valid label outside [0, V)      */
 #define FLCE_ERR_ALIAS 9       /* an output aliases an input                */
+#define FLCE_ERR_TOO_LARGE 10  /* beyond the allocation-free scratch        */
+
+/* bytes of the device array flce_forward_noalloc uses as its scratch */
+#define FLCE_NOALLOC_SCRATCH_BYTES (160ll << 20)
 
 /* element types */
 #define FLCE_DTYPE_F32 0
@@ -118,6 +122,28 @@ int flce_forward(const void* X, const void* W, const int64_t* labels,
                  int64_t ignore_index, int reduction, int shift,
                  float* loss, float* lse, int64_t* n_valid, int32_t* status,
                  void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * flce_forward_noalloc -- flce_forward without a workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  Arguments, outputs
+ * and errors as flce_forward.  The scratch is a fixed device array inside
+ * the library, FLCE_NOALLOC_SCRATCH_BYTES (160 MiB), one copy per device,
+ * held until the process ends; its address is looked up on a device's first
+ * call.  The call allocates nothing.  A problem whose forward needs more
+ * scratch than that returns FLCE_ERR_TOO_LARGE before anything is launched.
+ * The forward needs about N * (H * es + 24) + 4 MiB bytes (es = 2 for bf16,
+ * 4 for fp32; the compacted copy of the valid rows of X dominates), so every
+ * bf16 problem with N * H <= 64M elements and N <= 2^20 fits.  All calls on
+ * one device share the array: two such calls that overlap in time on one
+ * device (two streams, or two host threads) race and must be serialised by
+ * the caller.
+ */
+int flce_forward_noalloc(const void* X, const void* W, const int64_t* labels,
+                         int64_t B, int64_t T, int64_t H, int64_t V, int dtype,
+                         int64_t ignore_index, int reduction, int shift,
+                         float* loss, float* lse, int64_t* n_valid, int32_t* status,
+                         void* stream);
 
 /*
  * flce_backward -- gradients of grad_scale * loss with respect to X and W.

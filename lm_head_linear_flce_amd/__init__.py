@@ -25,6 +25,7 @@ import os
 __all__ = [
     "FLCE_OK", "FLCE_DTYPE_F32", "FLCE_DTYPE_BF16", "FLCE_REDUCTION_MEAN",
     "FLCE_REDUCTION_SUM", "FLCE_REDUCTION_NONE", "FlceError", "flce_workspace_size", "flce_forward",
+    "flce_forward_noalloc", "FLCE_NOALLOC_SCRATCH_BYTES",
     "flce_backward", "flce_chunked_workspace_size", "flce_chunked", "flce_scale_grads",
     "flce_shard_forward", "flce_shard_merge_workspace_size", "flce_shard_merge",
     "flce_shard_backward",
@@ -44,13 +45,15 @@ FLCE_ERR_WORKSPACE = 6
 FLCE_ERR_HIP = 7
 FLCE_ERR_LABEL_RANGE = 8
 FLCE_ERR_ALIAS = 9
+FLCE_ERR_TOO_LARGE = 10
+FLCE_NOALLOC_SCRATCH_BYTES = 160 << 20
 FLCE_DTYPE_F32 = 0
 FLCE_DTYPE_BF16 = 1
 FLCE_REDUCTION_MEAN = 0
 FLCE_REDUCTION_SUM = 1
 FLCE_REDUCTION_NONE = 2
 
-EXPORTS = ("flce_workspace_size", "flce_forward", "flce_backward",
+EXPORTS = ("flce_workspace_size", "flce_forward", "flce_forward_noalloc", "flce_backward",
            "flce_shard_forward", "flce_shard_merge_workspace_size", "flce_shard_merge",
            "flce_shard_backward", "flce_chunked_workspace_size", "flce_chunked",
            "flce_scale_grads", "flce_set_timing", "flce_status_string")
@@ -80,6 +83,9 @@ def _load() -> ctypes.CDLL:
     lib.flce_forward.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, i64, i32, i32,
                                  vp, vp, vp, vp, vp, sz, vp]
     lib.flce_forward.restype = i32
+    lib.flce_forward_noalloc.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, i64, i32, i32,
+                                         vp, vp, vp, vp, vp]
+    lib.flce_forward_noalloc.restype = i32
     lib.flce_backward.argtypes = [vp, vp, vp, i64, i64, i64, i64, i32, i64, i32, i32,
                                   vp, vp, vp, vp, i32, i32, vp, vp, sz, vp]
     lib.flce_backward.restype = i32
@@ -139,6 +145,15 @@ def flce_forward(X, W, labels, B, T, H, V, dtype, ignore_index, reduction, shift
                              ignore_index, reduction, int(bool(shift)), loss or None,
                              lse or None, n_valid or None, status or None,
                              workspace or None, workspace_bytes, stream or None)
+
+
+def flce_forward_noalloc(X, W, labels, B, T, H, V, dtype, ignore_index, reduction, shift,
+                         loss, lse, n_valid, status, stream) -> int:
+    """Returns the status code (0 on success); raises nothing."""
+    return _LIB.flce_forward_noalloc(X or None, W or None, labels or None, B, T, H, V, dtype,
+                                     ignore_index, reduction, int(bool(shift)), loss or None,
+                                     lse or None, n_valid or None, status or None,
+                                     stream or None)
 
 
 def flce_backward(X, W, labels, B, T, H, V, dtype, ignore_index, reduction, shift,

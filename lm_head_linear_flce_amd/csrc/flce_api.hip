@@ -6,6 +6,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "flce.h"
 #include "flce_kernels.h"
@@ -36,6 +37,7 @@ struct Plan {
   int64_t o_ctr, o_idx, o_tgt, o_rowpos, o_xc;
   int64_t o_part, o_zt, o_bsum;            // forward region
   int64_t o_lse2, o_rs, o_g, o_dx32;       // backward region
+  int64_t fwd_total;        // bytes the forward alone uses
   int64_t total;
 };
 
@@ -115,6 +117,7 @@ int make_plan(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, Plan* p) {
   q.o_g = take(2 * q.rows_pad * q.Vb * q.es);   // two slabs, alternating blocks
   q.o_dx32 = take(4 * q.dx_split * q.rows_pad * H);
   const int64_t bwd_end = off;
+  q.fwd_total = fwd_end;
   q.total = std::max(fwd_end, bwd_end);
   *p = q;
   return FLCE_OK;
@@ -577,6 +580,43 @@ int chunked_impl(const ChunkPlan& pl, const void* X, const void* W, const int64_
   return L.err == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }
 
+// ---------------------------------------------------------------------------
+// Allocation-free forward: a file-scope device array stands in for the
+// caller's workspace.  Each device holds its own copy; its address on the
+// current device is looked up once per device (hipGetSymbolAddress) and kept.
+// ---------------------------------------------------------------------------
+constexpr int64_t kScratchBytes = FLCE_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+}  // namespace
+}  // namespace flce
+
+// the array itself: never passed to a kernel by name (on the host the name is
+// only a stand-in), only through the per-device address looked up below
+static __device__ __align__(256) char scratch[flce::kScratchBytes];
+
+namespace flce {
+namespace {
+
+// Device address of `scratch` on the current device, or an error.
+hipError_t scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  *out = g_scratch_ptr[dev];
+  return *out != nullptr ? hipSuccess : hipErrorInvalidSymbol;
+}
+
 }  // namespace
 }  // namespace flce
 
@@ -627,6 +667,41 @@ int flce_forward(const void* X, const void* W, const int64_t* labels, int64_t B,
                               shift, loss, lse, n_valid, status, nullptr, (char*)workspace, s);
   return forward_impl<F32>(p, Shard{0, V}, X, W, labels, B, T, ignore_index, reduction, shift,
                            loss, lse, n_valid, status, nullptr, (char*)workspace, s);
+}
+
+int flce_forward_noalloc(const void* X, const void* W, const int64_t* labels, int64_t B,
+                         int64_t T, int64_t H, int64_t V, int dtype, int64_t ignore_index,
+                         int reduction, int shift, float* loss, float* lse, int64_t* n_valid,
+                         int32_t* status, void* stream) {
+  if (loss == nullptr) return FLCE_ERR_NULL;
+  Plan p;
+  int rc = make_plan(B, T, H, V, dtype, &p);
+  if (rc != FLCE_OK) return rc;
+  if (reduction != FLCE_REDUCTION_MEAN && reduction != FLCE_REDUCTION_SUM &&
+      reduction != FLCE_REDUCTION_NONE)
+    return FLCE_ERR_REDUCTION;
+  if (p.fwd_total > kScratchBytes) return FLCE_ERR_TOO_LARGE;
+  hipStream_t s = (hipStream_t)stream;
+  if (p.N == 0) {
+    hipLaunchKernelGGL(k_empty, dim3(1), dim3(1), 0, s,
+                       reduction == FLCE_REDUCTION_NONE ? (float*)nullptr : loss, n_valid,
+                       status);
+    return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
+  }
+  if (X == nullptr || W == nullptr || labels == nullptr || lse == nullptr)
+    return FLCE_ERR_NULL;
+  if (!aligned16(X) || !aligned16(W) || ((uintptr_t)labels & 7u) ||
+      ((uintptr_t)lse & 3u) || ((uintptr_t)loss & 3u))
+    return FLCE_ERR_ALIGN;
+  void* ws = nullptr;
+  if (scratch_address(&ws) != hipSuccess) return FLCE_ERR_HIP;
+  // every byte of the forward's region that a kernel reads is written earlier
+  // in the same call, so the array's previous contents never matter
+  if (dtype == FLCE_DTYPE_BF16)
+    return forward_impl<BF16>(p, Shard{0, V}, X, W, labels, B, T, ignore_index, reduction,
+                              shift, loss, lse, n_valid, status, nullptr, (char*)ws, s);
+  return forward_impl<F32>(p, Shard{0, V}, X, W, labels, B, T, ignore_index, reduction, shift,
+                           loss, lse, n_valid, status, nullptr, (char*)ws, s);
 }
 
 int flce_backward(const void* X, const void* W, const int64_t* labels, int64_t B,
@@ -924,6 +999,8 @@ const char* flce_status_string(int code) {
     case FLCE_ERR_HIP: return "a HIP launch failed";
     case FLCE_ERR_LABEL_RANGE: return "a label is neither ignore_index nor in [0, V)";
     case FLCE_ERR_ALIAS: return "an output buffer overlaps an input buffer";
+    case FLCE_ERR_TOO_LARGE:
+      return "the problem needs more scratch than the allocation-free entry point holds";
     default: return "unknown status code";
   }
 }

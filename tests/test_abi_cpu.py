@@ -36,7 +36,7 @@ def test_header_constants_match_binding():
 
 
 def test_status_strings():
-    for code in range(0, 10):
+    for code in range(0, 11):
         s = F.flce_status_string(code)
         assert s and s != "unknown status code"
     assert F.flce_status_string(1234) == "unknown status code"
@@ -244,3 +244,45 @@ def test_shard_merge_host_checks():
         a = dict(args)
         a.update(kw)
         assert F.flce_shard_merge(*a.values()) == code
+
+
+def fwd_noalloc(**kw):
+    a = dict(X=P, W=2 * P, labels=3 * P, B=1, T=16, H=128, V=50, dtype=F.FLCE_DTYPE_BF16,
+             ignore_index=-100, reduction=F.FLCE_REDUCTION_MEAN, shift=0, loss=4 * P,
+             lse=5 * P, n_valid=0, status=0, stream=0)
+    a.update(kw)
+    return F.flce_forward_noalloc(*a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(X=0), F.FLCE_ERR_NULL), (dict(loss=0), F.FLCE_ERR_NULL),
+    (dict(lse=0), F.FLCE_ERR_NULL), (dict(H=100), F.FLCE_ERR_ALIGN),
+    (dict(W=2 * P + 8), F.FLCE_ERR_ALIGN), (dict(dtype=3), F.FLCE_ERR_DTYPE),
+    (dict(reduction=3), F.FLCE_ERR_REDUCTION), (dict(V=0), F.FLCE_ERR_SHAPE),
+    # the forward of these needs more than the fixed scratch array holds
+    (dict(B=1, T=32768, H=4096), F.FLCE_ERR_TOO_LARGE),
+    (dict(B=2, T=1 << 20, H=64), F.FLCE_ERR_TOO_LARGE),
+    (dict(B=1, T=65536, H=2048, dtype=F.FLCE_DTYPE_F32), F.FLCE_ERR_TOO_LARGE),
+])
+def test_forward_noalloc_host_checks(kw, code):
+    assert fwd_noalloc(**kw) == code
+
+
+@pytest.mark.parametrize("B,T,H,V,dt", [
+    (1, 8192, 3584, 152064, F.FLCE_DTYPE_BF16), (2, 8192, 4096, 151936, F.FLCE_DTYPE_BF16),
+    (1, 32768, 2048, 152064, F.FLCE_DTYPE_BF16), (1, 4099, 1024, 262147, F.FLCE_DTYPE_BF16),
+    (2, 64, 256, 4096, F.FLCE_DTYPE_F32), (1, 1 << 20, 64, 1000, F.FLCE_DTYPE_BF16),
+])
+def test_forward_noalloc_fits_the_workloads(B, T, H, V, dt):
+    # the stated bound: N * (H * es + 24) + 4 MiB <= the array's 160 MiB
+    es = 2 if dt == F.FLCE_DTYPE_BF16 else 4
+    assert B * T * (H * es + 24) + (4 << 20) <= F.FLCE_NOALLOC_SCRATCH_BYTES
+    assert F.FLCE_NOALLOC_SCRATCH_BYTES == 160 << 20
+    # NULL X passes the size check and fails the pointer check after it
+    assert fwd_noalloc(B=B, T=T, H=H, V=V, dtype=dt, X=0) == F.FLCE_ERR_NULL
+
+
+def test_noalloc_scratch_constant_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define FLCE_NOALLOC_SCRATCH_BYTES \((\d+)ll << (\d+)\)", text)
+    assert m and (int(m.group(1)) << int(m.group(2))) == F.FLCE_NOALLOC_SCRATCH_BYTES

@@ -88,9 +88,10 @@ extern "C" {
  * Host-only arithmetic, no HIP call.  The figure is the engine's whole extra
  * device memory: it grows linearly in N (per-row indices, a compacted copy of
  * the valid rows of X, FP32 dX accumulators -- one, or up to eight vocabulary
- * parts when few hidden x row tiles would leave compute units idle -- and two
- * bounded slabs of softmax gradients, each covering a fixed vocabulary
- * block), never with N*V.
+ * parts when few hidden x row tiles would leave compute units idle -- FP32
+ * per-target row sums for the one-hot part of dW, and two bounded slabs of
+ * softmax gradients, each covering a fixed vocabulary block), plus 4 bytes
+ * per vocabulary entry; never with N*V.
  *   B, T, H, V : problem sizes (B*T = N rows)
  *   dtype      : FLCE_DTYPE_*
  *   bytes      : out, host pointer

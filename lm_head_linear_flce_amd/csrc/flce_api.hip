@@ -25,6 +25,11 @@ constexpr int64_t kMaxI32 = 0x7FFFFFFFll;
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 int64_t cdiv(int64_t x, int64_t m) { return (x + m - 1) / m; }
+int64_t pow2_at_least(int64_t x) {
+  int64_t p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
 
 // Problem geometry shared by the size query and the two calls.
 struct Plan {
@@ -37,6 +42,8 @@ struct Plan {
   int64_t o_ctr, o_idx, o_tgt, o_rowpos, o_xc;
   int64_t o_part, o_zt, o_bsum;            // forward region
   int64_t o_lse2, o_rs, o_g, o_dx32;       // backward region
+  int64_t P;                               // sort length: rows_pad rounded up to 2^k
+  int64_t o_keys, o_oh, o_map;             // one-hot sums for dW (backward)
   int64_t fwd_total;        // bytes the forward alone uses
   int64_t total;
 };
@@ -116,6 +123,10 @@ int make_plan(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, Plan* p) {
   q.o_rs = take(4 * q.rows_pad);
   q.o_g = take(2 * q.rows_pad * q.Vb * q.es);   // two slabs, alternating blocks
   q.o_dx32 = take(4 * q.dx_split * q.rows_pad * H);
+  q.P = pow2_at_least(q.rows_pad);
+  q.o_keys = take(8 * q.P);
+  q.o_oh = take(4 * q.rows_pad * H);
+  q.o_map = take(4 * V);
   const int64_t bwd_end = off;
   q.fwd_total = fwd_end;
   q.total = std::max(fwd_end, bwd_end);
@@ -250,6 +261,39 @@ int forward_impl(const Plan& pl, const Shard& sh, const void* X, const void* W,
   return L.err == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }
 
+// One-hot sums for the dW tiles (k_oh_*): sort the compacted rows by
+// (target, row), sum each target's rows of c_k Xc in that order.
+template <class E>
+void onehot_sums(int64_t P, int64_t rows_pad, int64_t H, int64_t V_local, const int* tgt,
+                 const Counters* ctr, const char* xc, const float* rs, uint64_t* keys,
+                 float* oh, int* map, Launch& L) {
+  hipStream_t s = L.s;
+  const int64_t fill = std::max(P, V_local);
+  hipLaunchKernelGGL(k_oh_keys, dim3((unsigned)std::min<int64_t>(cdiv(fill, 256), 8192)),
+                     dim3(256), 0, s, tgt, ctr, (int)V_local, (int)P, keys, map);
+  L.check();
+  hipLaunchKernelGGL(k_bsort_local, dim3((unsigned)std::max<int64_t>(1, P / kSortLocal)),
+                     dim3(1024), 0, s, keys, (int)P);
+  L.check();
+  for (int64_t st = 2 * kSortLocal; st <= P; st <<= 1) {
+    for (int64_t stride = st / 2; stride >= kSortLocal; stride >>= 1) {
+      hipLaunchKernelGGL(k_bsort_global, dim3((unsigned)cdiv(P / 2, 256)), dim3(256), 0, s,
+                         keys, (int)P, (int)st, (int)stride);
+      L.check();
+    }
+    hipLaunchKernelGGL(k_bsort_merge, dim3((unsigned)(P / kSortLocal)), dim3(1024), 0, s, keys,
+                       (int)st);
+    L.check();
+  }
+  const dim3 grid((unsigned)(rows_pad / kOhBlock), (unsigned)cdiv(H, 256));
+  hipLaunchKernelGGL(k_oh_partial<E>, grid, dim3(256), 0, s, (const uint64_t*)keys, xc,
+                     (int)H, ctr, rs, oh);
+  L.check();
+  hipLaunchKernelGGL(k_oh_final, grid, dim3(256), 0, s, (const uint64_t*)keys, (int)H,
+                     (int)rows_pad, oh, map);
+  L.check();
+}
+
 template <class E>
 int backward_impl(const Plan& pl, const Shard& sh, const void* X, const void* W,
                   const int64_t* labels, int64_t B, int64_t T, int64_t ignore_index,
@@ -282,12 +326,20 @@ int backward_impl(const Plan& pl, const Shard& sh, const void* X, const void* W,
                      (int64_t)pl.rows_pad * pl.H, grad_scale, rs);
   L.check();
 
+  float* oh = (float*)(ws + pl.o_oh);
+  int* oh_map = (int*)(ws + pl.o_map);
+  onehot_sums<E>(pl.P, pl.rows_pad, pl.H, pl.V, tgt, ctr, xc, rs, (uint64_t*)(ws + pl.o_keys),
+                 oh, oh_map, L);
+
   BwdArgs a;
   a.W = (const char*)W;
   a.Xc = xc;
   a.G = g;
   a.lse2 = lse2;
   a.rs = rs;
+  a.oh = oh;
+  a.oh_map = oh_map;
+  a.oh_rows = rows_pad;
   a.tgt = tgt;
   a.dx32 = dx32;
   a.dx32p = dx32 + (int64_t)pl.rows_pad * pl.H;
@@ -315,7 +367,7 @@ int backward_impl(const Plan& pl, const Shard& sh, const void* X, const void* W,
   };
   if (L.err == hipSuccess) L.err = allow_big_lds(k_bwd<E>);
   // launch b + 1 runs the dX / dW tiles of block b and the G tiles of block
-  // b + 1 (dX first: its tiles are the longest)
+  // b + 1
   const int64_t nblk = cdiv(pl.V, pl.Vb);
   // the dW tiles' K loop runs over the rows (bounded by rows_pad), the dX
   // tiles' over a part of the block: the longer kind starts first
@@ -332,15 +384,12 @@ int backward_impl(const Plan& pl, const Shard& sh, const void* X, const void* W,
                          kLdsBytes, stream, cur, nxt, nb_dx, nb_dw, nb_g, dw_first);
       L.check();
     }
-    if (b + 1 < nblk) {
-      hipLaunchKernelGGL(k_fixup<E>, dim3((unsigned)cdiv(rows_pad, 256)), dim3(256), 0,
-                         stream, nxt);
-      L.check();
-    }
   }
-  hipLaunchKernelGGL(k_dx_final, dim3((unsigned)cdiv(pl.N, 4)), dim3(256), 0, stream,
+  hipLaunchKernelGGL(k_dx_final<E>, dim3((unsigned)cdiv(pl.N, 4)), dim3(256), 0, stream,
                      (const float*)dx32, (int)pl.dx_split, (int64_t)pl.rows_pad * pl.H,
-                     (const int*)rowpos, (int)pl.N, (int)pl.H, (char*)dX, dx_f32);
+                     (const int*)rowpos, (int)pl.N, (int)pl.H, (char*)dX, dx_f32,
+                     (const char*)W, (const int*)tgt, (int)pl.V, (const Counters*)ctr,
+                     (const float*)rs);
   L.check();
   return L.err == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }
@@ -376,6 +425,7 @@ struct ChunkPlan {
   int64_t o_ctr, o_idx, o_tgt, o_rowpos, o_xc, o_zt, o_lse_c, o_lse2, o_rloss, o_bsum, o_cctr;
   int64_t o_rs;
   int64_t o_part, o_slab, o_dx32, o_dx32p;
+  int64_t P, o_keys, o_oh, o_map;   // one-hot sums for dW
   int64_t total;
 };
 
@@ -433,6 +483,10 @@ int make_chunk_plan(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, int64
   // the extra vocabulary parts of dX cover one chunk's rows; they are folded
   // into the main FP32 sum after each chunk
   q.o_dx32p = take(4 * (q.dx_split - 1) * q.C * H);
+  q.P = pow2_at_least(q.rows_pad);
+  q.o_keys = take(8 * q.P);
+  q.o_oh = take(4 * q.rows_pad * H);
+  q.o_map = take(4 * V);
   q.total = off;
   *p = q;
   return FLCE_OK;
@@ -479,6 +533,10 @@ int chunked_impl(const ChunkPlan& pl, const void* X, const void* W, const int64_
                      (const char*)xc, (const char*)W, (int)pl.H, (const int*)tgt,
                      (const Counters*)ctr, zt, (int)pl.V);
   L.check();
+  float* oh = (float*)(ws + pl.o_oh);
+  int* oh_map = (int*)(ws + pl.o_map);
+  onehot_sums<E>(pl.P, pl.rows_pad, pl.H, pl.V, tgt, ctr, xc, rs, (uint64_t*)(ws + pl.o_keys),
+                 oh, oh_map, L);
   if (L.err == hipSuccess) L.err = allow_big_lds(k_chunk_z<E>);
   if (L.err == hipSuccess) L.err = allow_big_lds(k_bwd<E>);
   for (int64_t ch = 0; ch < pl.nchunks && L.err == hipSuccess; ++ch) {
@@ -540,6 +598,10 @@ int chunked_impl(const ChunkPlan& pl, const void* X, const void* W, const int64_
     b.HT = HT;
     b.dw_f32 = grad_f32;
     b.dw_acc = ch > 0 || dw_acc;
+    // the one-hot part of dW (all rows) goes in with the first chunk's tiles
+    b.oh = ch == 0 ? oh : nullptr;
+    b.oh_map = oh_map;
+    b.oh_rows = rows_pad;
     for (int64_t v0 = 0; v0 < pl.V && L.err == hipSuccess; v0 += pl.VB) {
       b.v0 = (int)v0;
       b.vb = (int)std::min<int64_t>(pl.VB, pl.V - v0);
@@ -573,9 +635,10 @@ int chunked_impl(const ChunkPlan& pl, const void* X, const void* W, const int64_
   hipLaunchKernelGGL(k_loss, dim3(1), dim3(256), 0, stream, (const float*)bsum, (int)pl.TT,
                      (const Counters*)ctr, reduction, none ? (float*)nullptr : loss, n_valid);
   L.check();
-  hipLaunchKernelGGL(k_dx_final, dim3((unsigned)cdiv(pl.N, 4)), dim3(256), 0, stream,
+  hipLaunchKernelGGL(k_dx_final<E>, dim3((unsigned)cdiv(pl.N, 4)), dim3(256), 0, stream,
                      (const float*)dx32, 1, (int64_t)0, (const int*)rowpos, (int)pl.N,
-                     (int)pl.H, (char*)dX, grad_f32);
+                     (int)pl.H, (char*)dX, grad_f32, (const char*)W, (const int*)tgt,
+                     (int)pl.V, (const Counters*)ctr, (const float*)rs);
   L.check();
   return L.err == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }

@@ -434,6 +434,9 @@ struct BwdArgs {
   int TT, HT, VTb;     // token tiles (bound), hidden tiles, block vocab tiles
   int dw_f32;          // dW written as fp32 (else bf16)
   int dw_acc;          // dW tiles add to dW (else overwrite it)
+  const float* oh;     // [oh_rows, H] one-hot sums (see k_oh_*) or NULL: dW
+  const int* oh_map;   //   tiles then take off oh[oh_map[v]] for each column v
+  int oh_rows;         //   (all compacted rows, also where rows_pad is a chunk's)
 };
 
 // G = c * 2^(z*log2e - lse2) for one tile, stored as G[token][vocab].
@@ -527,34 +530,16 @@ __device__ __forceinline__ void g_tile(const BwdArgs& a, int b, lds_t* smem) {
                      vlim - wm * 128 - 4 * (lane >> 5), n - tau * kTile, smem);
 }
 
-// The one-hot part of G: G[k, y_k - v0] -= c for targets inside the block.
-template <class E>
-__global__ __launch_bounds__(256) void k_fixup(BwdArgs a) {
-  const int k = blockIdx.x * 256 + threadIdx.x;
-  if (k >= a.ctr->n) return;
-  const int y = a.tgt[k] - a.v0;
-  if (y < 0 || y >= a.vb) return;
-  const float c = a.rs ? a.ctr->c * a.rs[k] : a.ctr->c;
-  const int64_t off = (int64_t)k * a.Vb + y;
-  if constexpr (E::kBytes == 2) {
-    uint16_t* g = (uint16_t*)a.G + off;
-    *g = (uint16_t)f2bf(bf2f(*g) - c);
-  } else {
-    float* g = (float*)a.G + off;
-    *g = *g - c;
-  }
-}
-
 // dW tile in the output dtype: accumulator rows are hidden indices (4
 // consecutive per lane and register group), columns vocabulary entries of the
 // block.  kMasked: columns >= mlim lie past the block, rows >= hlim past H
 // (H % 8 == 0, so a group of 4 is either inside or outside).  Branch-free:
 // a masked lane stores to an offset past the descriptor's range, which the
 // hardware drops (the descriptor covers the tile's 256 rows, < 2^31 bytes).
-template <bool kMasked>
+template <bool kMasked, class Corr>
 __device__ __forceinline__ void dw_store(const BwdArgs& a, const f32x16 (&acc)[4][4],
                                          int vt, int ht, int wm, int wn, int lane,
-                                         int mlim, int hlim, lds_t* smem) {
+                                         int mlim, int hlim, lds_t* smem, const Corr& corr) {
   const int es = a.dw_f32 ? 4 : 2;
   const int64_t row0 = (int64_t)(a.v0 + vt * kTile) * a.H + (int64_t)ht * kTile;
   const int64_t left = ((int64_t)a.V * a.H - row0) * es;
@@ -576,7 +561,8 @@ __device__ __forceinline__ void dw_store(const BwdArgs& a, const f32x16 (&acc)[4
           [&](int o, int x0, f32x4 v) {
             __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), wr, off(o, x0),
                                                    0, 0);
-          });
+          },
+          corr);
     } else {
       rmw_quarter_f32(
           smem + wave * 32768, lane, acc,
@@ -590,7 +576,8 @@ __device__ __forceinline__ void dw_store(const BwdArgs& a, const f32x16 (&acc)[4
             pk[0] = pack_bf16(v[0], v[1]);
             pk[1] = pack_bf16(v[2], v[3]);
             __builtin_amdgcn_raw_buffer_store_b64(pk, wr, off(o, x0), 0, 0);
-          });
+          },
+          corr);
     }
     return;
   }
@@ -604,7 +591,8 @@ __device__ __forceinline__ void dw_store(const BwdArgs& a, const f32x16 (&acc)[4
           const bool ok = !kMasked || (m < mlim && h < hlim);
           __builtin_amdgcn_raw_buffer_store_b128(v, wr, ok ? (m * a.H + h) * 2 : (int)0x80000000u,
                                                  0, 0);
-        });
+        },
+        corr);
     return;
   }
 #pragma unroll
@@ -617,13 +605,57 @@ __device__ __forceinline__ void dw_store(const BwdArgs& a, const f32x16 (&acc)[4
         const int hc = acc_row(wm, i, 4 * g, lane);
         const bool ok = !kMasked || (mc < mlim && hc < hlim);
         const int off = ok ? (mc * a.H + hc) * 4 : (int)0x80000000u;
-        const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                         acc[i][j][4 * g + 3]};
+        const f32x4 cv = corr(i, j, g);
+        const f32x4 v = {acc[i][j][4 * g] - cv[0], acc[i][j][4 * g + 1] - cv[1],
+                         acc[i][j][4 * g + 2] - cv[2], acc[i][j][4 * g + 3] - cv[3]};
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), wr, off, 0, 0);
       }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
+
+// The one-hot part of a dW tile, taken off in FP32 before the tile's one
+// rounding: column m (vocabulary entry v0 + vt * 256 + m of this call's W)
+// loses oh[oh_map[v]] when some valid row has that target.  corr(i, j, g) is
+// the f32x4 for accumulator registers (i, j, 4 g .. 4 g + 3): hidden rows
+// acc_row(wm, i, 4 g, lane) .. + 3 of column acc_col(wn, j, lane), one
+// 16-byte load.  Column blocks without any target in the wave cost nothing
+// (a wave-uniform test); lanes without one read past the buffer (zeros).
+struct OneHotDW {
+  rsrc_t ohr;
+  int idx[4];
+  unsigned any;      // bit j: some lane of the wave has a target in block j
+  int H, hbase, wm, lane, hlim;
+  // the map lookups, issued before the tile's K loop so that they arrive
+  // under it
+  template <class A>
+  __device__ __forceinline__ static void lookup(const A& a, int vt, int wn, int lane, int mlim,
+                                                int (&idx)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int m = acc_col(wn, j, lane);
+      idx[j] = a.oh != nullptr && m < mlim ? a.oh_map[a.v0 + vt * kTile + m] : -1;
+    }
+  }
+  template <class A>
+  __device__ __forceinline__ OneHotDW(const A& a, const int (&idx_)[4], int ht, int wm_,
+                                      int lane_, int hlim_)
+      : H(a.H), hbase(ht * kTile), wm(wm_), lane(lane_), hlim(hlim_) {
+    any = 0;
+    ohr = make_rsrc(a.oh, a.oh != nullptr ? (int64_t)a.oh_rows * a.H * 4 : 0);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      idx[j] = idx_[j];
+      if (__ballot(idx[j] >= 0) != 0) any |= 1u << j;
+    }
+  }
+  __device__ __forceinline__ f32x4 operator()(int i, int j, int g) const {
+    if (!(any & (1u << j))) return f32x4{0.f, 0.f, 0.f, 0.f};
+    const int hr = acc_row(wm, i, 4 * g, lane);
+    const int off = idx[j] >= 0 && hr < hlim ? (idx[j] * H + hbase + hr) * 4 : (int)0x80000000u;
+    return __builtin_bit_cast(f32x4, bload128(ohr, off));
+  }
+};
 
 // dW[v0 + m, h] = sum_k Xc[k, h] G[k, m] for one (hidden tile, vocabulary
 // tile) of the block: A = Xc, B = G, both stored with K (rows) outer; K runs
@@ -650,13 +682,17 @@ __device__ __forceinline__ void dw_tile(const BwdArgs& a, int b, lds_t* smem) {
   B.bytes = (int64_t)a.rows_pad * a.Vb * es - (int64_t)vt * kTile * es;
   B.ldb = a.Vb * es;
   B.kbytes = 0;
+  const int mlim = a.vb - vt * kTile, hlim = a.H - ht * kTile;
+  int ohidx[4];
+  OneHotDW::lookup(a, vt, wn, lane, mlim, ohidx);
   f32x16 acc[4][4];
   zero_acc(acc);
   gemm_tile<E, LoadMN<E>, LoadMN<E>>(A, B, steps, smem, wm, wn, acc);
 
-  const int mlim = a.vb - vt * kTile, hlim = a.H - ht * kTile;
-  if (mlim >= kTile && hlim >= kTile) dw_store<false>(a, acc, vt, ht, wm, wn, lane, 0, 0, smem);
-  else dw_store<true>(a, acc, vt, ht, wm, wn, lane, mlim, hlim, smem);
+  const OneHotDW corr(a, ohidx, ht, wm, lane, hlim);
+  if (mlim >= kTile && hlim >= kTile)
+    dw_store<false>(a, acc, vt, ht, wm, wn, lane, 0, 0, smem, corr);
+  else dw_store<true>(a, acc, vt, ht, wm, wn, lane, mlim, hlim, smem, corr);
 }
 
 // dX32 += tile, read-modify-write: each (token tile, hidden tile) belongs to
@@ -769,7 +805,7 @@ void k_bwd(BwdArgs cur, BwdArgs nxt, int nb_dx, int nb_dw, int nb_g, int dw_firs
 //                  s = sum 2^(z log2e - M); the slab gets e = 2^(z log2e - M)
 //   k_chunk_lse    the rows' lse from the partials, row losses, the chunk's
 //                  counters (rows in the chunk)
-//   k_chunk_scale  G = c e 2^(M - lse2) - c [v = y], in place
+//   k_chunk_scale  G = c e 2^(M - lse2), in place
 //   k_bwd          dX and dW tiles per vocabulary block of the slab (dW added
 //                  to the previous chunks' sum)
 // ---------------------------------------------------------------------------
@@ -948,7 +984,8 @@ __global__ __launch_bounds__(256) void k_block_sums(const float* __restrict__ rl
   if (threadIdx.x == 0) bsum[blockIdx.x] = red[0];
 }
 
-// G = c e 2^(M - lse2) - c [v = y] for one 16-byte piece u of the slab (row
+// G = c e 2^(M - lse2) (the softmax part; the one-hot part is added in FP32
+// to the gradient sums) for one 16-byte piece u of the slab (row
 // kl of the chunk, columns v .. v + 16 / es - 1); rows from the chunk's row
 // count up to the next multiple of 64 (the last K step of the dW tiles) become
 // zero.
@@ -959,7 +996,6 @@ __device__ __forceinline__ i32x4 scale_piece(const ChunkArgs& a, int kl, int v, 
   const int k = a.row0 + kl;
   const float c = a.rs ? a.ctr->c * a.rs[k] : a.ctr->c;
   const float f = c * exp2f(a.part[(int64_t)kl * (2 * a.VT) + (v >> 7)].x - a.lse2[k]);
-  const int y = a.tgt[k] - v;
   if constexpr (E::kBytes == 2) {
     float g[8];
 #pragma unroll
@@ -967,18 +1003,12 @@ __device__ __forceinline__ i32x4 scale_piece(const ChunkArgs& a, int kl, int v, 
       g[2 * q] = bf2f((uint32_t)u[q] & 0xFFFFu) * f;
       g[2 * q + 1] = bf2f((uint32_t)u[q] >> 16) * f;
     }
-#pragma unroll
-    for (int q = 0; q < 8; ++q)
-      if (y == q) g[q] -= c;
     return i32x4{pack_bf16(g[0], g[1]), pack_bf16(g[2], g[3]), pack_bf16(g[4], g[5]),
                  pack_bf16(g[6], g[7])};
   } else {
     f32x4 g = __builtin_bit_cast(f32x4, u);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      g[q] *= f;
-      if (y == q) g[q] -= c;
-    }
+    for (int q = 0; q < 4; ++q) g[q] *= f;
     return __builtin_bit_cast(i32x4, g);
   }
 }
@@ -1077,22 +1107,44 @@ __global__ __launch_bounds__(256) void k_shard_merge(
   if (threadIdx.x == 0) blocksum[blockIdx.x] = red[0];
 }
 
+// dX = round(dX32 - c_k W[y_k]) scattered to the original rows (0 for
+// ignored rows): the softmax part summed in FP32 over the vocabulary (and
+// over its vocabulary parts, in part order) and the one-hot part, added in
+// FP32 before the one rounding.  Targets outside [0, V_local) (another
+// vocabulary shard's) have no one-hot term here.  One wave per row.
+template <class E>
 __global__ __launch_bounds__(256) void k_dx_final(
     const float* __restrict__ dx32, int dx_split, int64_t dx_stride,
-    const int* __restrict__ rowpos, int N, int H, char* __restrict__ dX, int out_f32) {
+    const int* __restrict__ rowpos, int N, int H, char* __restrict__ dX, int out_f32,
+    const char* __restrict__ W, const int* __restrict__ tgt, int V_local,
+    const Counters* __restrict__ ctr, const float* __restrict__ rs) {
   const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (i >= N) return;
   const int k = rowpos[i];
+  const int y = k >= 0 ? tgt[k] : -1;
+  const bool hot = y >= 0 && y < V_local;
+  const float ck = k >= 0 ? (rs ? ctr->c * rs[k] : ctr->c) : 0.f;
   const int groups = H >> 2;  // 4 values per lane step
   for (int g = lane; g < groups; g += 64) {
     f32x4 v = {0.f, 0.f, 0.f, 0.f};
     if (k >= 0) {
-      // the vocabulary parts' FP32 sums, added in part order
       v = *(const f32x4*)(dx32 + (int64_t)k * H + 4 * g);
       for (int sp = 1; sp < dx_split; ++sp) {
         const f32x4 u = *(const f32x4*)(dx32 + sp * dx_stride + (int64_t)k * H + 4 * g);
         v = f32x4{v[0] + u[0], v[1] + u[1], v[2] + u[2], v[3] + u[3]};
+      }
+      if (hot) {
+        f32x4 wv;
+        if constexpr (E::kBytes == 2) {
+          const i32x2 u = *(const i32x2*)(W + ((int64_t)y * H + 4 * g) * 2);
+          wv = f32x4{bf2f((uint32_t)u[0] & 0xFFFFu), bf2f((uint32_t)u[0] >> 16),
+                     bf2f((uint32_t)u[1] & 0xFFFFu), bf2f((uint32_t)u[1] >> 16)};
+        } else {
+          wv = *(const f32x4*)(W + ((int64_t)y * H + 4 * g) * 4);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = fmaf(-ck, wv[e], v[e]);
       }
     }
     if (out_f32) {
@@ -1104,6 +1156,192 @@ __global__ __launch_bounds__(256) void k_dx_final(
       *(i32x2*)((uint16_t*)dX + (int64_t)i * H + 4 * g) = pk;
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// One-hot sums for dW: OH_v = sum over valid rows k with y_k = v of c_k Xc[k]
+// (FP32), one row per target value that occurs, summed in row order.  The
+// compacted rows are sorted by the unique 64-bit key (target << 32 | row), so
+// the order of every sum is fixed; runs of equal targets are summed position
+// by position (per 256-position block, then across blocks in order).
+// ---------------------------------------------------------------------------
+
+constexpr uint64_t kNoKey = ~0ull;
+
+// keys[i] for i < P (a power of two): compacted rows k < n with a target in
+// [0, V_local); everything else sorts last.  Also map[v] = -1 for v < V_local.
+__global__ __launch_bounds__(256) void k_oh_keys(const int* __restrict__ tgt,
+                                                 const Counters* __restrict__ ctr, int V_local,
+                                                 int P, uint64_t* __restrict__ keys,
+                                                 int* __restrict__ map) {
+  const int n = ctr->n;
+  const int total = P > V_local ? P : V_local;
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < total; i += gridDim.x * 256) {
+    if (i < P) {
+      uint64_t key = kNoKey;
+      if (i < n) {
+        const int y = tgt[i];
+        if (y >= 0 && y < V_local) key = ((uint64_t)(uint32_t)y << 32) | (uint32_t)i;
+      }
+      keys[i] = key;
+    }
+    if (i < V_local) map[i] = -1;
+  }
+}
+
+// Bitonic compare-exchange of positions i < j = i + stride: ascending where
+// bit `s` of i is clear (the stage of sequences of length s).
+__device__ __forceinline__ void bitonic_pair(uint64_t& a, uint64_t& b, int i, int s) {
+  const bool up = (i & s) == 0;
+  if ((a > b) == up) {
+    const uint64_t t = a;
+    a = b;
+    b = t;
+  }
+}
+
+// Sorts each block of kSortLocal keys (the whole array when P is no larger)
+// in LDS: stages 2 .. min(P, kSortLocal), directions by global position.
+constexpr int kSortLocal = 2048;
+__global__ __launch_bounds__(1024) void k_bsort_local(uint64_t* __restrict__ keys, int P) {
+  __shared__ uint64_t sk[kSortLocal];
+  const int len = P < kSortLocal ? P : kSortLocal;
+  const int base = blockIdx.x * kSortLocal;
+  for (int t = threadIdx.x; t < len; t += 1024) sk[t] = keys[base + t];
+  __syncthreads();
+  for (int s = 2; s <= len; s <<= 1)
+    for (int stride = s >> 1; stride > 0; stride >>= 1) {
+      for (int t = threadIdx.x; t < len / 2; t += 1024) {
+        const int i = (t / stride) * 2 * stride + t % stride;
+        bitonic_pair(sk[i], sk[i + stride], base + i, s);
+      }
+      __syncthreads();
+    }
+  for (int t = threadIdx.x; t < len; t += 1024) keys[base + t] = sk[t];
+}
+
+// One stride (>= kSortLocal) of stage s over the whole array: thread t
+// handles one pair.
+__global__ __launch_bounds__(256) void k_bsort_global(uint64_t* __restrict__ keys, int P, int s,
+                                                      int stride) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= P / 2) return;
+  const int i = (t / stride) * 2 * stride + t % stride;
+  uint64_t a = keys[i], b = keys[i + stride];
+  bitonic_pair(a, b, i, s);
+  keys[i] = a;
+  keys[i + stride] = b;
+}
+
+// Strides kSortLocal / 2 .. 1 of stage s (> kSortLocal) inside each block
+// of kSortLocal keys.
+__global__ __launch_bounds__(1024) void k_bsort_merge(uint64_t* __restrict__ keys, int s) {
+  __shared__ uint64_t sk[kSortLocal];
+  const int base = blockIdx.x * kSortLocal;
+  for (int t = threadIdx.x; t < kSortLocal; t += 1024) sk[t] = keys[base + t];
+  __syncthreads();
+  for (int stride = kSortLocal / 2; stride > 0; stride >>= 1) {
+    for (int t = threadIdx.x; t < kSortLocal / 2; t += 1024) {
+      const int i = (t / stride) * 2 * stride + t % stride;
+      bitonic_pair(sk[i], sk[i + stride], base + i, s);
+    }
+    __syncthreads();
+  }
+  for (int t = threadIdx.x; t < kSortLocal; t += 1024) keys[base + t] = sk[t];
+}
+
+// Per block of kOhBlock sorted positions and hidden chunk of 256 (one thread
+// per hidden column): for every position that opens a run inside the block
+// (the block's first position, or a target different from the previous one),
+// ohp[pos] = sum over the run's positions in this block of c_k Xc[k], in
+// position order.  Short blocks keep the sequential chains short; runs that
+// cross blocks are completed by k_oh_final.
+constexpr int kOhBlock = 64;
+template <class E>
+__global__ __launch_bounds__(256) void k_oh_partial(const uint64_t* __restrict__ keys,
+                                                    const char* __restrict__ Xc, int H,
+                                                    const Counters* __restrict__ ctr,
+                                                    const float* __restrict__ rs,
+                                                    float* __restrict__ ohp) {
+  __shared__ uint64_t sk[kOhBlock + 1];
+  __shared__ float sc[kOhBlock];
+  const int base = blockIdx.x * kOhBlock;
+  const float c = ctr->c;
+  if (threadIdx.x < kOhBlock) {
+    const uint64_t key = keys[base + threadIdx.x];
+    sk[threadIdx.x] = key;
+    sc[threadIdx.x] = key == kNoKey ? 0.f : (rs ? c * rs[(uint32_t)key] : c);
+  }
+  if (threadIdx.x == 0) sk[kOhBlock] = kNoKey;
+  __syncthreads();
+  const int h = blockIdx.y * 256 + threadIdx.x;
+  if (h >= H || sk[0] == kNoKey) return;
+  float x[kOhBlock];
+#pragma unroll
+  for (int q = 0; q < kOhBlock; ++q) {
+    const uint64_t key = sk[q];
+    const int64_t row = key == kNoKey ? 0 : (int64_t)(uint32_t)key;
+    if constexpr (E::kBytes == 2)
+      x[q] = bf2f(((const uint16_t*)Xc)[row * H + h]);
+    else
+      x[q] = ((const float*)Xc)[row * H + h];
+  }
+  float acc = 0.f;
+  int start = 0;
+#pragma unroll
+  for (int q = 0; q < kOhBlock; ++q) {
+    const uint64_t key = sk[q];
+    if (key != kNoKey) {
+      acc = fmaf(sc[q], x[q], acc);
+      const uint64_t next = sk[q + 1];
+      if (q == kOhBlock - 1 || next == kNoKey || (next >> 32) != (key >> 32)) {
+        ohp[(int64_t)(base + start) * H + h] = acc;
+        acc = 0.f;
+        start = q + 1;
+      }
+    }
+  }
+}
+
+// Runs that cross kOhBlock-position blocks.  Every real run start (the first
+// position, or a target different from the previous position's) records
+// map[target] = its position.  The run holding a block's last position, when
+// it starts inside the block, is completed by that block: the partials that
+// the following blocks' first positions hold for the same target are added to
+// its own, in block order.  Grid: blocks of kOhBlock positions x hidden
+// chunks of 256.
+__device__ __forceinline__ uint32_t key_target(uint64_t k) { return (uint32_t)(k >> 32); }
+
+__global__ __launch_bounds__(256) void k_oh_final(const uint64_t* __restrict__ keys, int H,
+                                                  int rows_pad, float* __restrict__ ohp,
+                                                  int* __restrict__ map) {
+  __shared__ int open_at;
+  const int base = blockIdx.x * kOhBlock;
+  const int t = threadIdx.x;
+  const uint64_t key = t < kOhBlock ? keys[base + t] : kNoKey;
+  const bool prev_same = t < kOhBlock && base + t > 0 && keys[base + t - 1] != kNoKey &&
+                         key_target(keys[base + t - 1]) == key_target(key);
+  const bool real = key != kNoKey && !prev_same;
+  if (blockIdx.y == 0 && real) map[key_target(key)] = base + t;
+  if (t == 0) open_at = -1;
+  __syncthreads();
+  const uint64_t klast = keys[base + kOhBlock - 1];
+  // the real start of the run that holds the block's last position
+  if (real && klast != kNoKey && key_target(klast) == key_target(key)) open_at = t;
+  __syncthreads();
+  const int i0 = open_at;
+  const int h = blockIdx.y * 256 + t;
+  if (i0 < 0 || h >= H) return;
+  const uint32_t tg = key_target(klast);
+  float sum = ohp[(int64_t)(base + i0) * H + h];
+  for (int b = base + kOhBlock; b < rows_pad; b += kOhBlock) {
+    const uint64_t k0 = keys[b];
+    if (k0 == kNoKey || key_target(k0) != tg) break;
+    sum += ohp[(int64_t)b * H + h];
+    const uint64_t k1 = keys[b + kOhBlock - 1];
+    if (k1 == kNoKey || key_target(k1) != tg) break;
+  }
+  ohp[(int64_t)(base + i0) * H + h] = sum;
 }
 
 // dst[k, :] += sum over p = 0 .. parts - 1 of src_p[k, :] (src_p = src + p *

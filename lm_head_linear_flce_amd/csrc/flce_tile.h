@@ -500,24 +500,43 @@ __device__ __forceinline__ int acc_col(int wn, int j, int lane) {
 //   emit(o, x0, v)          store chunk v (8 bf16, inner x0 .. x0 + 7) of row o
 // The region must be free (after the K loop's last barrier) and only this
 // wave touches it, so no barrier is needed between the two phases.
-template <class Val, class Emit>
+// corr(i, j, g) -> f32x4   subtracted from the values of registers (i, j,
+//                          4 g .. 4 g + 3) before the rounding (NoCorr4: none)
+struct NoCorr4 {
+  __device__ __forceinline__ f32x4 operator()(int, int, int) const {
+    return f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+};
+
+template <class Val, class Emit, class Corr>
 __device__ __forceinline__ void store_quarter_bf16(lds_t* region, int lane, Val&& val,
-                                                   Emit&& emit) {
+                                                   Emit&& emit, Corr&& corr) {
   typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
   typedef __attribute__((address_space(3))) i32x4 lds_i32x4;
+  // the corrections of column block j + 1 are fetched while block j is packed
+  f32x4 cur[16], nxt[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) cur[q] = corr(q >> 2, 0, q & 3);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int o = 32 * j + (lane & 31);
+    if (j + 1 < 4) {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) nxt[q] = corr(q >> 2, j + 1, q & 3);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int u = 8 * i + 2 * g + (lane >> 5);
+        const f32x4 cv = cur[4 * i + g];
         i32x2 pk;
-        pk[0] = pack_bf16(val(i, j, 4 * g), val(i, j, 4 * g + 1));
-        pk[1] = pack_bf16(val(i, j, 4 * g + 2), val(i, j, 4 * g + 3));
+        pk[0] = pack_bf16(val(i, j, 4 * g) - cv[0], val(i, j, 4 * g + 1) - cv[1]);
+        pk[1] = pack_bf16(val(i, j, 4 * g + 2) - cv[2], val(i, j, 4 * g + 3) - cv[3]);
         *(lds_i32x2*)(region + o * 256 + ((u ^ (o & 31)) << 3)) = pk;
       }
+#pragma unroll
+    for (int q = 0; q < 16; ++q) cur[q] = nxt[q];
   }
   const int c = lane & 15;
 #pragma unroll
@@ -529,15 +548,21 @@ __device__ __forceinline__ void store_quarter_bf16(lds_t* region, int lane, Val&
   }
 }
 
+template <class Val, class Emit>
+__device__ __forceinline__ void store_quarter_bf16(lds_t* region, int lane, Val&& val,
+                                                   Emit&& emit) {
+  store_quarter_bf16(region, lane, val, emit, NoCorr4{});
+}
+
 // fp32 counterpart for read-modify-write epilogues: the same quarter, in two
 // halves of 64 rows (j = 0, 1 then j = 2, 3) of 512 B each, 16-byte unit u of
 // row o kept at u ^ (o % 32).  For every 16-byte chunk (4 fp32, inner x0 ..
 // x0 + 3) of row o, `load(o, x0)` fetches the old value (all of a half's
 // loads are issued before its LDS traffic) and `store(o, x0, v)` writes v.
-template <class Load, class Store>
+template <class Load, class Store, class Corr>
 __device__ __forceinline__ void rmw_quarter_f32(lds_t* region, int lane,
                                                 const f32x16 (&acc)[4][4], Load&& load,
-                                                Store&& store) {
+                                                Store&& store, Corr&& corr) {
   typedef __attribute__((address_space(3))) i32x4 lds_i32x4;
   const int c = lane & 31;
 #pragma unroll
@@ -553,8 +578,9 @@ __device__ __forceinline__ void rmw_quarter_f32(lds_t* region, int lane,
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int u = 8 * i + 2 * g + (lane >> 5);
-          const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
-                           acc[i][j][4 * g + 3]};
+          const f32x4 cv = corr(i, j, g);
+          const f32x4 v = {acc[i][j][4 * g] - cv[0], acc[i][j][4 * g + 1] - cv[1],
+                           acc[i][j][4 * g + 2] - cv[2], acc[i][j][4 * g + 3] - cv[3]};
           *(lds_i32x4*)(region + o * 512 + ((u ^ (o & 31)) << 4)) = __builtin_bit_cast(i32x4, v);
         }
     }
@@ -567,6 +593,13 @@ __device__ __forceinline__ void rmw_quarter_f32(lds_t* region, int lane,
                                       old[t][3] + v[3]});
     }
   }
+}
+
+template <class Load, class Store>
+__device__ __forceinline__ void rmw_quarter_f32(lds_t* region, int lane,
+                                                const f32x16 (&acc)[4][4], Load&& load,
+                                                Store&& store) {
+  rmw_quarter_f32(region, lane, acc, load, store, NoCorr4{});
 }
 
 // Maps a launch index to a work item so that items i, i+1, ... run on the same

@@ -175,8 +175,10 @@ def test_chunked_workspace_is_bounded_by_the_chunk():
     w1 = F.flce_chunked_workspace_size(1, 8192, H, V, F.FLCE_DTYPE_BF16)
     w2 = F.flce_chunked_workspace_size(1, 32768, H, V, F.FLCE_DTYPE_BF16)
     per_row = (w2 - w1) / (32768 - 8192)
-    assert per_row < 4 * H + 2 * H + 64      # dX32 + X copy + a few words per row
-    assert w1 < (1 << 30) + 8192 * (6 * H + 64) + 2 * 3 * 8 * 594 * 3328 + (4 << 20)
+    # per row: FP32 dX sum, compacted X copy, FP32 one-hot sum row for dW,
+    # and a few words (sort key, indices, lse)
+    assert per_row < 4 * H + 2 * H + 4 * H + 64
+    assert w1 < (1 << 30) + 8192 * (10 * H + 64) + 2 * 3 * 8 * 594 * 3328 + (4 << 20) + 4 * V
     assert w2 < 32768 * V * 2                # far below the logits
 
 

@@ -14,7 +14,7 @@ import torch
 import lm_head_linear_flce_amd as F
 import oracle
 import synth
-from gpu_util import DEV, check, run, soft_parts, soft_tolerance, to_device
+from gpu_util import DEV, check, run, run_chunked, soft_parts, soft_tolerance, to_device
 
 pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -194,12 +194,12 @@ def test_zero_weight_gives_log_vocab():
 
 def test_peak_memory_never_holds_logits():
     # the device memory a call takes beyond its inputs is the caller's
-    # workspace plus the outputs; the workspace is linear in N and does not
-    # grow with V (the gradient slabs are a fixed budget); at this shape the
-    # logits would be 4.3 GB
+    # workspace plus the outputs; the workspace is linear in N and grows with
+    # V only by the 4-byte vocabulary-to-one-hot-row map (the gradient slabs
+    # are a fixed budget); at this shape the logits would be 4.3 GB
     w = synth.workload("long_context", T=8192, H=128, V=262144, seed=151)
     ws_v = [F.flce_workspace_size(w.B, w.T, w.H, v, F.FLCE_DTYPE_BF16) for v in (w.V, 4 * w.V)]
-    assert ws_v[0] == ws_v[1], ws_v
+    assert 0 <= ws_v[1] - ws_v[0] <= 4 * (3 * w.V) + 256, ws_v
     X, W, lab = to_device(w)
     torch.cuda.synchronize()
     torch.cuda.reset_peak_memory_stats()
@@ -307,3 +307,31 @@ def test_dW_accumulates_over_micro_batches(mode, grad_dtype):
     assert np.abs(got - want).max() <= 1e-2 * np.abs(want).max()
     gx = dX.reshape(wb.N, wb.H).double().cpu().numpy()
     assert oracle.cosine(gx, refs[1]["dX"]) >= 0.9999
+
+
+@pytest.mark.parametrize("mode", ["recompute", "chunked"])
+def test_one_target_over_many_rows(mode):
+    """Most rows share one target, so that target's rows span many
+    256-position blocks of the sorted (target, row) order and its one-hot sum
+    for dW is carried across blocks; the others are spread over the
+    vocabulary.  dW and dX against the oracle, plus the softmax parts."""
+    w = synth.make_workload("skewed", B=1, T=3000, H=136, V=777, dtype="bf16", seed=4242,
+                            labels="uniform", mask="count", mask_arg=300, shift=False,
+                            reduction="mean")
+    rng = np.random.default_rng(5)
+    lab = w.labels.reshape(-1)
+    hot = rng.random(lab.shape) < 0.6
+    lab[hot & (lab != w.ignore_index)] = 5
+    print(f"[skewed] {mode} N={w.N} H={w.H} V={w.V}", flush=True)
+    ref = oracle.flce(w.X, w.W, w.labels, ignore_index=w.ignore_index, reduction=w.reduction,
+                      shift=w.shift, mode="global")
+    got = run(w) if mode == "recompute" else run_chunked(w, chunk_rows=512)
+    check(w, got, ref, what=f"skewed {mode}")
+    g32 = run(w, grad_dtype=torch.float32) if mode == "recompute" else \
+        run_chunked(w, grad_dtype=torch.float32, chunk_rows=512)
+    sx, sw = soft_parts(w, g32["dX"], g32["dW"], ref["n_valid"])
+    rx, rw = soft_parts(w, ref["dX"], ref["dW"], ref["n_valid"])
+    cmin, ntol = soft_tolerance(w)
+    for name, a, b in (("dX", sx, rx), ("dW", sw, rw)):
+        assert oracle.cosine(a, b) >= cmin, name
+        assert abs(np.linalg.norm(a) / np.linalg.norm(b) - 1.0) <= ntol, name

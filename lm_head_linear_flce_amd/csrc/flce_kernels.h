@@ -16,11 +16,12 @@
 // Backward (dX, dW), over vocabulary blocks [v0, v0 + vb), as tiles of k_bwd:
 //   G tiles     logits recomputed on MFMA, G = c * exp(z - lse) stored (bf16 or
 //               fp32) into a bounded [rows x block] slab (two, alternating)
-//   k_fixup     G[k, y_k - v0] -= c for targets inside the block
-//   dW tiles    dW[v0 + m, :] = sum_k G[k, m] Xc[k, :]   (complete, stored once)
+//   dW tiles    dW[v0 + m, :] = sum_k G[k, m] Xc[k, :] - OH[v0 + m]
+//               (complete, stored once; OH: the one-hot part, k_oh_*)
 //   dX tiles    dX32[k, :] += sum_m G[k, m] W[v0 + m, :] (FP32)
 // one launch runs the dX and dW tiles of block b with the G tiles of block
-// b + 1; k_dx_final rounds dX32 once and scatters it to the original rows.
+// b + 1; k_dx_final takes off the one-hot part c_k W[y_k], rounds dX32 once
+// and scatters it to the original rows.
 #pragma once
 
 #include "flce_tile.h"

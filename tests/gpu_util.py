@@ -79,6 +79,34 @@ def check(w, got, ref, dx_rows=None, dw_rows=None, what=""):
     return out
 
 
+def check_sampled_rows(w, got, e, what=""):
+    """Each stored row on its own: cosine >= 0.999 and max-abs error within
+    1e-2 of the row's largest value.  A dW row of a vocabulary entry that no
+    row targets is pure softmax part, so a wrong vocabulary block or tile
+    edge shows here even where the whole-sample cosine would hide it."""
+    for name, rows, ref in (("dX", e["dx_rows"], e["dx"]), ("dW", e["dw_rows"], e["dw"])):
+        g = got[name][rows]
+        for q, r in enumerate(rows):
+            a, b = g[q], ref[q].astype(np.float64)
+            if not np.any(b):
+                assert not np.any(a), f"{what} {name} row {r}"
+                continue
+            cos = oracle.cosine(a, b)
+            assert cos >= 0.999, f"{what} {name} row {r} cosine {cos}"
+            err = np.abs(a - b).max() / np.abs(b).max()
+            assert err <= 1e-2, f"{what} {name} row {r} max-abs {err}"
+
+
+def check_block_coverage(w, e):
+    """Every vocabulary block of both backward widths stored with e holds at
+    least two sampled dW rows (its first and last column)."""
+    rows = set(int(r) for r in e["dw_rows"])
+    for wdt in (int(x) for x in e["block_widths"]):
+        for b0 in range(0, w.V, wdt):
+            b1 = min(b0 + wdt, w.V) - 1
+            assert b0 in rows and b1 in rows, (wdt, b0, b1)
+
+
 def soft_parts(w, dX, dW, n):
     """The softmax parts of the gradients, P W and P^T X, rebuilt from dX and
     dW by removing the one-hot term: dX_i / c + W_{y_i} and dW / c + the sum

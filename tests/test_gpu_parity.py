@@ -14,7 +14,8 @@ import torch
 import lm_head_linear_flce_amd as F
 import oracle
 import synth
-from gpu_util import DEV, check, run, run_chunked, soft_parts, soft_tolerance, to_device
+from gpu_util import (DEV, check, check_block_coverage, check_sampled_rows, run,
+                      run_chunked, soft_parts, soft_tolerance, to_device)
 
 pytestmark = pytest.mark.gpu
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -265,6 +266,8 @@ def test_full_size_against_stored_oracle(name):
     ref = dict(n_valid=int(e["n_valid"]), loss=float(e["loss"]), lse=e["lse"],
                dX=e["dx"], dW=e["dw"])
     check(w, got, ref, dx_rows=e["dx_rows"], dw_rows=e["dw_rows"], what=name)
+    check_block_coverage(w, e)
+    check_sampled_rows(w, got, e, what=name)
     # invariants on the whole outputs
     _, valid = oracle.targets(w.labels, w.shift, w.ignore_index)
     assert np.all(got["dX"][~valid] == 0.0)

@@ -294,6 +294,27 @@ int flce_scale_grads(const void* dX_in, void* dX, int64_t nx, const void* dW_in,
                      int64_t nw, int grad_dtype, const float* scale, void* stream);
 
 /*
+ * flce_convert_grads -- dst = round(*scale * src (+ dst)) for FP32 gradient
+ * sums src [n] (flce_chunked's or flce_backward's with grad_dtype =
+ * FLCE_DTYPE_F32), with exactly one rounding to dst_dtype (FLCE_DTYPE_BF16,
+ * round-to-nearest-even; FLCE_DTYPE_F32: none).  This is how a bf16 caller
+ * of the chunked mode gets dW summed over all row chunks in FP32 and rounded
+ * once, as item 2 of Megatron-LM PR "[Dev] Fix Linear-Cross-Entropy
+ * Convergence Issue" prescribes for the gradient sums, and how an upstream
+ * gradient is applied to FP32 sums before that one rounding.
+ *   src [n]      : float32, device
+ *   dst [n]      : dst_dtype, device; must not overlap src
+ *   n            : element count, a multiple of 4
+ *   scale        : float32 scalar, device, or NULL (= 1)
+ *   accumulate   : 1 = the values dst already holds are added (in FP32,
+ *                  before the rounding); 0 = dst is overwritten
+ *   stream       : hipStream_t
+ * Buffers 16-byte aligned.
+ */
+int flce_convert_grads(const float* src, void* dst, int64_t n, int dst_dtype,
+                       const float* scale, int accumulate, void* stream);
+
+/*
  * flce_set_timing -- measurement hook for benchmarks and profilers.  While set,
  * every launch of the kernel named `kernel` ("k_fwd_lse", the forward GEMM;
  * "k_bwd", the backward GEMM launches; "k_chunk_z" and "k_chunk_dxdw", the

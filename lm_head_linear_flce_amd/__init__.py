@@ -27,6 +27,7 @@ __all__ = [
     "FLCE_REDUCTION_SUM", "FLCE_REDUCTION_NONE", "FlceError", "flce_workspace_size", "flce_forward",
     "flce_forward_noalloc", "FLCE_NOALLOC_SCRATCH_BYTES",
     "flce_backward", "flce_chunked_workspace_size", "flce_chunked", "flce_scale_grads",
+    "flce_convert_grads",
     "flce_shard_forward", "flce_shard_merge_workspace_size", "flce_shard_merge",
     "flce_shard_backward",
     "flce_set_timing", "flce_status_string", "linear_cross_entropy", "library_path",
@@ -56,7 +57,7 @@ FLCE_REDUCTION_NONE = 2
 EXPORTS = ("flce_workspace_size", "flce_forward", "flce_forward_noalloc", "flce_backward",
            "flce_shard_forward", "flce_shard_merge_workspace_size", "flce_shard_merge",
            "flce_shard_backward", "flce_chunked_workspace_size", "flce_chunked",
-           "flce_scale_grads", "flce_set_timing", "flce_status_string")
+           "flce_scale_grads", "flce_convert_grads", "flce_set_timing", "flce_status_string")
 
 
 class FlceError(RuntimeError):
@@ -108,6 +109,8 @@ def _load() -> ctypes.CDLL:
     lib.flce_chunked.restype = i32
     lib.flce_scale_grads.argtypes = [vp, vp, i64, vp, vp, i64, i32, vp, vp]
     lib.flce_scale_grads.restype = i32
+    lib.flce_convert_grads.argtypes = [vp, vp, i64, i32, vp, i32, vp]
+    lib.flce_convert_grads.restype = i32
     lib.flce_set_timing.argtypes = [ctypes.c_char_p, vp, i32, ctypes.POINTER(i32)]
     lib.flce_set_timing.restype = i32
     lib.flce_status_string.argtypes = [i32]
@@ -232,6 +235,12 @@ def flce_scale_grads(dX_in, dX, nx, dW_in, dW, nw, grad_dtype, scale, stream) ->
     """Returns the status code (0 on success); raises nothing."""
     return _LIB.flce_scale_grads(dX_in or None, dX or None, nx, dW_in or None, dW or None, nw,
                                  grad_dtype, scale or None, stream or None)
+
+
+def flce_convert_grads(src, dst, n, dst_dtype, scale, accumulate, stream) -> int:
+    """Returns the status code (0 on success); raises nothing."""
+    return _LIB.flce_convert_grads(src or None, dst or None, n, dst_dtype, scale or None,
+                                   int(bool(accumulate)), stream or None)
 
 
 def flce_set_timing(kernel, events, capacity, count) -> int:
@@ -477,17 +486,38 @@ def chunked_workspace(B, T, H, V, dtype_code, device, chunk_rows=0):
     return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device), nbytes
 
 
+def _convert(src, dst, accumulate=False, scale=None):
+    """dst = round(scale * src (+ dst)) through flce_convert_grads."""
+    rc = flce_convert_grads(src.data_ptr(), dst.data_ptr(), src.numel(), _dtype_code(dst),
+                            0 if scale is None else scale.data_ptr(), accumulate,
+                            _stream_handle(src.device))
+    if rc != FLCE_OK:
+        raise FlceError(rc, "flce_convert_grads")
+
+
 def chunked(hidden, weight, labels, grad_scale=None, ignore_index=-100, shift=False,
             reduction="mean", grad_dtype=None, ws=None, chunk_rows=0, dW=None,
-            accumulate=False):
+            accumulate=False, round_once=False):
     """(loss, lse, n_valid, dX, dW, status) from one flce_chunked call; a
     caller-provided ws must come from chunked_workspace with the same
-    chunk_rows."""
+    chunk_rows.  round_once=True with bf16 gradients keeps dX and dW in FP32
+    over all row chunks (flce_chunked with FP32 outputs) and rounds them once
+    (flce_convert_grads), at the price of FP32 temporaries; otherwise a bf16
+    dW is rounded once per row chunk."""
     torch = _torch()
     _check_tensors(hidden, weight, labels)
     B, T, H, V = _shape(hidden, weight, labels)
     dt = _dtype_code(hidden)
     gd = dt if grad_dtype is None else _dtype_code(torch.empty(0, dtype=grad_dtype))
+    if round_once and gd == FLCE_DTYPE_BF16:
+        loss, lse, n_valid, dX32, dW32, status = chunked(
+            hidden, weight, labels, grad_scale, ignore_index, shift, reduction,
+            torch.float32, ws, chunk_rows)
+        dX = torch.empty(hidden.shape, dtype=hidden.dtype, device=hidden.device)
+        _convert(dX32, dX)
+        dW = _dw_out(dW, weight, hidden.dtype, accumulate)
+        _convert(dW32, dW, accumulate=accumulate)
+        return loss, lse, n_valid, dX, dW, status
     out_dtype = torch.float32 if gd == FLCE_DTYPE_F32 else hidden.dtype
     dev = hidden.device
     if ws is None:
@@ -539,30 +569,29 @@ def _autograd_function():
             return dX, dW, None, None, None, None
 
     class LinearCrossEntropyChunked(torch.autograd.Function):
-        """Gradients formed in the forward (flce_chunked, grad_scale 1), scaled
-        by the upstream gradient in the backward (flce_scale_grads)."""
+        """Gradients formed in the forward (flce_chunked, grad_scale 1, FP32
+        sums over all row chunks), scaled by the upstream gradient and
+        rounded once to the input dtype in the backward (flce_convert_grads,
+        out of place: a second backward through a retained graph scales the
+        saved sums afresh)."""
 
         @staticmethod
         def forward(ctx, hidden, weight, labels, ignore_index, shift, reduction):
             loss, _, _, dX, dW, _ = chunked(hidden, weight, labels,
                                             ignore_index=ignore_index, shift=shift,
-                                            reduction=reduction)
+                                            reduction=reduction, grad_dtype=torch.float32)
             ctx.save_for_backward(dX, dW)
+            ctx.out_dtype = hidden.dtype
             return loss
 
         @staticmethod
         def backward(ctx, grad_out):
             dX, dW = ctx.saved_tensors
             g = grad_out.reshape(()).to(dtype=torch.float32).contiguous()
-            gd = _dtype_code(dX)
-            # out of place: the saved gradients stay unscaled, so a second
-            # backward (retain_graph=True) scales them afresh
-            gX, gW = torch.empty_like(dX), torch.empty_like(dW)
-            rc = flce_scale_grads(dX.data_ptr(), gX.data_ptr(), dX.numel(), dW.data_ptr(),
-                                  gW.data_ptr(), dW.numel(), gd, g.data_ptr(),
-                                  _stream_handle(dX.device))
-            if rc != FLCE_OK:
-                raise FlceError(rc, "flce_scale_grads")
+            gX = torch.empty(dX.shape, dtype=ctx.out_dtype, device=dX.device)
+            gW = torch.empty(dW.shape, dtype=ctx.out_dtype, device=dW.device)
+            _convert(dX, gX, scale=g)
+            _convert(dW, gW, scale=g)
             return gX, gW, None, None, None, None
 
     return LinearCrossEntropy, LinearCrossEntropyChunked

@@ -141,10 +141,23 @@ bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
   return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
 }
 
-template <class K>
-hipError_t allow_big_lds(K kernel) {
-  return hipFuncSetAttribute((const void*)kernel,
-                             hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+// The GEMM kernels take 128 KiB of dynamic LDS.  The limit is raised once per
+// kernel, device and process (the attribute belongs to the kernel, not to a
+// call), so that calls made under stream capture issue no attribute changes.
+constexpr int kAttrDevices = 64;
+template <auto Kernel>
+hipError_t allow_big_lds() {
+  static std::once_flag once[kAttrDevices];
+  static hipError_t err[kAttrDevices];
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kAttrDevices) return hipErrorInvalidDevice;
+  std::call_once(once[dev], [dev] {
+    err[dev] = hipFuncSetAttribute((const void*)Kernel,
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+  });
+  return err[dev];
 }
 
 // Launch bookkeeping: the first failing launch is remembered.
@@ -241,7 +254,7 @@ int forward_impl(const Plan& pl, const Shard& sh, const void* X, const void* W,
   fa.VT = (int)pl.VT;
   fa.ctr = ctr;
   fa.part = part;
-  if (L.err == hipSuccess) L.err = allow_big_lds(k_fwd_lse<E>);
+  if (L.err == hipSuccess) L.err = allow_big_lds<k_fwd_lse<E>>();
   {
     Timed t("k_fwd_lse", stream);
     // k_fwd_lse hands its items out XCD by XCD over the first pad8(P * TTn)
@@ -365,7 +378,7 @@ int backward_impl(const Plan& pl, const Shard& sh, const void* X, const void* W,
     r.G = g + (b & 1) * slab;
     return r;
   };
-  if (L.err == hipSuccess) L.err = allow_big_lds(k_bwd<E>);
+  if (L.err == hipSuccess) L.err = allow_big_lds<k_bwd<E>>();
   // launch b + 1 runs the dX / dW tiles of block b and the G tiles of block
   // b + 1
   const int64_t nblk = cdiv(pl.V, pl.Vb);
@@ -537,8 +550,8 @@ int chunked_impl(const ChunkPlan& pl, const void* X, const void* W, const int64_
   int* oh_map = (int*)(ws + pl.o_map);
   onehot_sums<E>(pl.P, pl.rows_pad, pl.H, pl.V, tgt, ctr, xc, rs, (uint64_t*)(ws + pl.o_keys),
                  oh, oh_map, L);
-  if (L.err == hipSuccess) L.err = allow_big_lds(k_chunk_z<E>);
-  if (L.err == hipSuccess) L.err = allow_big_lds(k_bwd<E>);
+  if (L.err == hipSuccess) L.err = allow_big_lds<k_chunk_z<E>>();
+  if (L.err == hipSuccess) L.err = allow_big_lds<k_bwd<E>>();
   for (int64_t ch = 0; ch < pl.nchunks && L.err == hipSuccess; ++ch) {
     ChunkArgs ca;
     ca.W = (const char*)W;
@@ -1033,6 +1046,23 @@ int flce_scale_grads(const void* dX_in, void* dX, int64_t nx, const void* dW_in,
                        (const char*)(t == 0 ? dX_in : dW_in), (char*)(t == 0 ? dX : dW),
                        chunks, f32, scale);
   }
+  return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
+}
+
+int flce_convert_grads(const float* src, void* dst, int64_t n, int dst_dtype,
+                       const float* scale, int accumulate, void* stream) {
+  if (dst_dtype != FLCE_DTYPE_F32 && dst_dtype != FLCE_DTYPE_BF16) return FLCE_ERR_DTYPE;
+  if (n < 0 || n % 4) return FLCE_ERR_SHAPE;
+  if (n == 0) return FLCE_OK;
+  if (src == nullptr || dst == nullptr) return FLCE_ERR_NULL;
+  if (!aligned16(src) || !aligned16(dst)) return FLCE_ERR_ALIGN;
+  const int64_t des = dst_dtype == FLCE_DTYPE_F32 ? 4 : 2;
+  if (overlaps(src, n * 4, dst, n * des)) return FLCE_ERR_ALIAS;
+  const int64_t chunks = n / 4;
+  const int64_t blocks = std::min<int64_t>(cdiv(chunks, 256), 8192);
+  hipLaunchKernelGGL(k_convert_grads, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                     src, (char*)dst, chunks, dst_dtype == FLCE_DTYPE_F32 ? 1 : 0, scale,
+                     accumulate ? 1 : 0);
   return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }
 

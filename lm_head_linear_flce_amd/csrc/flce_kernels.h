@@ -1073,6 +1073,40 @@ __global__ __launch_bounds__(256) void k_scale_grads(const char* src, char* dst,
   }
 }
 
+// dst = round(s * src (+ dst)) from FP32 gradient sums, 4 values per thread
+// step: one rounding to bf16 (or none for fp32), the caller's values added in
+// FP32 first when `accumulate`.  s = *scale, or 1 with no scale.
+__global__ __launch_bounds__(256) void k_convert_grads(const float* __restrict__ src,
+                                                       char* __restrict__ dst, int64_t chunks,
+                                                       int dst_f32, const float* __restrict__ scale,
+                                                       int accumulate) {
+  const float k = scale ? *scale : 1.0f;
+  for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < chunks; i += (int64_t)gridDim.x * 256) {
+    f32x4 v = *(const f32x4*)(src + 4 * i);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] *= k;
+    if (dst_f32) {
+      f32x4* d = (f32x4*)dst + i;
+      if (accumulate) {
+        const f32x4 o = *d;
+        v = f32x4{v[0] + o[0], v[1] + o[1], v[2] + o[2], v[3] + o[3]};
+      }
+      *d = v;
+    } else {
+      i32x2* d = (i32x2*)dst + i;
+      if (accumulate) {
+        const i32x2 o = *d;
+        v = f32x4{v[0] + bf2f((uint32_t)o[0] & 0xFFFFu), v[1] + bf2f((uint32_t)o[0] >> 16),
+                  v[2] + bf2f((uint32_t)o[1] & 0xFFFFu), v[3] + bf2f((uint32_t)o[1] >> 16)};
+      }
+      i32x2 pk;
+      pk[0] = pack_bf16(v[0], v[1]);
+      pk[1] = pack_bf16(v[2], v[3]);
+      *d = pk;
+    }
+  }
+}
+
 // Vocabulary shards: row i's lse is the log-sum-exp of the shards' lse and its
 // target logit the sum of the shards' (exactly one holds it); one thread per
 // original row, fixed-order block sums of the row losses.

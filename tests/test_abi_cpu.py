@@ -288,3 +288,17 @@ def test_noalloc_scratch_constant_matches_header():
     text = open(HEADER).read()
     m = re.search(r"#define FLCE_NOALLOC_SCRATCH_BYTES \((\d+)ll << (\d+)\)", text)
     assert m and (int(m.group(1)) << int(m.group(2))) == F.FLCE_NOALLOC_SCRATCH_BYTES
+
+
+@pytest.mark.parametrize("args,code", [
+    ((P, 2 * P, 64, 9, 0, 0, 0), F.FLCE_ERR_DTYPE),
+    ((P, 2 * P, 62, F.FLCE_DTYPE_BF16, 0, 0, 0), F.FLCE_ERR_SHAPE),
+    ((P, 2 * P, -4, F.FLCE_DTYPE_BF16, 0, 0, 0), F.FLCE_ERR_SHAPE),
+    ((0, 2 * P, 64, F.FLCE_DTYPE_BF16, 0, 0, 0), F.FLCE_ERR_NULL),
+    ((P, 0, 64, F.FLCE_DTYPE_F32, 0, 0, 0), F.FLCE_ERR_NULL),
+    ((P + 4, 2 * P, 64, F.FLCE_DTYPE_BF16, 0, 0, 0), F.FLCE_ERR_ALIGN),
+    ((P, P + 128, 64, F.FLCE_DTYPE_BF16, 0, 0, 0), F.FLCE_ERR_ALIAS),
+    ((P, 2 * P, 0, F.FLCE_DTYPE_BF16, 0, 0, 0), F.FLCE_OK),     # nothing to do
+])
+def test_convert_grads_host_checks(args, code):
+    assert F.flce_convert_grads(*args) == code

@@ -30,6 +30,8 @@ int64_t pow2_at_least(int64_t x) {
   while (p < x) p <<= 1;
   return p;
 }
+// per-block counts of the prep kernels: two ints per 1024 rows
+int64_t prep_blk_bytes(int64_t N) { return 8 * cdiv(N > 0 ? N : 1, kPrepBlock); }
 
 // Problem geometry shared by the size query and the two calls.
 struct Plan {
@@ -39,7 +41,7 @@ struct Plan {
   int64_t Vb;               // backward vocabulary block (multiple of 256)
   int64_t dx_split;         // dX tiles per (token tile, hidden tile) and block
   // workspace offsets (bytes)
-  int64_t o_ctr, o_idx, o_tgt, o_rowpos, o_xc;
+  int64_t o_ctr, o_idx, o_tgt, o_rowpos, o_xc, o_blk;
   int64_t o_part, o_zt, o_bsum;            // forward region
   int64_t o_lse2, o_rs, o_g, o_dx32;       // backward region
   int64_t P;                               // sort length: rows_pad rounded up to 2^k
@@ -84,7 +86,7 @@ int make_plan(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, Plan* p) {
   q.rows_pad = round_up(N > 0 ? N : 1, kTile);
   q.TT = q.rows_pad / kTile;
   q.VT = cdiv(V, kTile);
-  // forward: the split itself is chosen on the device (k_prep), once the
+  // forward: the split itself is chosen on the device (k_prep_scan), once the
   // number of valid rows is known; this bounds its item count and partials
   q.fwd_items = std::max<int64_t>(2048, q.TT);
   // backward: the vocabulary block is as wide as the slab budget allows for
@@ -98,8 +100,7 @@ int make_plan(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, Plan* p) {
   q.Vb = vb;
   q.dx_split = dx_split_for(cdiv(H, kTile), q.TT, FLCE_DX_TILES);
   // 32-bit offsets inside the kernels
-  if (q.rows_pad * q.Vb * q.es > kMaxI32 || q.rows_pad * H * 4 > kMaxI32 ||
-      (int64_t)kTile * H * q.es * 2 > kMaxI32)
+  if (q.rows_pad * q.Vb * q.es > kMaxI32 || (int64_t)kTile * H * q.es * 2 > kMaxI32)
     return FLCE_ERR_SHAPE;
 
   int64_t off = 0;
@@ -113,6 +114,7 @@ int make_plan(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, Plan* p) {
   q.o_tgt = take(4 * q.rows_pad);
   q.o_rowpos = take(4 * q.rows_pad);
   q.o_xc = take(q.rows_pad * H * q.es);
+  q.o_blk = take(prep_blk_bytes(N));
   const int64_t common = off;
   q.o_part = take(8 * kTile * q.fwd_items);
   q.o_zt = take(4 * q.rows_pad);
@@ -124,7 +126,7 @@ int make_plan(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, Plan* p) {
   q.o_g = take(2 * q.rows_pad * q.Vb * q.es);   // two slabs, alternating blocks
   q.o_dx32 = take(4 * q.dx_split * q.rows_pad * H);
   q.P = pow2_at_least(q.rows_pad);
-  q.o_keys = take(8 * q.P);
+  q.o_keys = take(16 * q.P);
   q.o_oh = take(4 * q.rows_pad * H);
   q.o_map = take(4 * V);
   const int64_t bwd_end = off;
@@ -145,7 +147,7 @@ bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
 // kernel, device and process (the attribute belongs to the kernel, not to a
 // call), so that calls made under stream capture issue no attribute changes.
 constexpr int kAttrDevices = 64;
-template <auto Kernel>
+template <auto Kernel, int kBytes = kLdsBytes>
 hipError_t allow_big_lds() {
   static std::once_flag once[kAttrDevices];
   static hipError_t err[kAttrDevices];
@@ -155,7 +157,7 @@ hipError_t allow_big_lds() {
   if (dev < 0 || dev >= kAttrDevices) return hipErrorInvalidDevice;
   std::call_once(once[dev], [dev] {
     err[dev] = hipFuncSetAttribute((const void*)Kernel,
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, kLdsBytes);
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, kBytes);
   });
   return err[dev];
 }
@@ -213,6 +215,25 @@ struct Shard {
   int64_t v_begin, V_total;
 };
 
+// Targets, validity and compaction (k_prep_*), counters and the forward
+// split; blk: prep_blk_bytes(N) of workspace.
+void launch_prep(Launch& L, const int64_t* labels, int64_t B, int64_t T, int64_t ignore,
+                 int64_t V_total, int shift, int reduction, const float* grad_scale,
+                 int max_items, int64_t v_begin, int64_t V_local, int* blk, int* idx, int* tgt,
+                 int* rowpos, Counters* ctr, int32_t* status) {
+  const int N = (int)(B * T);
+  const int nblk = (int)cdiv(N > 0 ? N : 1, kPrepBlock);
+  hipLaunchKernelGGL(k_prep_count, dim3((unsigned)nblk), dim3(kPrepBlock), 0, L.s, labels, N,
+                     (int)T, ignore, V_total, shift, blk);
+  L.check();
+  hipLaunchKernelGGL(k_prep_scan, dim3(1), dim3(1024), 0, L.s, blk, nblk, reduction, grad_scale,
+                     cu_count(), max_items, V_local, ctr, status);
+  L.check();
+  hipLaunchKernelGGL(k_prep_write, dim3((unsigned)nblk), dim3(kPrepBlock), 0, L.s, labels, N,
+                     (int)T, ignore, V_total, shift, (const int*)blk, v_begin, idx, tgt, rowpos);
+  L.check();
+}
+
 template <class E>
 int forward_impl(const Plan& pl, const Shard& sh, const void* X, const void* W,
                  const int64_t* labels, int64_t B, int64_t T, int64_t ignore_index,
@@ -231,15 +252,14 @@ int forward_impl(const Plan& pl, const Shard& sh, const void* X, const void* W,
   const int row_bytes = (int)(pl.H * E::kBytes);
   const bool none = reduction == FLCE_REDUCTION_NONE;
 
-  hipLaunchKernelGGL(k_prep, dim3(1), dim3(1024), 0, stream, labels, (int)B, (int)T,
-                     ignore_index, sh.V_total, shift, reduction, (const float*)nullptr,
-                     cu_count(), (int)pl.fwd_items, sh.v_begin, pl.V, idx, tgt, rowpos, ctr,
-                     status);
-  L.check();
+  launch_prep(L, labels, B, T, ignore_index, sh.V_total, shift, reduction, nullptr,
+              (int)pl.fwd_items, sh.v_begin, pl.V, (int*)(ws + pl.o_blk), idx, tgt, rowpos, ctr,
+              status);
   hipLaunchKernelGGL(k_gather, dim3((unsigned)cdiv(rows_pad, 4)), dim3(256), 0, stream,
                      (const char*)X, row_bytes, (const int*)idx, (const Counters*)ctr,
                      xc, rows_pad, (const float*)nullptr, (float*)nullptr,
-                     (float*)nullptr, 0, 0, (int64_t)0, (const float*)nullptr, (float*)nullptr);
+                     (float*)nullptr, 0, 0, (int64_t)0, (const float*)nullptr, (float*)nullptr,
+                     (int*)nullptr, 0);
   L.check();
   hipLaunchKernelGGL(k_target<E>, dim3((unsigned)cdiv(rows_pad, 4)), dim3(256), 0, stream,
                      (const char*)xc, (const char*)W, (int)pl.H, (const int*)tgt,
@@ -275,35 +295,42 @@ int forward_impl(const Plan& pl, const Shard& sh, const void* X, const void* W,
 }
 
 // One-hot sums for the dW tiles (k_oh_*): sort the compacted rows by
-// (target, row), sum each target's rows of c_k Xc in that order.
+// (target, row), sum the rows of each target held by several rows, in that
+// order, and fill the map.  `keys` holds 2 P entries; the map must already
+// be -1 (k_gather).
 template <class E>
 void onehot_sums(int64_t P, int64_t rows_pad, int64_t H, int64_t V_local, const int* tgt,
                  const Counters* ctr, const char* xc, const float* rs, uint64_t* keys,
                  float* oh, int* map, Launch& L) {
   hipStream_t s = L.s;
-  const int64_t fill = std::max(P, V_local);
-  hipLaunchKernelGGL(k_oh_keys, dim3((unsigned)std::min<int64_t>(cdiv(fill, 256), 8192)),
-                     dim3(256), 0, s, tgt, ctr, (int)V_local, (int)P, keys, map);
+  const bool merge = P > kSortLocal && P <= kMergeMax;
+  hipLaunchKernelGGL(k_oh_sort_local, dim3((unsigned)std::max<int64_t>(1, P / kSortLocal)),
+                     dim3(256), 0, s, tgt, ctr, (int)V_local, (int)P, merge ? 1 : 0, keys);
   L.check();
-  hipLaunchKernelGGL(k_bsort_local, dim3((unsigned)std::max<int64_t>(1, P / kSortLocal)),
-                     dim3(1024), 0, s, keys, (int)P);
-  L.check();
-  for (int64_t st = 2 * kSortLocal; st <= P; st <<= 1) {
-    for (int64_t stride = st / 2; stride >= kSortLocal; stride >>= 1) {
-      hipLaunchKernelGGL(k_bsort_global, dim3((unsigned)cdiv(P / 2, 256)), dim3(256), 0, s,
-                         keys, (int)P, (int)st, (int)stride);
+  const uint64_t* sorted = keys;
+  if (merge) {
+    hipLaunchKernelGGL(k_oh_merge_blocks, dim3((unsigned)(P / 1024)), dim3(1024), 0, s,
+                       (const uint64_t*)keys, (int)P, keys + P);
+    L.check();
+    sorted = keys + P;
+  } else {
+    for (int64_t st = 2 * kSortLocal; st <= P; st <<= 1) {
+      for (int64_t stride = st / 2; stride >= kSortLocal; stride >>= 1) {
+        hipLaunchKernelGGL(k_bsort_global, dim3((unsigned)cdiv(P / 2, 256)), dim3(256), 0, s,
+                           keys, (int)P, (int)st, (int)stride);
+        L.check();
+      }
+      hipLaunchKernelGGL(k_bsort_merge, dim3((unsigned)(P / kSortLocal)), dim3(256), 0, s, keys,
+                         (int)st);
       L.check();
     }
-    hipLaunchKernelGGL(k_bsort_merge, dim3((unsigned)(P / kSortLocal)), dim3(1024), 0, s, keys,
-                       (int)st);
-    L.check();
   }
   const dim3 grid((unsigned)(rows_pad / kOhBlock), (unsigned)cdiv(H, 256));
-  hipLaunchKernelGGL(k_oh_partial<E>, grid, dim3(256), 0, s, (const uint64_t*)keys, xc,
-                     (int)H, ctr, rs, oh);
+  hipLaunchKernelGGL(k_oh_partial<E>, grid, dim3(256), 0, s, sorted, (int)P, xc, (int)H,
+                     (int)rows_pad, ctr, rs, oh);
   L.check();
-  hipLaunchKernelGGL(k_oh_final, grid, dim3(256), 0, s, (const uint64_t*)keys, (int)H,
-                     (int)rows_pad, oh, map);
+  hipLaunchKernelGGL(k_oh_final, grid, dim3(256), 0, s, sorted, (int)P, (int)H, (int)rows_pad,
+                     oh, map);
   L.check();
 }
 
@@ -328,15 +355,14 @@ int backward_impl(const Plan& pl, const Shard& sh, const void* X, const void* W,
   // reduction "none": grad_scale is per row, gathered into compacted order
   const bool none = reduction == FLCE_REDUCTION_NONE;
   float* rs = none && grad_scale ? (float*)(ws + pl.o_rs) : nullptr;
-  hipLaunchKernelGGL(k_prep, dim3(1), dim3(1024), 0, stream, labels, (int)B, (int)T,
-                     ignore_index, sh.V_total, shift, reduction, none ? nullptr : grad_scale,
-                     cu_count(), (int)pl.fwd_items, sh.v_begin, pl.V, idx, tgt, rowpos, ctr,
-                     status);
-  L.check();
+  launch_prep(L, labels, B, T, ignore_index, sh.V_total, shift, reduction,
+              none ? nullptr : grad_scale, (int)pl.fwd_items, sh.v_begin, pl.V,
+              (int*)(ws + pl.o_blk), idx, tgt, rowpos, ctr, status);
   hipLaunchKernelGGL(k_gather, dim3((unsigned)cdiv(rows_pad, 4)), dim3(256), 0, stream,
                      (const char*)X, row_bytes, (const int*)idx, (const Counters*)ctr,
                      xc, rows_pad, lse, lse2, dx32, (int)(pl.H * 4), (int)pl.dx_split,
-                     (int64_t)pl.rows_pad * pl.H, grad_scale, rs);
+                     (int64_t)pl.rows_pad * pl.H, grad_scale, rs, (int*)(ws + pl.o_map),
+                     (int)pl.V);
   L.check();
 
   float* oh = (float*)(ws + pl.o_oh);
@@ -352,7 +378,7 @@ int backward_impl(const Plan& pl, const Shard& sh, const void* X, const void* W,
   a.rs = rs;
   a.oh = oh;
   a.oh_map = oh_map;
-  a.oh_rows = rows_pad;
+  a.ohx = xc;
   a.tgt = tgt;
   a.dx32 = dx32;
   a.dx32p = dx32 + (int64_t)pl.rows_pad * pl.H;
@@ -378,7 +404,7 @@ int backward_impl(const Plan& pl, const Shard& sh, const void* X, const void* W,
     r.G = g + (b & 1) * slab;
     return r;
   };
-  if (L.err == hipSuccess) L.err = allow_big_lds<k_bwd<E>>();
+  if (L.err == hipSuccess) L.err = allow_big_lds<k_bwd<E>, kBwdLdsBytes>();
   // launch b + 1 runs the dX / dW tiles of block b and the G tiles of block
   // b + 1
   const int64_t nblk = cdiv(pl.V, pl.Vb);
@@ -394,7 +420,7 @@ int backward_impl(const Plan& pl, const Shard& sh, const void* X, const void* W,
     {
       Timed t("k_bwd", stream);
       hipLaunchKernelGGL(k_bwd<E>, dim3((unsigned)(nb_dx + nb_dw + nb_g)), dim3(kThreads),
-                         kLdsBytes, stream, cur, nxt, nb_dx, nb_dw, nb_g, dw_first);
+                         kBwdLdsBytes, stream, cur, nxt, nb_dx, nb_dw, nb_g, dw_first);
       L.check();
     }
   }
@@ -436,6 +462,7 @@ struct ChunkPlan {
   int64_t VB;               // vocabulary block of the dX / dW launches
   int64_t dx_split;         // dX tiles per (token tile, hidden tile) and block
   int64_t o_ctr, o_idx, o_tgt, o_rowpos, o_xc, o_zt, o_lse_c, o_lse2, o_rloss, o_bsum, o_cctr;
+  int64_t o_blk;
   int64_t o_rs;
   int64_t o_part, o_slab, o_dx32, o_dx32p;
   int64_t P, o_keys, o_oh, o_map;   // one-hot sums for dW
@@ -489,6 +516,7 @@ int make_chunk_plan(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, int64
   q.o_rs = take(4 * q.rows_pad);
   q.o_bsum = take(4 * q.TT);
   q.o_cctr = take(sizeof(Counters) * q.nchunks);
+  q.o_blk = take(prep_blk_bytes(q.N));
   q.o_part = take(8 * 2 * q.VT * q.C);
   q.o_slab = take(q.C * q.Vp * q.es);
   q.dx_split = dx_split_for(cdiv(H, kTile), q.C / kTile, FLCE_DX_TILES_CHUNKED);
@@ -497,7 +525,7 @@ int make_chunk_plan(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, int64
   // into the main FP32 sum after each chunk
   q.o_dx32p = take(4 * (q.dx_split - 1) * q.C * H);
   q.P = pow2_at_least(q.rows_pad);
-  q.o_keys = take(8 * q.P);
+  q.o_keys = take(16 * q.P);
   q.o_oh = take(4 * q.rows_pad * H);
   q.o_map = take(4 * V);
   q.total = off;
@@ -533,14 +561,13 @@ int chunked_impl(const ChunkPlan& pl, const void* X, const void* W, const int64_
   const bool none = reduction == FLCE_REDUCTION_NONE;
   float* rs = none && grad_scale ? (float*)(ws + pl.o_rs) : nullptr;
 
-  hipLaunchKernelGGL(k_prep, dim3(1), dim3(1024), 0, stream, labels, (int)B, (int)T,
-                     ignore_index, pl.V, shift, reduction, none ? nullptr : grad_scale,
-                     cu_count(), 1, (int64_t)0, pl.V, idx, tgt, rowpos, ctr, status);
-  L.check();
+  launch_prep(L, labels, B, T, ignore_index, pl.V, shift, reduction, none ? nullptr : grad_scale,
+              1, 0, pl.V, (int*)(ws + pl.o_blk), idx, tgt, rowpos, ctr, status);
   hipLaunchKernelGGL(k_gather, dim3((unsigned)cdiv(rows_pad, 4)), dim3(256), 0, stream,
                      (const char*)X, row_bytes, (const int*)idx, (const Counters*)ctr, xc,
                      rows_pad, (const float*)nullptr, (float*)nullptr, dx32,
-                     (int)(pl.H * 4), 1, (int64_t)0, grad_scale, rs);
+                     (int)(pl.H * 4), 1, (int64_t)0, grad_scale, rs, (int*)(ws + pl.o_map),
+                     (int)pl.V);
   L.check();
   hipLaunchKernelGGL(k_target<E>, dim3((unsigned)cdiv(rows_pad, 4)), dim3(256), 0, stream,
                      (const char*)xc, (const char*)W, (int)pl.H, (const int*)tgt,
@@ -551,7 +578,7 @@ int chunked_impl(const ChunkPlan& pl, const void* X, const void* W, const int64_
   onehot_sums<E>(pl.P, pl.rows_pad, pl.H, pl.V, tgt, ctr, xc, rs, (uint64_t*)(ws + pl.o_keys),
                  oh, oh_map, L);
   if (L.err == hipSuccess) L.err = allow_big_lds<k_chunk_z<E>>();
-  if (L.err == hipSuccess) L.err = allow_big_lds<k_bwd<E>>();
+  if (L.err == hipSuccess) L.err = allow_big_lds<k_bwd<E>, kBwdLdsBytes>();
   for (int64_t ch = 0; ch < pl.nchunks && L.err == hipSuccess; ++ch) {
     ChunkArgs ca;
     ca.W = (const char*)W;
@@ -614,7 +641,7 @@ int chunked_impl(const ChunkPlan& pl, const void* X, const void* W, const int64_
     // the one-hot part of dW (all rows) goes in with the first chunk's tiles
     b.oh = ch == 0 ? oh : nullptr;
     b.oh_map = oh_map;
-    b.oh_rows = rows_pad;
+    b.ohx = xc;
     for (int64_t v0 = 0; v0 < pl.V && L.err == hipSuccess; v0 += pl.VB) {
       b.v0 = (int)v0;
       b.vb = (int)std::min<int64_t>(pl.VB, pl.V - v0);
@@ -623,7 +650,7 @@ int chunked_impl(const ChunkPlan& pl, const void* X, const void* W, const int64_
       const int nb_dx = (int)pad8((int64_t)pl.dx_split * HT * TTc);
       const int nb_dw = (int)pad8((int64_t)HT * b.VTb);
       Timed t("k_chunk_dxdw", stream);
-      hipLaunchKernelGGL(k_bwd<E>, dim3((unsigned)(nb_dx + nb_dw)), dim3(kThreads), kLdsBytes,
+      hipLaunchKernelGGL(k_bwd<E>, dim3((unsigned)(nb_dx + nb_dw)), dim3(kThreads), kBwdLdsBytes,
                          stream, b, b, nb_dx, nb_dw, 0, C > cdiv(b.vb, pl.dx_split) ? 1 : 0);
       L.check();
     }
@@ -859,7 +886,8 @@ int flce_shard_merge_workspace_size(int64_t B, int64_t T, size_t* bytes) {
   if (B < 0 || T < 0 || B > kMaxI32 || T > kMaxI32 || B * T > (1ll << 24)) return FLCE_ERR_SHAPE;
   const int64_t rows_pad = round_up(B * T > 0 ? B * T : 1, kTile);
   *bytes = (size_t)(round_up(sizeof(Counters), kAlign) + 3 * round_up(4 * rows_pad, kAlign) +
-                    round_up(4 * cdiv(rows_pad, 256), kAlign));
+                    round_up(4 * cdiv(rows_pad, 256), kAlign) +
+                    round_up(prep_blk_bytes(B * T), kAlign));
   return FLCE_OK;
 }
 
@@ -903,12 +931,11 @@ int flce_shard_merge(const float* lse_shards, const float* zt_shards, int shards
   int* tgt = (int*)(ws + take(4 * rows_pad));
   int* rowpos = (int*)(ws + take(4 * rows_pad));
   float* bsum = (float*)(ws + take(4 * cdiv(rows_pad, 256)));
+  int* blk = (int*)(ws + take(prep_blk_bytes(N)));
   const bool none = reduction == FLCE_REDUCTION_NONE;
   Launch L{s};
-  hipLaunchKernelGGL(k_prep, dim3(1), dim3(1024), 0, s, labels, (int)B, (int)T, ignore_index,
-                     V_total, shift, reduction, (const float*)nullptr, cu_count(), 1,
-                     (int64_t)0, V_total, idx, tgt, rowpos, ctr, status);
-  L.check();
+  launch_prep(L, labels, B, T, ignore_index, V_total, shift, reduction, nullptr, 1, 0, V_total,
+              blk, idx, tgt, rowpos, ctr, status);
   const int nb = (int)cdiv(N, 256);
   hipLaunchKernelGGL(k_shard_merge, dim3((unsigned)nb), dim3(256), 0, s, lse_shards, zt_shards,
                      shards, (int)N, (const int*)rowpos, (const Counters*)ctr, lse, bsum,

@@ -6,7 +6,7 @@
 // kernels compute one or more 256 x 256 tiles with flce_tile.h.
 //
 // Forward  (loss, lse):
-//   k_prep      targets, validity, compaction of the valid rows (idx, tgt)
+//   k_prep_*    targets, validity, compaction of the valid rows (idx, tgt)
 //   k_gather    Xc[k] = X[idx[k]] for k < n, zero rows up to a tile multiple
 //   k_target    zt[k] = <Xc[k], W[tgt[k]]>
 //   k_fwd_lse   logits tiles W.Xc^T on MFMA, online max / sum-exp2 per row
@@ -42,72 +42,106 @@ struct Counters {
 constexpr int kStatusLabelRange = 8;
 
 // ---------------------------------------------------------------------------
-// k_prep: one workgroup of 1024 threads walks the rows in order, so the
-// compacted order is the row order (deterministic).  Labels are checked
-// against V (the whole vocabulary); targets are stored relative to v_begin,
-// the first vocabulary row of this call's W (V_local rows; a vocabulary
-// shard), so a target outside the shard has an index outside [0, V_local).
+// Targets, validity and compaction in three kernels over blocks of 1024 rows:
+//   k_prep_count  valid rows and bad labels per block
+//   k_prep_scan   one workgroup: block offsets (exclusive scan, block order),
+//                 n, status, c and the forward split -> Counters
+//   k_prep_write  each block's valid rows to idx / tgt in row order, rowpos
+// so the compacted order is the row order (deterministic).  Labels are
+// checked against V (the whole vocabulary); targets are stored relative to
+// v_begin, the first vocabulary row of this call's W (V_local rows; a
+// vocabulary shard), so a target outside the shard has an index outside
+// [0, V_local).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void k_prep(
-    const int64_t* __restrict__ labels, int B, int T, int64_t ignore,
-    int64_t V, int shift, int reduction, const float* __restrict__ grad_scale,
-    int ncu, int max_items, int64_t v_begin, int64_t V_local, int* __restrict__ idx,
-    int* __restrict__ tgt, int* __restrict__ rowpos, Counters* __restrict__ ctr,
+constexpr int kPrepBlock = 1024;
+
+// the target of row i (ignore when it has none) and whether it is valid
+// (bad: neither ignore nor in [0, V))
+__device__ __forceinline__ bool row_target(const int64_t* __restrict__ labels, int i, int N,
+                                           int T, int64_t ignore, int64_t V, int shift,
+                                           int64_t& y, bool& bad) {
+  y = ignore;
+  bad = false;
+  if (i >= N) return false;
+  if (shift) {
+    const int t = i % T;
+    y = (t + 1 < T) ? labels[i + 1] : ignore;
+  } else {
+    y = labels[i];
+  }
+  if (y == ignore) return false;
+  if (y < 0 || y >= V) {
+    bad = true;
+    return false;
+  }
+  return true;
+}
+
+// per block: [0] valid rows, [1] 1 if a bad label
+__global__ __launch_bounds__(kPrepBlock) void k_prep_count(
+    const int64_t* __restrict__ labels, int N, int T, int64_t ignore, int64_t V, int shift,
+    int* __restrict__ blk) {
+  __shared__ int wsum[kPrepBlock / 64];
+  __shared__ int bad_s;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  if (tid == 0) bad_s = 0;
+  __syncthreads();
+  int64_t y;
+  bool bad;
+  const bool valid = row_target(labels, blockIdx.x * kPrepBlock + tid, N, T, ignore, V, shift,
+                                y, bad);
+  if (bad) bad_s = 1;
+  const uint64_t m = __ballot(valid);
+  if (lane == 0) wsum[w] = __popcll(m);
+  __syncthreads();
+  if (tid == 0) {
+    int tot = 0;
+    for (int q = 0; q < kPrepBlock / 64; ++q) tot += wsum[q];
+    blk[2 * blockIdx.x] = tot;
+    blk[2 * blockIdx.x + 1] = bad_s;
+  }
+}
+
+// One workgroup: blk[2 b] becomes the block's first compacted index; n,
+// status, c; the forward split: P vocabulary ranges per token tile, P * TTn
+// items of about VT / P tiles each, at most max_items of them (P = 1 always
+// fits).  With the items running in waves of `ncu` workgroups the time is
+// about waves(P) * ceil(VT / P) tiles; thread t prices P = t + 1 and the
+// cheapest (then the smallest) P wins.
+__global__ __launch_bounds__(1024) void k_prep_scan(
+    int* __restrict__ blk, int nblk, int reduction, const float* __restrict__ grad_scale,
+    int ncu, int max_items, int64_t V_local, Counters* __restrict__ ctr,
     int32_t* __restrict__ status_out) {
-  __shared__ int wsum[16];
-  __shared__ int base_s;
+  __shared__ int part[1024];
   __shared__ int bad_s;
   __shared__ unsigned long long best_s;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int N = B * T;
-  if (tid == 0) {
-    base_s = 0;
-    bad_s = 0;
+  const int tid = threadIdx.x;
+  // thread t scans blocks t * per .. (t + 1) * per - 1 in order
+  const int per = (nblk + 1023) / 1024;
+  const int b0 = tid * per, b1 = min(b0 + per, nblk);
+  int sum = 0, bad = 0;
+  for (int b = b0; b < b1; ++b) {
+    sum += blk[2 * b];
+    bad |= blk[2 * b + 1];
   }
+  if (tid == 0) bad_s = 0;
+  part[tid] = sum;
   __syncthreads();
-  for (int i0 = 0; i0 < N; i0 += 1024) {
-    const int i = i0 + tid;
-    bool valid = false;
-    int64_t y = ignore;
-    if (i < N) {
-      if (shift) {
-        const int t = i % T;
-        y = (t + 1 < T) ? labels[i + 1] : ignore;
-      } else {
-        y = labels[i];
-      }
-      if (y != ignore) {
-        if (y < 0 || y >= V) bad_s = 1;
-        else valid = true;
-      }
-    }
-    const uint64_t m = __ballot(valid);
-    const int pre = __popcll(m & ((1ull << lane) - 1ull));
-    if (lane == 0) wsum[w] = __popcll(m);
+  if (bad) bad_s = 1;
+  // inclusive scan of the 1024 partial sums (Hillis-Steele)
+  for (int d = 1; d < 1024; d <<= 1) {
+    const int v = tid >= d ? part[tid - d] : 0;
     __syncthreads();
-    int pos = base_s + pre;
-    for (int q = 0; q < w; ++q) pos += wsum[q];
-    if (i < N) {
-      rowpos[i] = valid ? pos : -1;
-      if (valid) {
-        idx[pos] = i;
-        tgt[pos] = (int)(y - v_begin);   // index into this call's W rows
-      }
-    }
-    __syncthreads();
-    if (tid == 0) {
-      int tot = 0;
-      for (int q = 0; q < 16; ++q) tot += wsum[q];
-      base_s += tot;
-    }
+    part[tid] += v;
     __syncthreads();
   }
-  // Forward split: P vocabulary ranges per token tile, P * TTn items of
-  // about VT / P tiles each, at most max_items of them (P = 1 always fits).
-  // With the items running in waves of `ncu` workgroups the time is about
-  // waves(P) * ceil(VT / P) tiles; thread t prices P = t + 1 and the
-  // cheapest (then the smallest) P wins.
-  const int n = base_s;
+  int run = tid > 0 ? part[tid - 1] : 0;
+  for (int b = b0; b < b1; ++b) {
+    const int c = blk[2 * b];
+    blk[2 * b] = run;
+    run += c;
+  }
+  const int n = part[1023];
   const int64_t VT = (V_local + kTile - 1) / kTile;
   const int64_t TTn = n > 0 ? (n + kTile - 1) / kTile : 1;
   if (tid == 0) best_s = ~0ull;
@@ -116,8 +150,8 @@ __global__ __launch_bounds__(1024) void k_prep(
     const int64_t P = tid + 1;
     if (P == 1 || (P <= VT && P * TTn <= max_items)) {
       const int64_t waves = (P * TTn + ncu - 1) / ncu;
-      const int64_t per = (VT + P - 1) / P;
-      atomicMin(&best_s, (unsigned long long)(waves * per) * 2048ull + (unsigned long long)P);
+      const int64_t pr = (VT + P - 1) / P;
+      atomicMin(&best_s, (unsigned long long)(waves * pr) * 2048ull + (unsigned long long)P);
     }
   }
   __syncthreads();
@@ -134,20 +168,49 @@ __global__ __launch_bounds__(1024) void k_prep(
   }
 }
 
+__global__ __launch_bounds__(kPrepBlock) void k_prep_write(
+    const int64_t* __restrict__ labels, int N, int T, int64_t ignore, int64_t V, int shift,
+    const int* __restrict__ blk, int64_t v_begin, int* __restrict__ idx, int* __restrict__ tgt,
+    int* __restrict__ rowpos) {
+  __shared__ int wsum[kPrepBlock / 64];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int i = blockIdx.x * kPrepBlock + tid;
+  int64_t y;
+  bool bad;
+  const bool valid = row_target(labels, i, N, T, ignore, V, shift, y, bad);
+  const uint64_t m = __ballot(valid);
+  const int pre = __popcll(m & ((1ull << lane) - 1ull));
+  if (lane == 0) wsum[w] = __popcll(m);
+  __syncthreads();
+  int pos = blk[2 * blockIdx.x] + pre;
+  for (int q = 0; q < w; ++q) pos += wsum[q];
+  if (i < N) {
+    rowpos[i] = valid ? pos : -1;
+    if (valid) {
+      idx[pos] = i;
+      tgt[pos] = (int)(y - v_begin);   // index into this call's W rows
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------
 // k_gather: one wave per compacted row k in [0, rows_pad).  Row k < n copies
 // X[idx[k]]; the rest is zero.  In the backward it also stages
-// lse2[k] = lse[idx[k]] * log2(e) and clears row k of each of the dx_split
-// FP32 dX accumulators (dx_stride floats apart).
+// lse2[k] = lse[idx[k]] * log2(e), clears row k of each of the dx_split
+// FP32 dX accumulators (dx_stride floats apart) and sets the one-hot map
+// (V_local entries) to -1.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_gather(
     const char* __restrict__ X, int row_bytes, const int* __restrict__ idx,
     const Counters* __restrict__ ctr, char* __restrict__ Xc, int rows_pad,
     const float* __restrict__ lse, float* __restrict__ lse2,
     float* __restrict__ dx32, int dx32_row_bytes, int dx_split, int64_t dx_stride,
-    const float* __restrict__ rs_in, float* __restrict__ rs_c) {
+    const float* __restrict__ rs_in, float* __restrict__ rs_c, int* __restrict__ map,
+    int V_local) {
   const int k = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
+  if (map != nullptr)
+    for (int v = blockIdx.x * 256 + threadIdx.x; v < V_local; v += gridDim.x * 256) map[v] = -1;
   if (k >= rows_pad) return;
   const int n = ctr->n;
   const int chunks = row_bytes >> 4;
@@ -270,7 +333,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_fwd_lse(FwdArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem_[];
   lds_t* smem = (lds_t*)smem_;
-  // the split k_prep chose: P ranges x TTn token tiles, handed out XCD by XCD
+  // the split k_prep_scan chose: P ranges x TTn token tiles, handed out XCD by XCD
   const int n = a.ctr->n, P = a.ctr->fwd_p;
   const int TTn = (n + kTile - 1) / kTile;
   const int nact = P * TTn, nact8 = (nact + 7) & ~7;
@@ -435,9 +498,11 @@ struct BwdArgs {
   int TT, HT, VTb;     // token tiles (bound), hidden tiles, block vocab tiles
   int dw_f32;          // dW written as fp32 (else bf16)
   int dw_acc;          // dW tiles add to dW (else overwrite it)
-  const float* oh;     // [oh_rows, H] one-hot sums (see k_oh_*) or NULL: dW
-  const int* oh_map;   //   tiles then take off oh[oh_map[v]] for each column v
-  int oh_rows;         //   (all compacted rows, also where rows_pad is a chunk's)
+  const float* oh;     // [rows, H] one-hot sums (see k_oh_*) or NULL: dW tiles
+  const int* oh_map;   //   then take off, for each column v, the part of the
+  const char* ohx;     //   rows with target v (oh_map[v]: -1 none, k >= 0 the
+                       //   one row k of ohx, the compacted rows with factors
+                       //   rs; -2 - p row p of oh)
 };
 
 // G = c * 2^(z*log2e - lse2) for one tile, stored as G[token][vocab].
@@ -537,63 +602,68 @@ __device__ __forceinline__ void g_tile(const BwdArgs& a, int b, lds_t* smem) {
 // (H % 8 == 0, so a group of 4 is either inside or outside).  Branch-free:
 // a masked lane stores to an offset past the descriptor's range, which the
 // hardware drops (the descriptor covers the tile's 256 rows, < 2^31 bytes).
-template <bool kMasked, class Corr>
+template <bool kMasked, class Fix>
 __device__ __forceinline__ void dw_store(const BwdArgs& a, const f32x16 (&acc)[4][4],
                                          int vt, int ht, int wm, int wn, int lane,
-                                         int mlim, int hlim, lds_t* smem, const Corr& corr) {
+                                         int mlim, int hlim, lds_t* smem, const Fix& fix) {
   const int es = a.dw_f32 ? 4 : 2;
   const int64_t row0 = (int64_t)(a.v0 + vt * kTile) * a.H + (int64_t)ht * kTile;
   const int64_t left = ((int64_t)a.V * a.H - row0) * es;
   const int64_t span = (int64_t)kTile * a.H * es;
   const rsrc_t wr = make_rsrc((char*)a.dW + row0 * es, left < span ? left : span);
   const int wave = threadIdx.x >> 6;
+  lds_t* region = smem + wave * 32768;
+  auto off = [&](int o, int x0) {
+    const int m = wn * 128 + o, h = wm * 128 + x0;
+    const bool ok = !kMasked || (m < mlim && h < hlim);
+    return ok ? (m * a.H + h) * es : (int)0x80000000u;
+  };
+  auto store_f32 = [&](int o, int x0, f32x4 v) {
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), wr, off(o, x0), 0, 0);
+  };
+  auto store_bf16 = [&](int o, int x0, f32x4 v) {
+    i32x2 pk;
+    pk[0] = pack_bf16(v[0], v[1]);
+    pk[1] = pack_bf16(v[2], v[3]);
+    __builtin_amdgcn_raw_buffer_store_b64(pk, wr, off(o, x0), 0, 0);
+  };
   if (a.dw_acc) {
     // dW += tile (chunked mode): rows of 4-value groups through LDS, the sum
     // formed in fp32 and rounded once per call
-    auto off = [&](int o, int x0) {
-      const int m = wn * 128 + o, h = wm * 128 + x0;
-      const bool ok = !kMasked || (m < mlim && h < hlim);
-      return ok ? (m * a.H + h) * es : (int)0x80000000u;
-    };
     if (a.dw_f32) {
       rmw_quarter_f32(
-          smem + wave * 32768, lane, acc,
+          region, lane, acc,
           [&](int o, int x0) { return __builtin_bit_cast(f32x4, bload128(wr, off(o, x0))); },
-          [&](int o, int x0, f32x4 v) {
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), wr, off(o, x0),
-                                                   0, 0);
-          },
-          corr);
+          store_f32, fix);
     } else {
       rmw_quarter_f32(
-          smem + wave * 32768, lane, acc,
+          region, lane, acc,
           [&](int o, int x0) {
             const i32x2 u = __builtin_amdgcn_raw_buffer_load_b64(wr, off(o, x0), 0, 0);
             return f32x4{bf2f((uint32_t)u[0] & 0xFFFFu), bf2f((uint32_t)u[0] >> 16),
                          bf2f((uint32_t)u[1] & 0xFFFFu), bf2f((uint32_t)u[1] >> 16)};
           },
-          [&](int o, int x0, f32x4 v) {
-            i32x2 pk;
-            pk[0] = pack_bf16(v[0], v[1]);
-            pk[1] = pack_bf16(v[2], v[3]);
-            __builtin_amdgcn_raw_buffer_store_b64(pk, wr, off(o, x0), 0, 0);
-          },
-          corr);
+          store_bf16, fix);
     }
+    return;
+  }
+  if (fix.any) {
+    // one-hot sums to take off: the FP32 rows through LDS, where they are fixed
+    if (a.dw_f32) rmw_quarter_f32(region, lane, acc, NoLoad{}, store_f32, fix);
+    else rmw_quarter_f32(region, lane, acc, NoLoad{}, store_bf16, fix);
     return;
   }
   if (!a.dw_f32) {
     // bf16 rows through LDS: row o of the quarter is vocabulary entry
     // wn * 128 + o of the tile, inner x its hidden index wm * 128 + x
     store_quarter_bf16(
-        smem + wave * 32768, lane, [&](int i, int j, int r) { return acc[i][j][r]; },
+        region, lane, [&](int i, int j, int r) { return acc[i][j][r]; },
         [&](int o, int x0, i32x4 v) {
           const int m = wn * 128 + o, h = wm * 128 + x0;
           const bool ok = !kMasked || (m < mlim && h < hlim);
           __builtin_amdgcn_raw_buffer_store_b128(v, wr, ok ? (m * a.H + h) * 2 : (int)0x80000000u,
                                                  0, 0);
-        },
-        corr);
+        });
     return;
   }
 #pragma unroll
@@ -606,9 +676,8 @@ __device__ __forceinline__ void dw_store(const BwdArgs& a, const f32x16 (&acc)[4
         const int hc = acc_row(wm, i, 4 * g, lane);
         const bool ok = !kMasked || (mc < mlim && hc < hlim);
         const int off = ok ? (mc * a.H + hc) * 4 : (int)0x80000000u;
-        const f32x4 cv = corr(i, j, g);
-        const f32x4 v = {acc[i][j][4 * g] - cv[0], acc[i][j][4 * g + 1] - cv[1],
-                         acc[i][j][4 * g + 2] - cv[2], acc[i][j][4 * g + 3] - cv[3]};
+        const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                         acc[i][j][4 * g + 3]};
         __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), wr, off, 0, 0);
       }
     __builtin_amdgcn_sched_barrier(0);
@@ -616,45 +685,134 @@ __device__ __forceinline__ void dw_store(const BwdArgs& a, const f32x16 (&acc)[4
 }
 
 // The one-hot part of a dW tile, taken off in FP32 before the tile's one
-// rounding: column m (vocabulary entry v0 + vt * 256 + m of this call's W)
-// loses oh[oh_map[v]] when some valid row has that target.  corr(i, j, g) is
-// the f32x4 for accumulator registers (i, j, 4 g .. 4 g + 3): hidden rows
-// acc_row(wm, i, 4 g, lane) .. + 3 of column acc_col(wn, j, lane), one
-// 16-byte load.  Column blocks without any target in the wave cost nothing
-// (a wave-uniform test); lanes without one read past the buffer (zeros).
+// rounding: column m (vocabulary entry v = v0 + vt * 256 + m of this call's W)
+// loses c_k Xc[k] summed over the rows k with target v: c_k Xc[k] itself for
+// a target of one row, the row of the one-hot sums for several.
+//
+// Only the few columns with a target are touched.  After the K loop each wave
+// fetches, for its columns that have one (in column order), the 128 values
+// under its hidden rows into a 512-byte slot of its own 8 KiB past the tile's
+// stages: all of the wave's loads go out together, one wait per tile.  The
+// tile then leaves through the FP32 staging of rmw_quarter_f32, and this
+// functor's fix step subtracts each slot from its column's staged row, two
+// columns per wave instruction.  Columns past the kOhDataSlots data slots
+// (dense targets) fetch their values in the fix step.  The last 512 bytes of
+// the region list the map entry of every slot.
+constexpr int kOhSlotBytes = 512;
+constexpr int kOhDataSlots = 15;
+constexpr int kOhWaveBytes = (kOhDataSlots + 1) * kOhSlotBytes;   // 8 KiB
+constexpr int kBwdLdsBytes = kLdsBytes + 4 * kOhWaveBytes;         // 160 KiB
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+typedef __attribute__((address_space(3))) int lds_int;
+
+// the map lookups, issued before the tile's K loop so that they arrive under
+// it: idx[j] = map entry of this lane's column in block j (-1: none)
+template <class A>
+__device__ __forceinline__ void onehot_lookup(const A& a, int vt, int wn, int lane, int mlim,
+                                              int (&idx)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int m = acc_col(wn, j, lane);
+    idx[j] = a.oh != nullptr && m < mlim ? a.oh_map[a.v0 + vt * kTile + m] : -1;
+  }
+}
+
+template <class E>
 struct OneHotDW {
-  rsrc_t ohr;
-  int idx[4];
-  unsigned any;      // bit j: some lane of the wave has a target in block j
-  int H, hbase, wm, lane, hlim;
-  // the map lookups, issued before the tile's K loop so that they arrive
-  // under it
+  const float* oh;
+  const char* ohx;
+  const float* rs;
+  float c;
+  lds_t* slots;        // this wave's slot region
+  unsigned m[4];       // bit c of m[j]: column 32 j + c has a target
+  int n0;              // targets among columns 0 .. 63
+  int hcol, H;         // hidden index of this lane's 4 values in a slot
+  bool any;
+  // This lane's 4 values for map entry `e` (!= -1); hidden columns past H
+  // are zeros.  A one-row target is scaled as the sums scale it.
+  __device__ __forceinline__ f32x4 values(int e) const {
+    f32x4 v = {0.f, 0.f, 0.f, 0.f};
+    if (hcol >= H) return v;
+    if (e >= 0) {
+      const float sc = rs ? c * rs[e] : c;
+      f32x4 x;
+      if constexpr (E::kBytes == 2) {
+        const i32x2 u = *(const i32x2*)(ohx + ((int64_t)e * H + hcol) * 2);
+        x = f32x4{bf2f((uint32_t)u[0] & 0xFFFFu), bf2f((uint32_t)u[0] >> 16),
+                  bf2f((uint32_t)u[1] & 0xFFFFu), bf2f((uint32_t)u[1] >> 16)};
+      } else {
+        x = *(const f32x4*)(ohx + ((int64_t)e * H + hcol) * 4);
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q) v[q] = fmaf(sc, x[q], 0.f);
+    } else {
+      v = *(const f32x4*)(oh + (int64_t)(-2 - e) * H + hcol);   // 64-bit: past 2^31 bytes
+    }
+    return v;
+  }
+  // After the K loop's last barrier (`slots_` is the wave's region).
   template <class A>
-  __device__ __forceinline__ static void lookup(const A& a, int vt, int wn, int lane, int mlim,
-                                                int (&idx)[4]) {
+  __device__ __forceinline__ OneHotDW(const A& a, const int (&idx)[4], int ht, int wm, int lane,
+                                      lds_t* slots_)
+      : oh(a.oh), ohx(a.ohx), rs(a.rs), slots(slots_),
+        hcol(ht * kTile + wm * 128 + 4 * (lane & 31)), H(a.H) {
+    const int cl = lane & 31, hi = lane >> 5;
+    int slot[4], total = 0;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int m = acc_col(wn, j, lane);
-      idx[j] = a.oh != nullptr && m < mlim ? a.oh_map[a.v0 + vt * kTile + m] : -1;
+      // lanes 32..63 hold the columns of lanes 0..31
+      m[j] = (unsigned)__ballot(idx[j] != -1);
+      slot[j] = total + __builtin_popcount(m[j] & ((1u << cl) - 1u));
+      total += __builtin_popcount(m[j]);
+      if (j == 1) n0 = total;
     }
-  }
-  template <class A>
-  __device__ __forceinline__ OneHotDW(const A& a, const int (&idx_)[4], int ht, int wm_,
-                                      int lane_, int hlim_)
-      : H(a.H), hbase(ht * kTile), wm(wm_), lane(lane_), hlim(hlim_) {
-    any = 0;
-    ohr = make_rsrc(a.oh, a.oh != nullptr ? (int64_t)a.oh_rows * a.H * 4 : 0);
+    any = total > 0;
+    if (!any) return;
+    c = a.ctr->c;
+    // slot -> map entry (LDS operations of one wave complete in order, so the
+    // reads below see these writes)
+    lds_int* tab = (lds_int*)(slots_ + kOhDataSlots * kOhSlotBytes);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      idx[j] = idx_[j];
-      if (__ballot(idx[j] >= 0) != 0) any |= 1u << j;
+    for (int j = 0; j < 4; ++j)
+      if (hi == 0 && idx[j] != -1) tab[slot[j]] = idx[j];
+    // lanes 0..31 fill slot 2 q, lanes 32..63 slot 2 q + 1, 16 bytes each
+    const int nload = total < kOhDataSlots ? total : kOhDataSlots;
+    f32x4 v[(kOhDataSlots + 1) / 2];
+#pragma unroll
+    for (int q = 0; q < (kOhDataSlots + 1) / 2; ++q) {
+      v[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int s = 2 * q + hi;
+      if (2 * q < nload && s < nload) v[q] = values(tab[s]);
+    }
+#pragma unroll
+    for (int q = 0; q < (kOhDataSlots + 1) / 2; ++q) {
+      const int s = 2 * q + hi;
+      if (2 * q < nload && s < nload) *(lds_f32x4*)(slots_ + s * kOhSlotBytes + 16 * cl) = v[q];
     }
   }
-  __device__ __forceinline__ f32x4 operator()(int i, int j, int g) const {
-    if (!(any & (1u << j))) return f32x4{0.f, 0.f, 0.f, 0.f};
-    const int hr = acc_row(wm, i, 4 * g, lane);
-    const int off = idx[j] >= 0 && hr < hlim ? (idx[j] * H + hbase + hr) * 4 : (int)0x80000000u;
-    return __builtin_bit_cast(f32x4, bload128(ohr, off));
+  // rmw_quarter_f32's fix step: staged row o of half hf (column 64 hf + o)
+  // loses its slot; 16-byte unit u of a staged row sits at (u ^ (o % 32)).
+  __device__ __forceinline__ void operator()(int hf, lds_t* region) const {
+    if (!any) return;
+    const int cl = threadIdx.x & 31, hi = (threadIdx.x >> 5) & 1;
+    const lds_int* tab = (const lds_int*)(slots + kOhDataSlots * kOhSlotBytes);
+    uint64_t hm = (uint64_t)m[2 * hf] | ((uint64_t)m[2 * hf + 1] << 32);
+    int s = hf ? n0 : 0;
+    while (hm != 0) {
+      const int o0 = __builtin_ctzll(hm);
+      hm &= hm - 1;
+      const int o1 = hm != 0 ? __builtin_ctzll(hm) : -1;
+      if (hm != 0) hm &= hm - 1;
+      const int o = hi ? o1 : o0, sl = s + hi;
+      s += 2;
+      if (o >= 0) {
+        const f32x4 p = sl < kOhDataSlots ? *(const lds_f32x4*)(slots + sl * kOhSlotBytes + 16 * cl)
+                                          : values(tab[sl]);
+        lds_f32x4* r = (lds_f32x4*)(region + o * 512 + ((cl ^ (o & 31)) << 4));
+        const f32x4 x = *r;
+        *r = f32x4{x[0] - p[0], x[1] - p[1], x[2] - p[2], x[3] - p[3]};
+      }
+    }
   }
 };
 
@@ -685,15 +843,21 @@ __device__ __forceinline__ void dw_tile(const BwdArgs& a, int b, lds_t* smem) {
   B.kbytes = 0;
   const int mlim = a.vb - vt * kTile, hlim = a.H - ht * kTile;
   int ohidx[4];
-  OneHotDW::lookup(a, vt, wn, lane, mlim, ohidx);
+  onehot_lookup(a, vt, wn, lane, mlim, ohidx);
   f32x16 acc[4][4];
   zero_acc(acc);
-  gemm_tile<E, LoadMN<E>, LoadMN<E>>(A, B, steps, smem, wm, wn, acc);
+  // K runs over the rows: past 2^31 bytes of an operand (very many rows) the
+  // loaders rebase their descriptor per step
+  const int64_t reach = (int64_t)steps * E::kKStep * (A.ldb > B.ldb ? A.ldb : B.ldb);
+  if (reach <= 0x7FFFFFFF)
+    gemm_tile<E, LoadMN<E>, LoadMN<E>>(A, B, steps, smem, wm, wn, acc);
+  else
+    gemm_tile<E, LoadMN<E, true>, LoadMN<E, true>>(A, B, steps, smem, wm, wn, acc);
 
-  const OneHotDW corr(a, ohidx, ht, wm, lane, hlim);
+  const OneHotDW<E> fix(a, ohidx, ht, wm, lane, smem + kLdsBytes + wave * kOhWaveBytes);
   if (mlim >= kTile && hlim >= kTile)
-    dw_store<false>(a, acc, vt, ht, wm, wn, lane, 0, 0, smem, corr);
-  else dw_store<true>(a, acc, vt, ht, wm, wn, lane, mlim, hlim, smem, corr);
+    dw_store<false>(a, acc, vt, ht, wm, wn, lane, 0, 0, smem, fix);
+  else dw_store<true>(a, acc, vt, ht, wm, wn, lane, mlim, hlim, smem, fix);
 }
 
 // dX32 += tile, read-modify-write: each (token tile, hidden tile) belongs to
@@ -701,19 +865,22 @@ __device__ __forceinline__ void dw_tile(const BwdArgs& a, int b, lds_t* smem) {
 // Accumulator rows are hidden indices, columns tokens; the quarter goes
 // through LDS (rmw_quarter_f32) so that each token row is read and written in
 // 512-byte runs.  Token columns >= nlim (padding) and hidden rows >= hlim are
-// skipped: their offset lies past the buffer (rows_pad * H * 4 < 2^31), so
+// skipped: their offset lies past the tile's rows (256 * H * 4 < 2^31), so
 // the load returns zeros and the store is dropped.
 template <bool kMasked>
 __device__ __forceinline__ void dx_add(const BwdArgs& a, const f32x16 (&acc)[4][4],
                                        int part, int tau, int ht, int wm, int wn, int lane,
                                        int nlim, int hlim, lds_t* smem) {
-  float* base = part == 0 ? a.dx32 : a.dx32p + (part - 1) * a.dx_stride;
-  const rsrc_t xr = make_rsrc(base, (int64_t)a.rows_pad * a.H * 4);
+  // the descriptor starts at the token tile's first row (64-bit base), so
+  // the offsets stay below 256 * H * 4 bytes whatever the row count
+  float* base = (part == 0 ? a.dx32 : a.dx32p + (part - 1) * a.dx_stride) +
+                (int64_t)tau * kTile * a.H;
+  const rsrc_t xr = make_rsrc(base, (int64_t)kTile * a.H * 4);
   const int wave = threadIdx.x >> 6;
   auto offset = [&](int o, int x0) {
     const int tcol = wn * 128 + o, hc = wm * 128 + x0;
     const bool ok = !kMasked || (tcol < nlim && hc < hlim);
-    return ok ? ((tau * kTile + tcol) * a.H + ht * kTile + hc) * 4 : (int)0x80000000u;
+    return ok ? (tcol * a.H + ht * kTile + hc) * 4 : (int)0x80000000u;
   };
   rmw_quarter_f32(
       smem + wave * 32768, lane, acc,
@@ -1195,33 +1362,35 @@ __global__ __launch_bounds__(256) void k_dx_final(
 
 // ---------------------------------------------------------------------------
 // One-hot sums for dW: OH_v = sum over valid rows k with y_k = v of c_k Xc[k]
-// (FP32), one row per target value that occurs, summed in row order.  The
-// compacted rows are sorted by the unique 64-bit key (target << 32 | row), so
-// the order of every sum is fixed; runs of equal targets are summed position
-// by position (per 256-position block, then across blocks in order).
+// (FP32), summed in row order.  The compacted rows are sorted by the unique
+// 64-bit key (target << 32 | row), so the order of every sum is fixed.  A
+// target held by one row needs no sum (the dW tiles scale that row of Xc
+// themselves); the runs of several rows are summed position by position, per
+// block of kOhBlock sorted positions and then across blocks in order.
+// map[v] (v < V_local) afterwards: -1 no row has target v; k >= 0 the one
+// row k; -2 - p the sum is row p of OH.
 // ---------------------------------------------------------------------------
 
 constexpr uint64_t kNoKey = ~0ull;
 
-// keys[i] for i < P (a power of two): compacted rows k < n with a target in
-// [0, V_local); everything else sorts last.  Also map[v] = -1 for v < V_local.
-__global__ __launch_bounds__(256) void k_oh_keys(const int* __restrict__ tgt,
-                                                 const Counters* __restrict__ ctr, int V_local,
-                                                 int P, uint64_t* __restrict__ keys,
-                                                 int* __restrict__ map) {
-  const int n = ctr->n;
-  const int total = P > V_local ? P : V_local;
-  for (int i = blockIdx.x * 256 + threadIdx.x; i < total; i += gridDim.x * 256) {
-    if (i < P) {
-      uint64_t key = kNoKey;
-      if (i < n) {
-        const int y = tgt[i];
-        if (y >= 0 && y < V_local) key = ((uint64_t)(uint32_t)y << 32) | (uint32_t)i;
-      }
-      keys[i] = key;
-    }
-    if (i < V_local) map[i] = -1;
+__device__ __forceinline__ uint32_t key_target(uint64_t k) { return (uint32_t)(k >> 32); }
+
+// a value every lane holds, kept in scalar registers
+__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// key of sorted-array position i before sorting: compacted row i when it has
+// a target in [0, V_local), else kNoKey (sorts last)
+__device__ __forceinline__ uint64_t oh_key(const int* __restrict__ tgt, int n, int V_local,
+                                           int i) {
+  if (i < n) {
+    const int y = tgt[i];
+    if (y >= 0 && y < V_local) return ((uint64_t)(uint32_t)y << 32) | (uint32_t)i;
   }
+  return kNoKey;
 }
 
 // Bitonic compare-exchange of positions i < j = i + stride: ascending where
@@ -1235,28 +1404,72 @@ __device__ __forceinline__ void bitonic_pair(uint64_t& a, uint64_t& b, int i, in
   }
 }
 
-// Sorts each block of kSortLocal keys (the whole array when P is no larger)
-// in LDS: stages 2 .. min(P, kSortLocal), directions by global position.
-constexpr int kSortLocal = 2048;
-__global__ __launch_bounds__(1024) void k_bsort_local(uint64_t* __restrict__ keys, int P) {
+// Builds the keys and sorts each block of kSortLocal of them (the whole array
+// when P is no larger) in LDS: stages 2 .. min(P, kSortLocal).  The
+// directions follow the global position (alternating blocks, as the bitonic
+// stages past kSortLocal need) or, with `ascending`, the position in the block
+// (every block ascending, as k_oh_merge_blocks needs).  256 threads, two
+// pairs each per step.
+constexpr int kSortLocal = 1024;
+__global__ __launch_bounds__(256) void k_oh_sort_local(const int* __restrict__ tgt,
+                                                       const Counters* __restrict__ ctr,
+                                                       int V_local, int P, int ascending,
+                                                       uint64_t* __restrict__ keys) {
   __shared__ uint64_t sk[kSortLocal];
   const int len = P < kSortLocal ? P : kSortLocal;
   const int base = blockIdx.x * kSortLocal;
-  for (int t = threadIdx.x; t < len; t += 1024) sk[t] = keys[base + t];
+  const int n = ctr->n;
+  for (int t = threadIdx.x; t < len; t += 256) sk[t] = oh_key(tgt, n, V_local, base + t);
   __syncthreads();
   for (int s = 2; s <= len; s <<= 1)
     for (int stride = s >> 1; stride > 0; stride >>= 1) {
-      for (int t = threadIdx.x; t < len / 2; t += 1024) {
+      for (int t = threadIdx.x; t < len / 2; t += 256) {
         const int i = (t / stride) * 2 * stride + t % stride;
-        bitonic_pair(sk[i], sk[i + stride], base + i, s);
+        bitonic_pair(sk[i], sk[i + stride], ascending ? i : base + i, s);
       }
       __syncthreads();
     }
-  for (int t = threadIdx.x; t < len; t += 1024) keys[base + t] = sk[t];
+  for (int t = threadIdx.x; t < len; t += 256) keys[base + t] = sk[t];
 }
 
-// One stride (>= kSortLocal) of stage s over the whole array: thread t
-// handles one pair.
+// P <= kMergeMax: the P / kSortLocal ascending blocks merged in one pass.  Every
+// workgroup holds all keys in LDS; a key's place is its index in its block
+// plus, for every other block, the number of that block's keys below it
+// (binary search; the keys are unique).  The kNoKey padding goes after the
+// valid keys in block order.  Grid: P / 1024 workgroups of 1024 threads.
+constexpr int kMergeMax = 8192;
+__device__ __forceinline__ int lower_bound_lds(const uint64_t* b, int len, uint64_t key) {
+  int lo = 0;
+  for (int step = len >> 1; step > 0; step >>= 1)
+    if (b[lo + step - 1] < key) lo += step;
+  return lo + (lo < len && b[lo] < key ? 1 : 0);
+}
+__global__ __launch_bounds__(1024) void k_oh_merge_blocks(const uint64_t* __restrict__ keys,
+                                                          int P, uint64_t* __restrict__ out) {
+  __shared__ uint64_t sk[kMergeMax];
+  const int nb = P / kSortLocal;
+  for (int t = threadIdx.x; t < P; t += 1024) sk[t] = keys[t];
+  __syncthreads();
+  const int i = blockIdx.x * 1024 + threadIdx.x;
+  if (i >= P) return;
+  const int b = i / kSortLocal, li = i - b * kSortLocal;
+  const uint64_t key = sk[i];
+  int r = li;
+  if (key != kNoKey) {
+    for (int bb = 0; bb < nb; ++bb)
+      if (bb != b) r += lower_bound_lds(sk + bb * kSortLocal, kSortLocal, key);
+  } else {
+    // after every valid key, then the padding of the blocks before b
+    for (int bb = 0; bb < nb; ++bb) {
+      const int valid = lower_bound_lds(sk + bb * kSortLocal, kSortLocal, kNoKey);
+      r += bb == b ? 0 : (bb < b ? kSortLocal : valid);
+    }
+  }
+  out[r] = key;
+}
+
+// P > kMergeMax: bitonic stages past kSortLocal.  One stride (>= kSortLocal)
+// of stage s over the whole array: thread t handles one pair.
 __global__ __launch_bounds__(256) void k_bsort_global(uint64_t* __restrict__ keys, int P, int s,
                                                       int stride) {
   const int t = blockIdx.x * 256 + threadIdx.x;
@@ -1268,101 +1481,120 @@ __global__ __launch_bounds__(256) void k_bsort_global(uint64_t* __restrict__ key
   keys[i + stride] = b;
 }
 
-// Strides kSortLocal / 2 .. 1 of stage s (> kSortLocal) inside each block
-// of kSortLocal keys.
-__global__ __launch_bounds__(1024) void k_bsort_merge(uint64_t* __restrict__ keys, int s) {
+// Strides kSortLocal / 2 .. 1 of stage s (> kSortLocal) inside each block of
+// kSortLocal keys.
+__global__ __launch_bounds__(256) void k_bsort_merge(uint64_t* __restrict__ keys, int s) {
   __shared__ uint64_t sk[kSortLocal];
   const int base = blockIdx.x * kSortLocal;
-  for (int t = threadIdx.x; t < kSortLocal; t += 1024) sk[t] = keys[base + t];
+  for (int t = threadIdx.x; t < kSortLocal; t += 256) sk[t] = keys[base + t];
   __syncthreads();
   for (int stride = kSortLocal / 2; stride > 0; stride >>= 1) {
-    for (int t = threadIdx.x; t < kSortLocal / 2; t += 1024) {
+    for (int t = threadIdx.x; t < kSortLocal / 2; t += 256) {
       const int i = (t / stride) * 2 * stride + t % stride;
       bitonic_pair(sk[i], sk[i + stride], base + i, s);
     }
     __syncthreads();
   }
-  for (int t = threadIdx.x; t < kSortLocal; t += 1024) keys[base + t] = sk[t];
+  for (int t = threadIdx.x; t < kSortLocal; t += 256) keys[base + t] = sk[t];
 }
 
 // Per block of kOhBlock sorted positions and hidden chunk of 256 (one thread
-// per hidden column): for every position that opens a run inside the block
-// (the block's first position, or a target different from the previous one),
-// ohp[pos] = sum over the run's positions in this block of c_k Xc[k], in
-// position order.  Short blocks keep the sequential chains short; runs that
+// per hidden column): for every piece of a run of several rows inside the
+// block, ohp[start] = the sum over the piece's positions of c_k Xc[k], in
+// position order, where start is the piece's first position (the block's
+// first, or the run's).  Positions of one-row runs are skipped; runs that
 // cross blocks are completed by k_oh_final.
-constexpr int kOhBlock = 64;
+constexpr int kOhBlock = 64;   // one wave's lanes: the run masks come from ballots
 template <class E>
-__global__ __launch_bounds__(256) void k_oh_partial(const uint64_t* __restrict__ keys,
+__global__ __launch_bounds__(256) void k_oh_partial(const uint64_t* __restrict__ keys, int P,
                                                     const char* __restrict__ Xc, int H,
+                                                    int rows_pad,
                                                     const Counters* __restrict__ ctr,
                                                     const float* __restrict__ rs,
                                                     float* __restrict__ ohp) {
-  __shared__ uint64_t sk[kOhBlock + 1];
+  // sk[q + 1] = key of block position q; sk[0], sk[kOhBlock + 1] the neighbours
+  __shared__ uint64_t sk[kOhBlock + 2];
   __shared__ float sc[kOhBlock];
+  __shared__ uint64_t masks[2];   // positions in runs of several rows; piece ends
   const int base = blockIdx.x * kOhBlock;
-  const float c = ctr->c;
-  if (threadIdx.x < kOhBlock) {
-    const uint64_t key = keys[base + threadIdx.x];
-    sk[threadIdx.x] = key;
-    sc[threadIdx.x] = key == kNoKey ? 0.f : (rs ? c * rs[(uint32_t)key] : c);
+  if (threadIdx.x < kOhBlock + 2) {
+    const int p = base + (int)threadIdx.x - 1;
+    sk[threadIdx.x] = p >= 0 && p < P ? keys[p] : kNoKey;
   }
-  if (threadIdx.x == 0) sk[kOhBlock] = kNoKey;
   __syncthreads();
+  if (threadIdx.x < kOhBlock) {
+    const int q = threadIdx.x;
+    const uint64_t key = sk[q + 1];
+    const bool valid = key != kNoKey;
+    const bool ps = valid && sk[q] != kNoKey && key_target(sk[q]) == key_target(key);
+    const bool ns = valid && sk[q + 2] != kNoKey && key_target(sk[q + 2]) == key_target(key);
+    const bool m = ps || ns;
+    const float c = ctr->c;
+    sc[q] = m ? (rs ? c * rs[(uint32_t)key] : c) : 0.f;
+    const uint64_t bm = __ballot(m), be = __ballot(m && !ns);
+    if (q == 0) {
+      masks[0] = bm;
+      masks[1] = be;
+    }
+  }
+  __syncthreads();
+  const uint64_t mm = uniform64(masks[0]), me = uniform64(masks[1]);
   const int h = blockIdx.y * 256 + threadIdx.x;
-  if (h >= H || sk[0] == kNoKey) return;
+  if (mm == 0 || h >= H) return;
   float x[kOhBlock];
 #pragma unroll
   for (int q = 0; q < kOhBlock; ++q) {
-    const uint64_t key = sk[q];
-    const int64_t row = key == kNoKey ? 0 : (int64_t)(uint32_t)key;
-    if constexpr (E::kBytes == 2)
-      x[q] = bf2f(((const uint16_t*)Xc)[row * H + h]);
-    else
-      x[q] = ((const float*)Xc)[row * H + h];
+    x[q] = 0.f;
+    const int64_t row = (uint32_t)sk[q + 1];
+    if (((mm >> q) & 1) && row < rows_pad) {
+      if constexpr (E::kBytes == 2)
+        x[q] = bf2f(((const uint16_t*)Xc)[row * H + h]);
+      else
+        x[q] = ((const float*)Xc)[row * H + h];
+    }
   }
   float acc = 0.f;
   int start = 0;
 #pragma unroll
   for (int q = 0; q < kOhBlock; ++q) {
-    const uint64_t key = sk[q];
-    if (key != kNoKey) {
-      acc = fmaf(sc[q], x[q], acc);
-      const uint64_t next = sk[q + 1];
-      if (q == kOhBlock - 1 || next == kNoKey || (next >> 32) != (key >> 32)) {
-        ohp[(int64_t)(base + start) * H + h] = acc;
-        acc = 0.f;
-        start = q + 1;
-      }
+    if (!((mm >> q) & 1)) {
+      start = q + 1;
+      continue;
+    }
+    acc = fmaf(sc[q], x[q], acc);
+    if (q == kOhBlock - 1 || ((me >> q) & 1)) {
+      ohp[(int64_t)(base + start) * H + h] = acc;
+      acc = 0.f;
+      start = q + 1;
     }
   }
 }
 
-// Runs that cross kOhBlock-position blocks.  Every real run start (the first
-// position, or a target different from the previous position's) records
-// map[target] = its position.  The run holding a block's last position, when
-// it starts inside the block, is completed by that block: the partials that
-// the following blocks' first positions hold for the same target are added to
-// its own, in block order.  Grid: blocks of kOhBlock positions x hidden
-// chunks of 256.
-__device__ __forceinline__ uint32_t key_target(uint64_t k) { return (uint32_t)(k >> 32); }
-
-__global__ __launch_bounds__(256) void k_oh_final(const uint64_t* __restrict__ keys, int H,
-                                                  int rows_pad, float* __restrict__ ohp,
+// map and cross-block runs.  Every run start (the first position, or a
+// target different from the previous position's) sets map[target].  The run
+// of several rows that holds a block's last position, when it starts inside
+// the block, is completed by that block: the partials that the following
+// blocks' first positions hold for the same target are added to its own, in
+// block order.  Grid: blocks of kOhBlock positions x hidden chunks of 256.
+__global__ __launch_bounds__(256) void k_oh_final(const uint64_t* __restrict__ keys, int P,
+                                                  int H, int rows_pad, float* __restrict__ ohp,
                                                   int* __restrict__ map) {
   __shared__ int open_at;
   const int base = blockIdx.x * kOhBlock;
   const int t = threadIdx.x;
-  const uint64_t key = t < kOhBlock ? keys[base + t] : kNoKey;
-  const bool prev_same = t < kOhBlock && base + t > 0 && keys[base + t - 1] != kNoKey &&
-                         key_target(keys[base + t - 1]) == key_target(key);
-  const bool real = key != kNoKey && !prev_same;
-  if (blockIdx.y == 0 && real) map[key_target(key)] = base + t;
+  const int p = base + t;
+  const uint64_t key = t < kOhBlock ? keys[p] : kNoKey;
+  const bool prev_same = t < kOhBlock && p > 0 && keys[p - 1] != kNoKey &&
+                         key_target(keys[p - 1]) == key_target(key);
+  const bool next_same = t < kOhBlock && key != kNoKey && p + 1 < P && keys[p + 1] != kNoKey &&
+                         key_target(keys[p + 1]) == key_target(key);
+  const bool start = key != kNoKey && !prev_same;
+  if (blockIdx.y == 0 && start) map[key_target(key)] = next_same ? -2 - p : (int)(uint32_t)key;
   if (t == 0) open_at = -1;
   __syncthreads();
   const uint64_t klast = keys[base + kOhBlock - 1];
-  // the real start of the run that holds the block's last position
-  if (real && klast != kNoKey && key_target(klast) == key_target(key)) open_at = t;
+  // the start of the run of several rows that holds the block's last position
+  if (start && next_same && key_target(klast) == key_target(key)) open_at = t;
   __syncthreads();
   const int i0 = open_at;
   const int h = blockIdx.y * 256 + t;

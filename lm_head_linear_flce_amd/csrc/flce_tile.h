@@ -182,26 +182,41 @@ struct LoadDirect::Frag {
 //         copies chunk t % 32 of K rows t / 32 + 8 i.
 //   fp32: 32 K rows of 1 KiB, no permutation; thread t copies chunk t % 64 of
 //         K rows t / 64 + 4 i.
-template <class E> struct LoadMN;
+//   kFar: K * ldb may pass 2^31 bytes; each step then gets a descriptor that
+//         starts at its first K row (64-bit base), at a few scalar
+//         instructions per step that the common case does without.
+template <class E, bool kFar = false> struct LoadMN;
 
-template <>
-struct LoadMN<BF16> {
+template <bool kFar>
+struct LoadMN<BF16, kFar> {
   static constexpr bool kTransposed = true;
   i32x4 v[8];
   template <class E>
   __device__ __forceinline__ void issue_part(const Opnd& o, int s, int part, bool live,
                                              int tid) {
     const int c = tid & 31, kr = tid >> 5;
-    // one descriptor for the whole operand: the plans keep K * ldb below
-    // 2^31, so live offsets do too; a step that is not `live` reads at 2^31
-    // and up (below 2^32: the rows it adds are within the tile), past the
-    // descriptor's end, so it loads zeros
-    const rsrc_t r = make_rsrc(o.base, o.bytes < 0x7FFFFFFF ? o.bytes : 0x7FFFFFFF);
-    const uint32_t off = live ? (uint32_t)(s * BF16::kKStep + kr) * (uint32_t)o.ldb + c * 16
-                              : 0x80000000u;
+    if constexpr (kFar) {
+      // the descriptor starts at the step's first K row, so the offsets stay
+      // below 64 rows; a step that is not `live` gets an empty descriptor
+      const int64_t skip = (int64_t)s * BF16::kKStep * o.ldb;
+      const int64_t left = o.bytes - skip;
+      const rsrc_t r =
+          make_rsrc(o.base + skip, live ? (left < 0x7FFFFFFF ? left : 0x7FFFFFFF) : 0);
+      const int off = kr * o.ldb + c * 16;
 #pragma unroll
-    for (int i = 2 * part; i < 2 * part + 2; ++i)
-      v[i] = bload128(r, (int)(off + (uint32_t)(8 * i) * (uint32_t)o.ldb));
+      for (int i = 2 * part; i < 2 * part + 2; ++i) v[i] = bload128(r, off + 8 * i * o.ldb);
+    } else {
+      // one descriptor for the whole operand (K * ldb below 2^31, so live
+      // offsets are too); a step that is not `live` reads at 2^31 and up
+      // (below 2^32: the rows it adds are within the tile), past the
+      // descriptor's end, so it loads zeros
+      const rsrc_t r = make_rsrc(o.base, o.bytes < 0x7FFFFFFF ? o.bytes : 0x7FFFFFFF);
+      const uint32_t off = live ? (uint32_t)(s * BF16::kKStep + kr) * (uint32_t)o.ldb + c * 16
+                                : 0x80000000u;
+#pragma unroll
+      for (int i = 2 * part; i < 2 * part + 2; ++i)
+        v[i] = bload128(r, (int)(off + (uint32_t)(8 * i) * (uint32_t)o.ldb));
+    }
   }
   template <class E>
   __device__ __forceinline__ void issue(const Opnd& o, int s, bool live, int tid) {
@@ -246,21 +261,31 @@ struct LoadMN<BF16> {
   };
 };
 
-template <>
-struct LoadMN<F32> {
+template <bool kFar>
+struct LoadMN<F32, kFar> {
   static constexpr bool kTransposed = true;
   i32x4 v[8];
   template <class E>
   __device__ __forceinline__ void issue_part(const Opnd& o, int s, int part, bool live,
                                              int tid) {
     const int c = tid & 63, kr = tid >> 6;
-    // one descriptor per operand, as for bf16
-    const rsrc_t r = make_rsrc(o.base, o.bytes < 0x7FFFFFFF ? o.bytes : 0x7FFFFFFF);
-    const uint32_t off = live ? (uint32_t)(s * F32::kKStep + kr) * (uint32_t)o.ldb + c * 16
-                              : 0x80000000u;
+    // descriptors as for bf16
+    if constexpr (kFar) {
+      const int64_t skip = (int64_t)s * F32::kKStep * o.ldb;
+      const int64_t left = o.bytes - skip;
+      const rsrc_t r =
+          make_rsrc(o.base + skip, live ? (left < 0x7FFFFFFF ? left : 0x7FFFFFFF) : 0);
+      const int off = kr * o.ldb + c * 16;
 #pragma unroll
-    for (int i = 2 * part; i < 2 * part + 2; ++i)
-      v[i] = bload128(r, (int)(off + (uint32_t)(4 * i) * (uint32_t)o.ldb));
+      for (int i = 2 * part; i < 2 * part + 2; ++i) v[i] = bload128(r, off + 4 * i * o.ldb);
+    } else {
+      const rsrc_t r = make_rsrc(o.base, o.bytes < 0x7FFFFFFF ? o.bytes : 0x7FFFFFFF);
+      const uint32_t off = live ? (uint32_t)(s * F32::kKStep + kr) * (uint32_t)o.ldb + c * 16
+                                : 0x80000000u;
+#pragma unroll
+      for (int i = 2 * part; i < 2 * part + 2; ++i)
+        v[i] = bload128(r, (int)(off + (uint32_t)(4 * i) * (uint32_t)o.ldb));
+    }
   }
   template <class E>
   __device__ __forceinline__ void issue(const Opnd& o, int s, bool live, int tid) {
@@ -500,43 +525,24 @@ __device__ __forceinline__ int acc_col(int wn, int j, int lane) {
 //   emit(o, x0, v)          store chunk v (8 bf16, inner x0 .. x0 + 7) of row o
 // The region must be free (after the K loop's last barrier) and only this
 // wave touches it, so no barrier is needed between the two phases.
-// corr(i, j, g) -> f32x4   subtracted from the values of registers (i, j,
-//                          4 g .. 4 g + 3) before the rounding (NoCorr4: none)
-struct NoCorr4 {
-  __device__ __forceinline__ f32x4 operator()(int, int, int) const {
-    return f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-};
-
-template <class Val, class Emit, class Corr>
+template <class Val, class Emit>
 __device__ __forceinline__ void store_quarter_bf16(lds_t* region, int lane, Val&& val,
-                                                   Emit&& emit, Corr&& corr) {
+                                                   Emit&& emit) {
   typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
   typedef __attribute__((address_space(3))) i32x4 lds_i32x4;
-  // the corrections of column block j + 1 are fetched while block j is packed
-  f32x4 cur[16], nxt[16];
-#pragma unroll
-  for (int q = 0; q < 16; ++q) cur[q] = corr(q >> 2, 0, q & 3);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int o = 32 * j + (lane & 31);
-    if (j + 1 < 4) {
-#pragma unroll
-      for (int q = 0; q < 16; ++q) nxt[q] = corr(q >> 2, j + 1, q & 3);
-    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int u = 8 * i + 2 * g + (lane >> 5);
-        const f32x4 cv = cur[4 * i + g];
         i32x2 pk;
-        pk[0] = pack_bf16(val(i, j, 4 * g) - cv[0], val(i, j, 4 * g + 1) - cv[1]);
-        pk[1] = pack_bf16(val(i, j, 4 * g + 2) - cv[2], val(i, j, 4 * g + 3) - cv[3]);
+        pk[0] = pack_bf16(val(i, j, 4 * g), val(i, j, 4 * g + 1));
+        pk[1] = pack_bf16(val(i, j, 4 * g + 2), val(i, j, 4 * g + 3));
         *(lds_i32x2*)(region + o * 256 + ((u ^ (o & 31)) << 3)) = pk;
       }
-#pragma unroll
-    for (int q = 0; q < 16; ++q) cur[q] = nxt[q];
   }
   const int c = lane & 15;
 #pragma unroll
@@ -548,21 +554,27 @@ __device__ __forceinline__ void store_quarter_bf16(lds_t* region, int lane, Val&
   }
 }
 
-template <class Val, class Emit>
-__device__ __forceinline__ void store_quarter_bf16(lds_t* region, int lane, Val&& val,
-                                                   Emit&& emit) {
-  store_quarter_bf16(region, lane, val, emit, NoCorr4{});
-}
-
 // fp32 counterpart for read-modify-write epilogues: the same quarter, in two
 // halves of 64 rows (j = 0, 1 then j = 2, 3) of 512 B each, 16-byte unit u of
 // row o kept at u ^ (o % 32).  For every 16-byte chunk (4 fp32, inner x0 ..
 // x0 + 3) of row o, `load(o, x0)` fetches the old value (all of a half's
 // loads are issued before its LDS traffic) and `store(o, x0, v)` writes v.
-template <class Load, class Store, class Corr>
+// `fix(hf, region)` may change the staged half (rows 64 hf .. 64 hf + 63,
+// FP32, laid out as above) between the two phases.  With NoLoad for `load`
+// the tile is stored as it is (a plain store through the same layout).
+struct NoFix {
+  __device__ __forceinline__ void operator()(int, lds_t*) const {}
+};
+struct NoLoad {
+  __device__ __forceinline__ f32x4 operator()(int, int) const {
+    return f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+};
+
+template <class Load, class Store, class Fix>
 __device__ __forceinline__ void rmw_quarter_f32(lds_t* region, int lane,
                                                 const f32x16 (&acc)[4][4], Load&& load,
-                                                Store&& store, Corr&& corr) {
+                                                Store&& store, Fix&& fix) {
   typedef __attribute__((address_space(3))) i32x4 lds_i32x4;
   const int c = lane & 31;
 #pragma unroll
@@ -578,19 +590,22 @@ __device__ __forceinline__ void rmw_quarter_f32(lds_t* region, int lane,
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int u = 8 * i + 2 * g + (lane >> 5);
-          const f32x4 cv = corr(i, j, g);
-          const f32x4 v = {acc[i][j][4 * g] - cv[0], acc[i][j][4 * g + 1] - cv[1],
-                           acc[i][j][4 * g + 2] - cv[2], acc[i][j][4 * g + 3] - cv[3]};
+          const f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1], acc[i][j][4 * g + 2],
+                           acc[i][j][4 * g + 3]};
           *(lds_i32x4*)(region + o * 512 + ((u ^ (o & 31)) << 4)) = __builtin_bit_cast(i32x4, v);
         }
     }
+    fix(hf, region);
 #pragma unroll
     for (int t = 0; t < 32; ++t) {
       const int o = 2 * t + (lane >> 5);
       const f32x4 v = __builtin_bit_cast(
           f32x4, *(const lds_i32x4*)(region + o * 512 + ((c ^ (o & 31)) << 4)));
-      store(64 * hf + o, 4 * c, f32x4{old[t][0] + v[0], old[t][1] + v[1], old[t][2] + v[2],
-                                      old[t][3] + v[3]});
+      if constexpr (__is_same(__remove_cvref(Load), NoLoad))
+        store(64 * hf + o, 4 * c, v);
+      else
+        store(64 * hf + o, 4 * c, f32x4{old[t][0] + v[0], old[t][1] + v[1], old[t][2] + v[2],
+                                        old[t][3] + v[3]});
     }
   }
 }
@@ -599,7 +614,7 @@ template <class Load, class Store>
 __device__ __forceinline__ void rmw_quarter_f32(lds_t* region, int lane,
                                                 const f32x16 (&acc)[4][4], Load&& load,
                                                 Store&& store) {
-  rmw_quarter_f32(region, lane, acc, load, store, NoCorr4{});
+  rmw_quarter_f32(region, lane, acc, load, store, NoFix{});
 }
 
 // Maps a launch index to a work item so that items i, i+1, ... run on the same

@@ -302,3 +302,17 @@ def test_noalloc_scratch_constant_matches_header():
 ])
 def test_convert_grads_host_checks(args, code):
     assert F.flce_convert_grads(*args) == code
+
+
+@pytest.mark.parametrize("B,T,H,V", [(1, 262144, 4096, 151936), (1, 131072, 4096, 152064),
+                                     (1, 65536, 8192, 152064), (8, 8192, 8192, 151936),
+                                     (1, 1 << 20, 1024, 32000)])
+def test_long_sequences_are_accepted(B, T, H, V):
+    # N * H well past 2^29: the kernels address the FP32 sums per token tile
+    # and, past 2^31 bytes of rows, rebase the dW loaders' descriptors per K
+    # step, so only the workspace grows (linearly in N), never with N * V
+    for dt in (F.FLCE_DTYPE_BF16, F.FLCE_DTYPE_F32):
+        ws = F.flce_workspace_size(B, T, H, V, dt)
+        assert 0 < ws < B * T * V * 2
+        cws = F.flce_chunked_workspace_size(B, T, H, V, dt)
+        assert 0 < cws < B * T * V * 2

@@ -46,3 +46,43 @@ def test_more_than_2048_token_tiles():
     gdw = dW.double().cpu().numpy()
     assert oracle.cosine(gdw, rdw) >= TOL["bf16"]["cos"]
     assert np.abs(gdw - rdw).max() <= TOL["bf16"]["maxabs"] * np.abs(rdw).max()
+
+
+def test_rows_times_hidden_past_2_29():
+    """N * H = 2^29 (262144 rows of H = 2048, 1 GiB of bf16 hidden states): the
+    FP32 dX sums (2 GiB) and the one-hot row sums pass 2^31 bytes and the dW
+    contraction runs over 0.5 Gi elements of X.  Sampled lse and dX rows (every
+    64th token tile's edges) and all of dW (V = 333) against the oracle."""
+    T, H, V = 262144, 2048, 333
+    w = synth.make_workload("long_rows", B=1, T=T, H=H, V=V, dtype="bf16", seed=7721,
+                            x_rms=True, labels="zipf", mask="prefix", mask_arg=4096,
+                            shift=True, reduction="mean")
+    print(f"[long-rows] N={w.N} H={H} V={V} bf16", flush=True)
+    X = torch.from_numpy(w.X).to(DEV).to(torch.bfloat16)
+    W = torch.from_numpy(w.W).to(DEV).to(torch.bfloat16)
+    lab = torch.from_numpy(w.labels).to(DEV)
+    loss, lse, n_valid, status = F.forward(X, W, lab, w.ignore_index, w.shift, w.reduction)
+    dX, dW, bstatus = F.backward(X, W, lab, lse, ignore_index=w.ignore_index, shift=w.shift,
+                                 reduction=w.reduction)
+    torch.cuda.synchronize()
+    assert int(status) == 0 and int(bstatus) == 0
+    full = oracle.forward_rows(w.X, w.W, w.labels, ignore_index=w.ignore_index, shift=True,
+                               chunk=4096)
+    assert int(n_valid) == full["n_valid"]
+    assert abs(float(loss) - full["loss"]) <= TOL["bf16"]["loss_rel"] * abs(full["loss"])
+    vrows = np.flatnonzero(full["valid"])
+    edges = np.arange(0, len(vrows), 64 * 256)
+    rows = np.unique(np.concatenate([vrows[edges], vrows[np.maximum(edges - 1, 0)],
+                                     vrows[-2:], [0, w.N - 1]]))
+    got_lse = lse.double().cpu().numpy()
+    sel = rows[full["valid"][rows]]
+    assert np.abs(got_lse[sel] - full["lse"][sel]).max() <= LSE_ABS
+    c = 1.0 / full["n_valid"]
+    rdx = oracle.dx_rows(w.X, w.W, full["y"], full["valid"], full["lse"], c, rows)
+    gdx = dX.double().cpu().numpy()[rows]
+    assert oracle.cosine(gdx, rdx) >= TOL["bf16"]["cos"]
+    assert np.abs(gdx - rdx).max() <= TOL["bf16"]["maxabs"] * np.abs(rdx).max()
+    rdw = oracle.dw_rows(w.X, w.W, full["y"], full["valid"], full["lse"], c, np.arange(V))
+    gdw = dW.double().cpu().numpy()
+    assert oracle.cosine(gdw, rdw) >= TOL["bf16"]["cos"]
+    assert np.abs(gdw - rdw).max() <= TOL["bf16"]["maxabs"] * np.abs(rdw).max()

@@ -428,7 +428,7 @@ int backward_impl(const Plan& pl, const Shard& sh, const void* X, const void* W,
                      (const float*)dx32, (int)pl.dx_split, (int64_t)pl.rows_pad * pl.H,
                      (const int*)rowpos, (int)pl.N, (int)pl.H, (char*)dX, dx_f32,
                      (const char*)W, (const int*)tgt, (int)pl.V, (const Counters*)ctr,
-                     (const float*)rs);
+                     (const float*)rs, (const float*)nullptr);
   L.check();
   return L.err == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }
@@ -465,6 +465,7 @@ struct ChunkPlan {
   int64_t o_blk;
   int64_t o_rs;
   int64_t o_part, o_slab, o_dx32, o_dx32p;
+  int64_t o_fk, o_mrow, o_redo, o_redo_t, o_xs;   // per-row factors, second pass, scaled rows
   int64_t P, o_keys, o_oh, o_map;   // one-hot sums for dW
   int64_t total;
 };
@@ -518,6 +519,11 @@ int make_chunk_plan(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, int64
   q.o_cctr = take(sizeof(Counters) * q.nchunks);
   q.o_blk = take(prep_blk_bytes(q.N));
   q.o_part = take(8 * 2 * q.VT * q.C);
+  q.o_fk = take(4 * q.rows_pad);
+  q.o_mrow = take(4 * q.rows_pad);
+  q.o_redo = take(4 * q.rows_pad);
+  q.o_redo_t = take(4 * (q.C / kTile));
+  q.o_xs = take(q.C * H * q.es);
   q.o_slab = take(q.C * q.Vp * q.es);
   q.dx_split = dx_split_for(cdiv(H, kTile), q.C / kTile, FLCE_DX_TILES_CHUNKED);
   q.o_dx32 = take(4 * q.rows_pad * H);
@@ -555,6 +561,11 @@ int chunked_impl(const ChunkPlan& pl, const void* X, const void* W, const int64_
   char* slab = ws + pl.o_slab;
   float* dx32 = (float*)(ws + pl.o_dx32);
   float* dx32p = (float*)(ws + pl.o_dx32p);
+  float* fk = (float*)(ws + pl.o_fk);
+  float* mrow = (float*)(ws + pl.o_mrow);
+  int* redo = (int*)(ws + pl.o_redo);
+  int* redo_t = (int*)(ws + pl.o_redo_t);
+  char* xs = ws + pl.o_xs;
   const int rows_pad = (int)pl.rows_pad;
   const int row_bytes = (int)(pl.H * E::kBytes);
   const int C = (int)pl.C, TTc = C / kTile, HT = (int)cdiv(pl.H, kTile);
@@ -577,7 +588,8 @@ int chunked_impl(const ChunkPlan& pl, const void* X, const void* W, const int64_
   int* oh_map = (int*)(ws + pl.o_map);
   onehot_sums<E>(pl.P, pl.rows_pad, pl.H, pl.V, tgt, ctr, xc, rs, (uint64_t*)(ws + pl.o_keys),
                  oh, oh_map, L);
-  if (L.err == hipSuccess) L.err = allow_big_lds<k_chunk_z<E>>();
+  if (L.err == hipSuccess) L.err = allow_big_lds<k_chunk_z<E, 0>, kChunkZLdsBytes>();
+  if (L.err == hipSuccess) L.err = allow_big_lds<k_chunk_z<E, 1>, kChunkZLdsBytes>();
   if (L.err == hipSuccess) L.err = allow_big_lds<k_bwd<E>, kBwdLdsBytes>();
   for (int64_t ch = 0; ch < pl.nchunks && L.err == hipSuccess; ++ch) {
     ChunkArgs ca;
@@ -600,26 +612,31 @@ int chunked_impl(const ChunkPlan& pl, const void* X, const void* W, const int64_
     ca.C = C;
     ca.VT = (int)pl.VT;
     ca.TTc = TTc;
+    ca.fk = fk;
+    ca.mrow = mrow;
+    ca.redo = redo;
+    ca.redo_t = redo_t;
+    ca.Xs = xs;
+    const int nbz = (int)pad8(pl.VT * TTc);
     {
-      const int nb = (int)pad8(pl.VT * TTc);
       Timed t("k_chunk_z", stream);
-      hipLaunchKernelGGL(k_chunk_z<E>, dim3((unsigned)nb), dim3(kThreads), kLdsBytes, stream,
+      hipLaunchKernelGGL((k_chunk_z<E, 0>), dim3((unsigned)nbz), dim3(kThreads), kChunkZLdsBytes,
+                         stream,
                          ca);
       L.check();
     }
-    hipLaunchKernelGGL(k_chunk_lse, dim3((unsigned)(C / 4)), dim3(256), 0, stream, ca);
+    hipLaunchKernelGGL(k_chunk_lse<E>, dim3((unsigned)(C / 4)), dim3(256), 0, stream, ca);
     L.check();
-    // rows strided over at most 1024 workgroup rows: the chunk past the valid
-    // rows (the host does not know n) exits at once
-    constexpr int per = 16 / E::kBytes;
-    hipLaunchKernelGGL(k_chunk_scale<E>,
-                       dim3((unsigned)cdiv(pl.Vp, 256 * per), (unsigned)std::min(C, 1024)),
-                       dim3(256), 0, stream, ca, 0, (int)pl.Vp);
+    // the rows whose largest logit lies far above the target logit, against
+    // their max (token tiles without such a row exit at once)
+    hipLaunchKernelGGL((k_chunk_z<E, 1>), dim3((unsigned)nbz), dim3(kThreads), kChunkZLdsBytes,
+                       stream, ca);
     L.check();
-    // dX and dW tiles of the chunk, one vocabulary block per launch
+    // dX and dW tiles of the chunk, one vocabulary block per launch; the dW
+    // tiles contract the slab with the rows scaled by their factor
     BwdArgs b;
     b.W = (const char*)W;
-    b.Xc = ca.Xc;
+    b.Xc = xs;
     b.lse2 = lse2;
     b.rs = rs;
     b.tgt = tgt;
@@ -678,7 +695,7 @@ int chunked_impl(const ChunkPlan& pl, const void* X, const void* W, const int64_
   hipLaunchKernelGGL(k_dx_final<E>, dim3((unsigned)cdiv(pl.N, 4)), dim3(256), 0, stream,
                      (const float*)dx32, 1, (int64_t)0, (const int*)rowpos, (int)pl.N,
                      (int)pl.H, (char*)dX, grad_f32, (const char*)W, (const int*)tgt,
-                     (int)pl.V, (const Counters*)ctr, (const float*)rs);
+                     (int)pl.V, (const Counters*)ctr, (const float*)rs, (const float*)fk);
   L.check();
   return L.err == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
 }

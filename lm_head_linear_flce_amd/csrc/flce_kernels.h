@@ -965,18 +965,32 @@ void k_bwd(BwdArgs cur, BwdArgs nxt, int nb_dx, int nb_dw, int nb_g, int dw_firs
 
 // ---------------------------------------------------------------------------
 // Chunked mode: loss, lse, dX and dW in one call, over chunks of C compacted
-// rows, with the chunk's softmax gradient over the whole vocabulary held in a
-// [C, Vp] slab (the pages' row-chunk recipe: three contractions instead of
-// four, memory proportional to the chunk).  Per chunk:
-//   k_chunk_z      logits tiles of the chunk's rows; each (row, 128-wide half
-//                  of a vocabulary tile) keeps its max M (log2 units) and
-//                  s = sum 2^(z log2e - M); the slab gets e = 2^(z log2e - M)
-//   k_chunk_lse    the rows' lse from the partials, row losses, the chunk's
-//                  counters (rows in the chunk)
-//   k_chunk_scale  G = c e 2^(M - lse2), in place
-//   k_bwd          dX and dW tiles per vocabulary block of the slab (dW added
-//                  to the previous chunks' sum)
+// rows, with the chunk's softmax over the whole vocabulary held in a [C, Vp]
+// slab (the pages' row-chunk recipe: three contractions instead of four,
+// memory proportional to the chunk).  The slab keeps e = 2^(z log2e - R_k)
+// against a per-row reference R_k, so the gradient G = f_k e needs no pass
+// over the slab: f_k = c_k 2^(R_k - lse2_k) goes into the FP32 dX sums at the
+// end and into a scaled copy of the chunk's rows for the dW tiles.  R_k is
+// the row's target logit (known before the logits; the target's own entry is
+// then 1 up to the two FP32 sums' rounding, so G at the target keeps its FP32
+// precision), unless the row's largest z log2e lies more than kRefSpan above
+// it (a target more than 44 nats below the row's best): such a row is stored
+// again against its max by a second pass, so every stored row's largest
+// entry lies in [1, 2^64] (no overflow, and what underflows is negligible
+// next to it).  Per chunk:
+//   k_chunk_z (pass 0)  logits tiles of the chunk's rows; each (row, 128-wide
+//                       half of a vocabulary tile) keeps its max M (log2
+//                       units) and s = sum 2^(z log2e - M); the slab gets e
+//   k_chunk_lse         the rows' lse from the partials, row losses, f_k, the
+//                       rows' flags for the second pass, the chunk's rows
+//                       scaled by f_k (Xs), the chunk's counters
+//   k_chunk_z (pass 1)  the flagged rows' slab rows against their max (token
+//                       tiles without a flagged row exit at once)
+//   k_bwd               dX and dW tiles per vocabulary block of the slab (dW
+//                       added to the previous chunks' sum)
 // ---------------------------------------------------------------------------
+constexpr float kRefSpan = 64.f;
+constexpr int kChunkZLdsBytes = kLdsBytes + 2 * kTile * 4;   // + the tokens' references, flags
 struct ChunkArgs {
   const char* W;        // [V, H]
   const char* Xc;       // the chunk's first compacted row
@@ -990,6 +1004,11 @@ struct ChunkArgs {
   float* lse_c;         // [rows_pad] lse per compacted row
   float* lse2;          // [rows_pad] lse * log2(e)
   float* rloss;         // [rows_pad] row losses lse - z_target
+  float* fk;            // [rows_pad] G = fk * e per row
+  float* mrow;          // [rows_pad] the row's max of z log2e
+  int* redo;            // [rows_pad] 1: the row is stored against its max
+  int* redo_t;          // [C / 256] some row of the chunk's token tile is
+  char* Xs;             // [C, H] the chunk's rows times fk (the dW operand)
   int H, V, Vp, C, row0, VT, TTc;
 };
 
@@ -999,19 +1018,32 @@ __device__ __forceinline__ int chunk_rows(const ChunkArgs& a) {
 }
 
 // Epilogue of a logits tile of the chunked mode: per (token, 128-row half of
-// the tile) the max M of z log2e and s = sum 2^(z log2e - M), and
-// e = 2^(z log2e - M) into the slab.  kMasked: vocabulary rows
-// 32i + 8g + q >= vlim (the lane's offset already in vlim) lie past V and
-// count as absent; full tiles skip the test.
-template <class E, bool kMasked>
+// the tile) the max M of z log2e and s = sum 2^(z log2e - M) (pass 0), and
+// e = 2^(z log2e - M) 2^(M - R) into the slab, R the token's reference
+// (token rows past the chunk's rows store zeros; pass 1 stores the flagged
+// tokens only).  kMasked: vocabulary rows 32i + 8g + q >= vlim (the lane's
+// offset already in vlim) lie past V and count as absent; full tiles skip
+// the test.
+template <class E, int kPass, bool kMasked>
 __device__ __forceinline__ void z_store(const ChunkArgs& a, const f32x16 (&acc)[4][4], int vt,
                                         int tau, int wm, int wn, int lane, int vlim,
                                         lds_t* smem) {
-  // lanes l and l ^ 32 hold the two halves of the 64 rows a wave keeps per
-  // token column
-  float m2[4], sum[4];
+  const int nc = chunk_rows(a);
+  // the tokens' references and (second pass) flags, staged in LDS by z_tile
+  typedef const __attribute__((address_space(3))) float lds_cfloat;
+  lds_cfloat* zref = (lds_cfloat*)(smem + kLdsBytes);
+  lds_cint* zflag = (lds_cint*)(smem + kLdsBytes + kTile * 4);
+  float ref[4];
+  unsigned keep[4];   // bit c: token 32 j + c of the wave is stored
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
+    ref[j] = zref[acc_col(wn, j, lane)];
+    keep[j] = kPass == 0 ? ~0u : (unsigned)__ballot(zflag[acc_col(wn, j, lane)] != 0);
+  }
+  // lanes l and l ^ 32 hold the two halves of the 64 rows a wave keeps per
+  // token column; each block j's max is taken right before its values
+  float m2[4], sum[4], sc[4];
+  auto begin = [&](int j) {
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -1021,24 +1053,35 @@ __device__ __forceinline__ void z_store(const ChunkArgs& a, const f32x16 (&acc)[
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     m2[j] = mx == -INFINITY ? 0.f : mx * kLog2e;
     sum[j] = 0.f;
-  }
+    const bool live = tau * kTile + acc_col(wn, j, lane) < nc;
+    sc[j] = live ? __builtin_amdgcn_exp2f(m2[j] - ref[j]) : 0.f;
+  };
   auto val = [&](int i, int j, int r) {
     const float e = __builtin_amdgcn_exp2f(fmaf(acc[i][j][r], kLog2e, -m2[j]));
     const float v = (!kMasked || 32 * i + 8 * (r >> 2) + (r & 3) < vlim) ? e : 0.f;
     sum[j] += v;
-    return v;
+    return v * sc[j];
   };
   const rsrc_t er = make_rsrc(a.E, (int64_t)a.C * a.Vp * E::kBytes);
   const int wave = threadIdx.x >> 6;
   if constexpr (E::kBytes == 2) {
     const int tok0 = tau * kTile + wn * 128, voc0 = vt * kTile + wm * 128;
-    store_quarter_bf16(smem + wave * 32768, lane, val, [&](int o, int x0, i32x4 v) {
-      __builtin_amdgcn_raw_buffer_store_b128(v, er, ((tok0 + o) * a.Vp + voc0 + x0) * 2, 0, 0);
-    });
+    store_quarter_bf16(
+        smem + wave * 32768, lane, val,
+        [&](int o, int x0, i32x4 v) {
+          // row o of the quarter is token tok0 + o (= column 32 j + c of the wave)
+          const bool st = (keep[o >> 5] >> (o & 31)) & 1;
+          __builtin_amdgcn_raw_buffer_store_b128(
+              v, er, st ? ((tok0 + o) * a.Vp + voc0 + x0) * 2 : (int)0x80000000u, 0, 0);
+        },
+        begin);
   } else {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+      __builtin_amdgcn_sched_barrier(0);
+      begin(j);
       const int tok = tau * kTile + acc_col(wn, j, lane);
+      const bool st = (keep[j] >> (lane & 31)) & 1;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -1046,11 +1089,13 @@ __device__ __forceinline__ void z_store(const ChunkArgs& a, const f32x16 (&acc)[
           const int row0 = acc_row(wm, i, 4 * g, lane);
           const f32x4 fv = {val(i, j, 4 * g), val(i, j, 4 * g + 1), val(i, j, 4 * g + 2),
                             val(i, j, 4 * g + 3)};
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, fv), er,
-                                                 (tok * a.Vp + vt * kTile + row0) * 4, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(
+              __builtin_bit_cast(i32x4, fv), er,
+              st ? (tok * a.Vp + vt * kTile + row0) * 4 : (int)0x80000000u, 0, 0);
         }
     }
   }
+  if constexpr (kPass == 1) return;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const float s2 = sum[j] + __shfl_xor(sum[j], 32);
@@ -1061,13 +1106,17 @@ __device__ __forceinline__ void z_store(const ChunkArgs& a, const f32x16 (&acc)[
 }
 
 // Logits tile (vocabulary tile vt x token tile tau of the chunk).
-template <class E>
+template <class E, int kPass>
 __device__ __forceinline__ void z_tile(const ChunkArgs& a, int b, lds_t* smem) {
+  // pass 0 clears the second pass's token-tile flags (k_chunk_lse sets them)
+  if (kPass == 0 && b == 0)
+    for (int t = threadIdx.x; t < a.TTc; t += kThreads) a.redo_t[t] = 0;
   const int TTn = (chunk_rows(a) + kTile - 1) / kTile;
   const int item = live_item(b, a.VT * TTn);
   if (item < 0) return;
   int vt, tau;
   grouped(item, a.VT, TTn, vt, tau);
+  if (kPass == 1 && !a.redo_t[tau]) return;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int ldb = a.H * E::kBytes;
@@ -1081,20 +1130,31 @@ __device__ __forceinline__ void z_tile(const ChunkArgs& a, int b, lds_t* smem) {
   B.bytes = (int64_t)(a.C - tau * kTile) * ldb;
   B.ldb = ldb;
   B.kbytes = ldb;
+  // thread t fetches token t's reference now and stages it after the K loop:
+  // the target logit (pass 0) or the row's max (pass 1), log2 units
+  const int nc = chunk_rows(a);
+  const int tk = tau * kTile + (int)threadIdx.x;
+  const float zr = tk >= nc ? 0.f : (kPass ? a.mrow[a.row0 + tk] : a.zt[a.row0 + tk] * kLog2e);
+  const int zf = kPass && tk < nc ? a.redo[a.row0 + tk] : 0;
   f32x16 acc[4][4];
   zero_acc(acc);
   gemm_tile<E, LoadDirect, LoadDirect>(A, B, steps, smem, wm, wn, acc);
+  ((__attribute__((address_space(3))) float*)(smem + kLdsBytes))[threadIdx.x] = zr;
+  if (kPass) ((__attribute__((address_space(3))) int*)(smem + kLdsBytes + kTile * 4))[threadIdx.x] = zf;
+  __syncthreads();
 
   const int vlim = a.V - vt * kTile;
-  if (vlim >= kTile) z_store<E, false>(a, acc, vt, tau, wm, wn, lane, 0, smem);
-  else z_store<E, true>(a, acc, vt, tau, wm, wn, lane, vlim - wm * 128 - 4 * (lane >> 5), smem);
+  if (vlim >= kTile) z_store<E, kPass, false>(a, acc, vt, tau, wm, wn, lane, 0, smem);
+  else
+    z_store<E, kPass, true>(a, acc, vt, tau, wm, wn, lane, vlim - wm * 128 - 4 * (lane >> 5),
+                            smem);
 }
 
-template <class E>
+template <class E, int kPass>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_chunk_z(ChunkArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem_[];
-  z_tile<E>(a, blockIdx.x, (lds_t*)smem_);
+  z_tile<E, kPass>(a, blockIdx.x, (lds_t*)smem_);
 }
 
 // One wave per row of the chunk: lse from the row's 2 VT partials (each lane
@@ -1107,6 +1167,7 @@ __device__ __forceinline__ void lse_pair_merge(float& M, float& S, float m2, flo
   M = Mn;
 }
 
+template <class E>
 __global__ __launch_bounds__(256) void k_chunk_lse(ChunkArgs a) {
   const int lane = threadIdx.x & 63;
   const int kl = blockIdx.x * 4 + (threadIdx.x >> 6), k = a.row0 + kl;
@@ -1117,7 +1178,15 @@ __global__ __launch_bounds__(256) void k_chunk_lse(ChunkArgs a) {
     c.fwd_p = 0;
     *a.cctr = c;
   }
-  if (kl >= nc) return;
+  if (kl >= a.C) return;
+  const int pieces = a.H * E::kBytes / 16;
+  i32x4* xs = (i32x4*)(a.Xs + (int64_t)kl * a.H * E::kBytes);
+  if (kl >= nc) {
+    // the dW tiles' K steps read up to the last token tile's end: zeros there
+    if (kl < (nc + kTile - 1) / kTile * kTile)
+      for (int c = lane; c < pieces; c += 64) xs[c] = i32x4{0, 0, 0, 0};
+    return;
+  }
   const float2* pr = a.part + (int64_t)kl * (2 * a.VT);
   float M = -INFINITY, S = 0.f;
   for (int h = lane; h < 2 * a.VT; h += 64) {
@@ -1129,11 +1198,37 @@ __global__ __launch_bounds__(256) void k_chunk_lse(ChunkArgs a) {
     const float m2 = __shfl_xor(M, d), s2 = __shfl_xor(S, d);
     lse_pair_merge(M, S, m2, s2);
   }
+  // the reference of the stored e: the target logit, or the row's max when
+  // that lies more than kRefSpan above it (the row goes to the second pass)
+  const float l2 = M + log2f(S);
+  const float zt2 = a.zt[k] * kLog2e;
+  const bool far = !(M - zt2 <= kRefSpan);
+  const float ck = a.rs ? a.ctr->c * a.rs[k] : a.ctr->c;
+  const float f = ck * exp2f((far ? M : zt2) - l2);
   if (lane == 0) {
-    const float l2 = M + log2f(S);
     a.lse2[k] = l2;
     a.lse_c[k] = l2 * kLn2;
     a.rloss[k] = l2 * kLn2 - a.zt[k];
+    a.fk[k] = f;
+    a.mrow[k] = M;
+    a.redo[k] = far ? 1 : 0;
+    if (far) a.redo_t[kl / kTile] = 1;
+  }
+  // the row scaled by f for the dW tiles (one rounding to the input dtype)
+  const i32x4* xc = (const i32x4*)(a.Xc + (int64_t)kl * a.H * E::kBytes);
+  for (int c = lane; c < pieces; c += 64) {
+    i32x4 u = xc[c];
+    if constexpr (E::kBytes == 2) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        u[q] = pack_bf16(bf2f((uint32_t)u[q] & 0xFFFFu) * f, bf2f((uint32_t)u[q] >> 16) * f);
+    } else {
+      f32x4 g = __builtin_bit_cast(f32x4, u);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) g[q] *= f;
+      u = __builtin_bit_cast(i32x4, g);
+    }
+    xs[c] = u;
   }
 }
 
@@ -1150,56 +1245,6 @@ __global__ __launch_bounds__(256) void k_block_sums(const float* __restrict__ rl
     __syncthreads();
   }
   if (threadIdx.x == 0) bsum[blockIdx.x] = red[0];
-}
-
-// G = c e 2^(M - lse2) (the softmax part; the one-hot part is added in FP32
-// to the gradient sums) for one 16-byte piece u of the slab (row
-// kl of the chunk, columns v .. v + 16 / es - 1); rows from the chunk's row
-// count up to the next multiple of 64 (the last K step of the dW tiles) become
-// zero.
-template <class E>
-__device__ __forceinline__ i32x4 scale_piece(const ChunkArgs& a, int kl, int v, int nc,
-                                             i32x4 u) {
-  if (kl >= nc) return i32x4{0, 0, 0, 0};
-  const int k = a.row0 + kl;
-  const float c = a.rs ? a.ctr->c * a.rs[k] : a.ctr->c;
-  const float f = c * exp2f(a.part[(int64_t)kl * (2 * a.VT) + (v >> 7)].x - a.lse2[k]);
-  if constexpr (E::kBytes == 2) {
-    float g[8];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      g[2 * q] = bf2f((uint32_t)u[q] & 0xFFFFu) * f;
-      g[2 * q + 1] = bf2f((uint32_t)u[q] >> 16) * f;
-    }
-    return i32x4{pack_bf16(g[0], g[1]), pack_bf16(g[2], g[3]), pack_bf16(g[4], g[5]),
-                 pack_bf16(g[6], g[7])};
-  } else {
-    f32x4 g = __builtin_bit_cast(f32x4, u);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) g[q] *= f;
-    return __builtin_bit_cast(i32x4, g);
-  }
-}
-
-__device__ __forceinline__ i32x4* slab_piece(const ChunkArgs& a, int kl, int v, int es) {
-  return (i32x4*)(a.E + ((int64_t)kl * a.Vp + v) * es);
-}
-
-// Slab columns [v_begin, v_end) (multiples of 256) in place, rows below the
-// chunk's row count rounded up to 64; 16 bytes per thread, grid
-// ((v_end - v_begin) / (256 * per), any row count), rows strided by gridDim.y
-// (so a chunk past the valid rows costs one early exit per workgroup).
-template <class E>
-__global__ __launch_bounds__(256) void k_chunk_scale(ChunkArgs a, int v_begin, int v_end) {
-  constexpr int per = 16 / E::kBytes;
-  const int nc = chunk_rows(a);
-  const int rows = (nc + 63) & ~63;
-  const int v = v_begin + (blockIdx.x * 256 + threadIdx.x) * per;
-  if (v >= v_end) return;
-  for (int kl = blockIdx.y; kl < rows; kl += gridDim.y) {
-    i32x4* p = slab_piece(a, kl, v, E::kBytes);
-    *p = scale_piece<E>(a, kl, v, nc, *p);
-  }
 }
 
 // lse of every original row (0 for ignored rows) after the chunks.
@@ -1309,17 +1354,19 @@ __global__ __launch_bounds__(256) void k_shard_merge(
   if (threadIdx.x == 0) blocksum[blockIdx.x] = red[0];
 }
 
-// dX = round(dX32 - c_k W[y_k]) scattered to the original rows (0 for
+// dX = round(f_k dX32 - c_k W[y_k]) scattered to the original rows (0 for
 // ignored rows): the softmax part summed in FP32 over the vocabulary (and
-// over its vocabulary parts, in part order) and the one-hot part, added in
-// FP32 before the one rounding.  Targets outside [0, V_local) (another
-// vocabulary shard's) have no one-hot term here.  One wave per row.
+// over its vocabulary parts, in part order), times the row's factor f_k of
+// the chunked mode (1 when fk is NULL), and the one-hot part, added in FP32
+// before the one rounding.  Targets outside [0, V_local) (another vocabulary
+// shard's) have no one-hot term here.  One wave per row.
 template <class E>
 __global__ __launch_bounds__(256) void k_dx_final(
     const float* __restrict__ dx32, int dx_split, int64_t dx_stride,
     const int* __restrict__ rowpos, int N, int H, char* __restrict__ dX, int out_f32,
     const char* __restrict__ W, const int* __restrict__ tgt, int V_local,
-    const Counters* __restrict__ ctr, const float* __restrict__ rs) {
+    const Counters* __restrict__ ctr, const float* __restrict__ rs,
+    const float* __restrict__ fk) {
   const int i = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (i >= N) return;
@@ -1335,6 +1382,10 @@ __global__ __launch_bounds__(256) void k_dx_final(
       for (int sp = 1; sp < dx_split; ++sp) {
         const f32x4 u = *(const f32x4*)(dx32 + sp * dx_stride + (int64_t)k * H + 4 * g);
         v = f32x4{v[0] + u[0], v[1] + u[1], v[2] + u[2], v[3] + u[3]};
+      }
+      if (fk) {
+        const float f = fk[k];
+        v = f32x4{v[0] * f, v[1] * f, v[2] * f, v[3] * f};
       }
       if (hot) {
         f32x4 wv;

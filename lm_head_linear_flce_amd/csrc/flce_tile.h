@@ -525,14 +525,26 @@ __device__ __forceinline__ int acc_col(int wn, int j, int lane) {
 //   emit(o, x0, v)          store chunk v (8 bf16, inner x0 .. x0 + 7) of row o
 // The region must be free (after the K loop's last barrier) and only this
 // wave touches it, so no barrier is needed between the two phases.
-template <class Val, class Emit>
+// begin(j), when given, runs before block j's values are taken (a value that
+// depends on the whole block, such as its max); the blocks are then kept
+// apart in the schedule, so one block's registers are live at a time.
+struct NoBegin {
+  __device__ __forceinline__ void operator()(int) const {}
+};
+
+template <class Val, class Emit, class Begin = NoBegin>
 __device__ __forceinline__ void store_quarter_bf16(lds_t* region, int lane, Val&& val,
-                                                   Emit&& emit) {
+                                                   Emit&& emit, Begin&& begin = NoBegin{}) {
   typedef __attribute__((address_space(3))) i32x2 lds_i32x2;
   typedef __attribute__((address_space(3))) i32x4 lds_i32x4;
+  constexpr bool kBegin = !__is_same(__remove_cvref(Begin), NoBegin);
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int o = 32 * j + (lane & 31);
+    if constexpr (kBegin) {
+      __builtin_amdgcn_sched_barrier(0);
+      begin(j);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll

@@ -145,6 +145,29 @@ def make_workload(name, *, B, T, H, V, dtype, seed, x_rms=False, w_std=0.02,
                     ignore_index=ignore_index)
 
 
+def far_logit_workload(*, B, T, H, V, dtype, seed, offset=120.0, w_std=0.05):
+    """Logits far from zero: every W row carries a shared unit direction u, and
+    row k of X carries t_k u with t_k uniform in [-offset, offset], so row k's
+    logits sit around t_k (a spread of about w_std * sqrt(H) around it).  For
+    schedules that keep exp(z) against a fixed reference: rows well above,
+    well below and near zero in one problem."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    N = B * T
+    u = _normal(rng, (H,), 1.0)
+    u /= np.float32(np.linalg.norm(u.astype(np.float64)))
+    W = _normal(rng, (V, H), w_std) + u[None, :]
+    t = rng.uniform(-offset, offset, size=N).astype(np.float32)
+    X = _normal(rng, (N, H), 1.0) + t[:, None] * u[None, :]
+    lab = rng.integers(0, V, size=(B, T), dtype=np.int64)
+    if dtype == "bf16":
+        X = round_to_bf16(X)
+        W = round_to_bf16(W)
+    elif dtype != "f32":
+        raise ValueError(dtype)
+    return Workload(name="far_logits", X=X, W=W, labels=lab, B=B, T=T, H=H, V=V,
+                    dtype=dtype, shift=False, reduction="mean", ignore_index=IGNORE_INDEX)
+
+
 # The five workloads.  Sizes follow the LM heads the pages talk about: a ~152K
 # token vocabulary (Qwen2/Qwen3 tokenizers), 8K-32K token sequences, hidden
 # widths 1024-4096, and one prime-sized vocabulary to exercise ragged tiles.

@@ -55,16 +55,20 @@ def run_chunked(w, grad_dtype=None, grad_scale=None, chunk_rows=0):
                 dW=dW.double().cpu().numpy())
 
 
-def check(w, got, ref, dx_rows=None, dw_rows=None, what=""):
-    """Contract tolerances plus the per-row lse diagnostic."""
+def check(w, got, ref, dx_rows=None, dw_rows=None, what="", lse_rel=0.0):
+    """Contract tolerances plus the per-row lse diagnostic.  lse_rel widens the
+    per-row lse bound by lse_rel * |lse| (for logits far from zero, where the
+    FP32 sum over H alone carries errors of that size)."""
     tol = TOL[w.dtype]
     assert got["status"] == 0 and got["bstatus"] == 0, what
     assert got["n_valid"] == ref["n_valid"], what
     rl = abs(got["loss"] - ref["loss"]) / max(abs(ref["loss"]), 1e-30)
     assert rl <= tol["loss_rel"], f"{what} loss {got['loss']} vs {ref['loss']} rel {rl}"
     _, valid = oracle.targets(w.labels, w.shift, w.ignore_index)
-    lerr = np.abs(got["lse"][valid] - ref["lse"][valid]).max() if valid.any() else 0.0
-    assert lerr <= LSE_ABS, f"{what} lse max abs err {lerr}"
+    if valid.any():
+        err = np.abs(got["lse"][valid] - ref["lse"][valid])
+        bound = LSE_ABS + lse_rel * np.abs(ref["lse"][valid])
+        assert np.all(err <= bound), f"{what} lse max abs err {err.max()}"
     assert np.all(got["lse"][~valid] == 0.0), what
     gx = got["dX"] if dx_rows is None else got["dX"][dx_rows]
     gw = got["dW"] if dw_rows is None else got["dW"][dw_rows]

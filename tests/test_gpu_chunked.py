@@ -95,6 +95,27 @@ def test_chunked_matches_recompute_path(case):
         assert oracle.cosine(a[k], b[k]) > 0.9999
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_chunked_logits_far_from_zero(dtype):
+    """Rows whose logits sit near +-120 (beyond the +-44 the slab's fixed
+    reference covers, so they are stored again against their own max) next to
+    rows near zero, over several chunks: loss, lse and both gradients against
+    the oracle, and the same results as the recompute path."""
+    w = synth.far_logit_workload(B=1, T=1100, H=256, V=3001, dtype=dtype, seed=881)
+    print(f"[chunked far logits] {dtype} N={w.N} H={w.H} V={w.V}", flush=True)
+    ref = oracle.flce(w.X, w.W, w.labels, ignore_index=w.ignore_index,
+                      reduction=w.reduction, shift=w.shift, mode="rows", chunk=1024)
+    assert np.abs(ref["lse"]).max() > 80.0 and np.abs(ref["lse"]).min() < 20.0
+    got = run_chunked(w, chunk_rows=256)
+    # |lse| up to ~140: the FP32 logits' own rounding over H = 256 terms is
+    # ~sqrt(H) ulp(140) ~ 1e-4, so the lse bound grows with |lse| (4e-6 |lse|)
+    check(w, got, ref, what="chunked far logits " + dtype, lse_rel=4e-6)
+    a = run(w)
+    assert abs(a["loss"] - got["loss"]) <= 1e-5 * abs(a["loss"])
+    for k in ("dX", "dW"):
+        assert oracle.cosine(a[k], got[k]) > 0.9999
+
+
 def test_chunked_autograd_and_grad_scale():
     w = synth.workload("qwen2_7b_head", T=300, H=128, V=700, seed=71)
     X, W, lab = to_device(w)

@@ -314,19 +314,6 @@ int flce_scale_grads(const void* dX_in, void* dX, int64_t nx, const void* dW_in,
 int flce_convert_grads(const float* src, void* dst, int64_t n, int dst_dtype,
                        const float* scale, int accumulate, void* stream);
 
-/*
- * flce_set_timing -- measurement hook for benchmarks and profilers.  While set,
- * every launch of the kernel named `kernel` ("k_fwd_lse", the forward GEMM;
- * "k_bwd", the backward GEMM launches; "k_chunk_z" and "k_chunk_dxdw", the
- * chunked mode's logits and gradient launches) made by the library records
- * events[2*i] on its stream right before the launch and events[2*i+1] right
- * after it, where i = *count, and then increments *count (a host int), until
- * *count reaches `capacity`.  `events` holds 2*capacity hipEvent_t handles
- * created by the caller.  kernel == NULL (or events / count NULL) switches the
- * hook off.  Process-wide and not thread-safe; the computation is unchanged.
- */
-int flce_set_timing(const char* kernel, void* const* events, int capacity, int* count);
-
 /* flce_status_string -- static, NUL-terminated description of a status code. */
 const char* flce_status_string(int code);
 

@@ -30,7 +30,7 @@ __all__ = [
     "flce_convert_grads",
     "flce_shard_forward", "flce_shard_merge_workspace_size", "flce_shard_merge",
     "flce_shard_backward",
-    "flce_set_timing", "flce_status_string", "linear_cross_entropy", "library_path",
+    "flce_status_string", "linear_cross_entropy", "library_path",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libflce.so")
@@ -57,7 +57,7 @@ FLCE_REDUCTION_NONE = 2
 EXPORTS = ("flce_workspace_size", "flce_forward", "flce_forward_noalloc", "flce_backward",
            "flce_shard_forward", "flce_shard_merge_workspace_size", "flce_shard_merge",
            "flce_shard_backward", "flce_chunked_workspace_size", "flce_chunked",
-           "flce_scale_grads", "flce_convert_grads", "flce_set_timing", "flce_status_string")
+           "flce_scale_grads", "flce_convert_grads", "flce_status_string")
 
 
 class FlceError(RuntimeError):
@@ -111,8 +111,6 @@ def _load() -> ctypes.CDLL:
     lib.flce_scale_grads.restype = i32
     lib.flce_convert_grads.argtypes = [vp, vp, i64, i32, vp, i32, vp]
     lib.flce_convert_grads.restype = i32
-    lib.flce_set_timing.argtypes = [ctypes.c_char_p, vp, i32, ctypes.POINTER(i32)]
-    lib.flce_set_timing.restype = i32
     lib.flce_status_string.argtypes = [i32]
     lib.flce_status_string.restype = ctypes.c_char_p
     return lib
@@ -242,18 +240,6 @@ def flce_convert_grads(src, dst, n, dst_dtype, scale, accumulate, stream) -> int
     return _LIB.flce_convert_grads(src or None, dst or None, n, dst_dtype, scale or None,
                                    int(bool(accumulate)), stream or None)
 
-
-def flce_set_timing(kernel, events, capacity, count) -> int:
-    """kernel: str or None; events: address of 2*capacity hipEvent_t handles;
-    count: a ctypes.c_int the library increments (keep it alive while set)."""
-    return _LIB.flce_set_timing(kernel.encode() if kernel else None, events or None,
-                                capacity, ctypes.byref(count) if count is not None
-                                else None)
-
-
-# ---------------------------------------------------------------------------
-# Tensor level
-# ---------------------------------------------------------------------------
 
 def _torch():
     import torch

@@ -184,31 +184,6 @@ int cu_count() {
   return n;
 }
 
-// Measurement hook (flce_set_timing): events recorded around the launches of
-// one named kernel.
-struct TimingHook {
-  char name[64] = {0};
-  hipEvent_t* events = nullptr;
-  int capacity = 0;
-  int* count = nullptr;
-};
-TimingHook g_timing;
-
-struct Timed {
-  bool on;
-  hipStream_t s;
-  Timed(const char* kernel, hipStream_t stream) : s(stream) {
-    on = g_timing.events != nullptr && g_timing.count != nullptr &&
-         *g_timing.count < g_timing.capacity && strcmp(kernel, g_timing.name) == 0;
-    // a launch whose events cannot be recorded is left out of the count
-    if (on) on = hipEventRecord(g_timing.events[2 * *g_timing.count], s) == hipSuccess;
-  }
-  ~Timed() {
-    if (on && hipEventRecord(g_timing.events[2 * *g_timing.count + 1], s) == hipSuccess)
-      ++*g_timing.count;
-  }
-};
-
 // The calls' W may be a vocabulary shard: rows [v_begin, v_begin + V) of a
 // vocabulary of V_total entries (labels index the whole vocabulary).
 struct Shard {
@@ -275,14 +250,11 @@ int forward_impl(const Plan& pl, const Shard& sh, const void* X, const void* W,
   fa.ctr = ctr;
   fa.part = part;
   if (L.err == hipSuccess) L.err = allow_big_lds<k_fwd_lse<E>>();
-  {
-    Timed t("k_fwd_lse", stream);
-    // k_fwd_lse hands its items out XCD by XCD over the first pad8(P * TTn)
-    // workgroups (P * TTn <= fwd_items), so the grid covers pad8(fwd_items)
-    hipLaunchKernelGGL(k_fwd_lse<E>, dim3((unsigned)pad8(pl.fwd_items)), dim3(kThreads),
-                       kLdsBytes, stream, fa);
-    L.check();
-  }
+  // k_fwd_lse hands its items out XCD by XCD over the first pad8(P * TTn)
+  // workgroups (P * TTn <= fwd_items), so the grid covers pad8(fwd_items)
+  hipLaunchKernelGGL(k_fwd_lse<E>, dim3((unsigned)pad8(pl.fwd_items)), dim3(kThreads),
+                     kLdsBytes, stream, fa);
+  L.check();
   const int nb = (int)cdiv(pl.N, 256);
   hipLaunchKernelGGL(k_merge, dim3(nb), dim3(256), 0, stream, (const float2*)part,
                      (const Counters*)ctr, (const int*)rowpos, (const float*)zt,
@@ -417,12 +389,9 @@ int backward_impl(const Plan& pl, const Shard& sh, const void* X, const void* W,
     const int nb_dx = b >= 0 ? (int)pad8((int64_t)a.dx_split * a.HT * a.TT) : 0;
     const int nb_dw = b >= 0 ? (int)pad8((int64_t)a.HT * cur.VTb) : 0;
     const int nb_g = b + 1 < nblk ? (int)pad8((int64_t)nxt.VTb * a.TT) : 0;
-    {
-      Timed t("k_bwd", stream);
-      hipLaunchKernelGGL(k_bwd<E>, dim3((unsigned)(nb_dx + nb_dw + nb_g)), dim3(kThreads),
-                         kBwdLdsBytes, stream, cur, nxt, nb_dx, nb_dw, nb_g, dw_first);
-      L.check();
-    }
+    hipLaunchKernelGGL(k_bwd<E>, dim3((unsigned)(nb_dx + nb_dw + nb_g)), dim3(kThreads),
+                       kBwdLdsBytes, stream, cur, nxt, nb_dx, nb_dw, nb_g, dw_first);
+    L.check();
   }
   hipLaunchKernelGGL(k_dx_final<E>, dim3((unsigned)cdiv(pl.N, 4)), dim3(256), 0, stream,
                      (const float*)dx32, (int)pl.dx_split, (int64_t)pl.rows_pad * pl.H,
@@ -618,13 +587,10 @@ int chunked_impl(const ChunkPlan& pl, const void* X, const void* W, const int64_
     ca.redo_t = redo_t;
     ca.Xs = xs;
     const int nbz = (int)pad8(pl.VT * TTc);
-    {
-      Timed t("k_chunk_z", stream);
-      hipLaunchKernelGGL((k_chunk_z<E, 0>), dim3((unsigned)nbz), dim3(kThreads), kChunkZLdsBytes,
-                         stream,
-                         ca);
-      L.check();
-    }
+    hipLaunchKernelGGL((k_chunk_z<E, 0>), dim3((unsigned)nbz), dim3(kThreads), kChunkZLdsBytes,
+                       stream,
+                       ca);
+    L.check();
     hipLaunchKernelGGL(k_chunk_lse<E>, dim3((unsigned)(C / 4)), dim3(256), 0, stream, ca);
     L.check();
     // the rows whose largest logit lies far above the target logit, against
@@ -666,7 +632,6 @@ int chunked_impl(const ChunkPlan& pl, const void* X, const void* W, const int64_
       b.G = slab + v0 * E::kBytes;
       const int nb_dx = (int)pad8((int64_t)pl.dx_split * HT * TTc);
       const int nb_dw = (int)pad8((int64_t)HT * b.VTb);
-      Timed t("k_chunk_dxdw", stream);
       hipLaunchKernelGGL(k_bwd<E>, dim3((unsigned)(nb_dx + nb_dw)), dim3(kThreads), kBwdLdsBytes,
                          stream, b, b, nb_dx, nb_dw, 0, C > cdiv(b.vb, pl.dx_split) ? 1 : 0);
       L.check();
@@ -1108,20 +1073,6 @@ int flce_convert_grads(const float* src, void* dst, int64_t n, int dst_dtype,
                      src, (char*)dst, chunks, dst_dtype == FLCE_DTYPE_F32 ? 1 : 0, scale,
                      accumulate ? 1 : 0);
   return hipGetLastError() == hipSuccess ? FLCE_OK : FLCE_ERR_HIP;
-}
-
-int flce_set_timing(const char* kernel, void* const* events, int capacity, int* count) {
-  if (kernel == nullptr || events == nullptr || count == nullptr || capacity <= 0) {
-    g_timing = TimingHook();
-    return FLCE_OK;
-  }
-  if (strlen(kernel) >= sizeof(g_timing.name)) return FLCE_ERR_SHAPE;
-  g_timing = TimingHook();
-  strcpy(g_timing.name, kernel);
-  g_timing.events = (hipEvent_t*)events;
-  g_timing.capacity = capacity;
-  g_timing.count = count;
-  return FLCE_OK;
 }
 
 const char* flce_status_string(int code) {

@@ -79,7 +79,7 @@ MFMA_PROFILE_COMMANDS = (
     "python $R/bench.py --summarize-mfma $R/gpurun_out",
 )
 # every bf16 workload through the bench (profiles/flce_workloads_bench.md)
-BENCH_WORKLOADS = ("qwen2_7b_head", "qwen3_sft_batch", "long_context", "ragged_vocab")
+BENCH_WORKLOADS = ("tiny_f32", "qwen2_7b_head", "qwen3_sft_batch", "long_context", "ragged_vocab")
 WORKLOAD_BENCH_COMMANDS = tuple(
     f"python $R/bench.py --workload {name} --steps 5 --warmup 2 > $R/gpurun_out/bench_{name}.json"
     for name in BENCH_WORKLOADS) + ("python $R/bench.py --summarize-workloads $R/gpurun_out",)
@@ -389,23 +389,26 @@ def summarize_workloads(prof_dir):
             continue
         rows.append((name, json.loads(lines[-1])))
     gb = 1e9
-    out = ["# Every bf16 workload through bench.py (MI355X, one GPU)", "",
+    out = ["# Every workload through bench.py (MI355X, one GPU)", "",
            "Commands ($R = repository root):", "", "```", *WORKLOAD_BENCH_COMMANDS, "```", "",
            "Model basis: 6 N H V flop over all N rows; the recompute path executes 8 n H V "
-           "(n valid rows), the chunked mode 6 n H V. PyTorch eager and hipBLASLt are "
-           "context, not part of the path.", "",
-           "| workload | recompute ms | tokens/s | % bf16 peak (model) | peak extra GB | "
-           "chunked ms | chunked % | PyTorch eager ms | eager peak extra GB | hipBLASLt logits "
-           "GEMM ms | oracle tokens/s (host) |",
-           "|---|---|---|---|---|---|---|---|---|---|---|"]
+           "(n valid rows), the chunked mode 6 n H V. Each workload against the dense MFMA "
+           "peak of its own dtype: bf16 2500 TFLOP/s, fp32 157.3 TFLOP/s (the fp32 workload "
+           "runs v_mfma_f32_32x32x2f32). PyTorch eager and hipBLASLt (bf16 only) are context, "
+           "not part of the path.", "",
+           "| workload | recompute ms | tokens/s | peak TFLOP/s | % peak (model) | "
+           "peak extra GB | chunked ms | chunked % | PyTorch eager ms | eager peak extra GB | "
+           "hipBLASLt logits GEMM ms | oracle tokens/s (host) |",
+           "|---|---|---|---|---|---|---|---|---|---|---|---|"]
     for name, d in rows:
         ch = d.get("chunked_mode") or {}
         te = d.get("torch_eager") or {}
         vg = d.get("vendor_gemm") or {}
         cb = d.get("cpu_baseline") or {}
+        pk = (BF16_PEAK if d.get("dtype") == "bf16" else F32_PEAK) / 1e12
         out.append(
             f"| {d['config']['workload']} | {d['ms_per_step']:.2f} | {d['value']:.3g} | "
-            f"{100 * d['mfma_frac_model']:.1f} | {d['peak_extra_bytes'] / gb:.2f} | "
+            f"{pk:g} | {100 * d['mfma_frac_model']:.1f} | {d['peak_extra_bytes'] / gb:.2f} | "
             f"{ch.get('ms_per_step', float('nan')):.2f} | "
             f"{100 * ch.get('mfma_frac_model', float('nan')):.1f} | "
             f"{te.get('ms_per_step', float('nan')):.2f} | "

@@ -83,13 +83,24 @@ def test_workload_table_has_one_row_per_bench_line(out):
     run.mkdir()
     line = {"config": {"workload": "qwen2_7b_head: N=8192"}, "ms_per_step": 22.5,
             "value": 364088.9, "mfma_frac_model": 0.4761, "peak_extra_bytes": 1.86e9,
+            "dtype": "bf16",
             "chunked_mode": {"ms_per_step": 18.0, "mfma_frac_model": 0.595},
             "torch_eager": {"ms_per_step": 34.0, "peak_extra_bytes": 1.49e10},
             "vendor_gemm": {"ms": 5.05}, "cpu_baseline": {"value": 390.2}}
+    tiny = {"config": {"workload": "tiny_f32: N=128"}, "ms_per_step": 0.05, "value": 2.56e6,
+            "mfma_frac_model": 0.0161, "peak_extra_bytes": 3.0e6, "dtype": "f32",
+            "chunked_mode": {"ms_per_step": 0.04, "mfma_frac_model": 0.0201},
+            "cpu_baseline": {"value": 5000.0}}
     with open(run / "bench_qwen2_7b_head.json", "w") as f:
         f.write("[bench] progress line\n" + json.dumps(line) + "\n")
+    with open(run / "bench_tiny_f32.json", "w") as f:
+        f.write(json.dumps(tiny) + "\n")
     bench.summarize_workloads(str(run))
     md = open(out / "profiles" / "flce_workloads_bench.md").read()
-    rows = [l for l in md.splitlines() if l.startswith("| qwen2_7b_head")]
-    assert rows == ["| qwen2_7b_head: N=8192 | 22.50 | 3.64e+05 | 47.6 | 1.86 | 18.00 | 59.5 | "
-                    "34.00 | 14.9 | 5.05 | 390 |"]
+    rows = [l for l in md.splitlines() if l.startswith("| qwen2_7b_head") or
+            l.startswith("| tiny_f32")]
+    # one row per bench line, each against its own dtype's dense peak
+    assert rows == ["| tiny_f32: N=128 | 0.05 | 2.56e+06 | 157.3 | 1.6 | 0.00 | 0.04 | 2.0 | "
+                    "nan | nan | nan | 5000 |",
+                    "| qwen2_7b_head: N=8192 | 22.50 | 3.64e+05 | 2500 | 47.6 | 1.86 | 18.00 | "
+                    "59.5 | 34.00 | 14.9 | 5.05 | 390 |"]

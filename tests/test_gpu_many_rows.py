@@ -48,13 +48,10 @@ def test_more_than_2048_token_tiles():
     assert np.abs(gdw - rdw).max() <= TOL["bf16"]["maxabs"] * np.abs(rdw).max()
 
 
-def test_rows_times_hidden_past_2_29():
-    """N * H = 2^29 (262144 rows of H = 2048, 1 GiB of bf16 hidden states): the
-    FP32 dX sums (2 GiB) and the one-hot row sums pass 2^31 bytes and the dW
-    contraction runs over 0.5 Gi elements of X.  Sampled lse and dX rows (every
-    64th token tile's edges) and all of dW (V = 333) against the oracle."""
-    T, H, V = 262144, 2048, 333
-    w = synth.make_workload("long_rows", B=1, T=T, H=H, V=V, dtype="bf16", seed=7721,
+def _long_rows_case(T, H, V, seed):
+    """Sampled lse and dX rows (every 64th token tile's edges) and all of dW
+    (small V) against the oracle for one long sequence."""
+    w = synth.make_workload("long_rows", B=1, T=T, H=H, V=V, dtype="bf16", seed=seed,
                             x_rms=True, labels="zipf", mask="prefix", mask_arg=4096,
                             shift=True, reduction="mean")
     print(f"[long-rows] N={w.N} H={H} V={V} bf16", flush=True)
@@ -86,3 +83,18 @@ def test_rows_times_hidden_past_2_29():
     gdw = dW.double().cpu().numpy()
     assert oracle.cosine(gdw, rdw) >= TOL["bf16"]["cos"]
     assert np.abs(gdw - rdw).max() <= TOL["bf16"]["maxabs"] * np.abs(rdw).max()
+
+
+def test_rows_times_hidden_past_2_29():
+    """N * H = 2^29 (262144 rows of H = 2048, 1 GiB of bf16 hidden states): the
+    FP32 dX sums (2 GiB) and the one-hot row sums pass 2^31 bytes and the dW
+    contraction runs over 0.5 Gi elements of X."""
+    _long_rows_case(262144, 2048, 333, 7721)
+
+
+def test_rows_times_hidden_past_2_30():
+    """N * H just past 2^30 (532480 rows of H = 2048, 2.03 GiB of bf16 hidden
+    states; 528383 valid rows): the dW tiles' K loop over the rows reaches past
+    2^31 bytes of X, so their loaders rebase the buffer descriptor at every K
+    step."""
+    _long_rows_case(532480, 2048, 97, 7723)

@@ -64,7 +64,8 @@ extern "C" {
 #define FLCE_ERR_WORKSPACE 6   /* workspace NULL or smaller than required   */
 #define FLCE_ERR_HIP 7         /* a HIP launch or query failed              */
 #define FLCE_ERR_LABEL_RANGE 8 /* device: a valid label outside [0, V)      */
-#define FLCE_ERR_ALIAS 9       /* an output aliases an input                */
+#define FLCE_ERR_ALIAS 9       /* an output overlaps an input, another
+                                  output or the workspace                   */
 #define FLCE_ERR_TOO_LARGE 10  /* beyond the allocation-free scratch        */
 
 /* bytes of the device array flce_forward_noalloc uses as its scratch */
@@ -161,7 +162,9 @@ int flce_forward_noalloc(const void* X, const void* W, const int64_t* labels,
  *                   micro-batches, or the gradient buffer of a weight tied to
  *                   the input embedding), summed in FP32 and rounded once
  *   status, workspace, workspace_bytes, stream : as forward
- * dX must not alias X and dW must not alias W.  The FP32 accumulation and the
+ * dX must not overlap X, dW must not overlap W, and neither may overlap the
+ * other or the workspace's first flce_workspace_size bytes (else
+ * FLCE_ERR_ALIAS, before anything is launched).  The FP32 accumulation and the
  * single final rounding follow Megatron-LM PR "[Dev] Fix Linear-Cross-Entropy
  * Convergence Issue", item 2.
  */
@@ -228,6 +231,7 @@ int flce_shard_merge(const float* lse_shards, const float* zt_shards, int shards
  *                  shards, then round once
  *   dW [V, H]    : out, grad_dtype, this shard's rows (dW_accumulate as in
  *                  flce_backward)
+ * dX_partial and dW follow flce_backward's rules on overlapping buffers.
  */
 int flce_shard_backward(const void* X, const void* W, const int64_t* labels,
                         int64_t B, int64_t T, int64_t H, int64_t V, int64_t v_begin,
@@ -264,7 +268,8 @@ int flce_chunked_workspace_size(int64_t B, int64_t T, int64_t H, int64_t V, int 
  *   chunk_rows    : as flce_chunked_workspace_size
  *   grad_scale    : as flce_backward (scalar, or per row under NONE); NULL = 1
  *   loss, lse, n_valid : as flce_forward's outputs
- *   dX, dW, grad_dtype, dW_accumulate : as flce_backward's
+ *   dX, dW, grad_dtype, dW_accumulate : as flce_backward's (the same rules
+ *                   on overlapping buffers, with this call's workspace size)
  *   status        : as forward (a bad label also makes the gradients NaN)
  *   workspace, workspace_bytes : device scratch of flce_chunked_workspace_size
  *   stream        : hipStream_t

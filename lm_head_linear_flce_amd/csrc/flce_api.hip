@@ -143,6 +143,14 @@ bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
   return a0 < b0 + (uintptr_t)nb && b0 < a0 + (uintptr_t)na;
 }
 
+// The two gradient outputs lie apart from each other and from the bytes of
+// the workspace the call uses (dX of nx bytes may be absent: nx = 0).
+bool grads_overlap(const void* dX, int64_t nx, const void* dW, int64_t nw, const void* ws,
+                   int64_t nws) {
+  return (nx > 0 && (overlaps(dX, nx, dW, nw) || overlaps(dX, nx, ws, nws))) ||
+         overlaps(dW, nw, ws, nws);
+}
+
 // The GEMM kernels take 128 KiB of dynamic LDS.  The limit is raised once per
 // kernel, device and process (the attribute belongs to the kernel, not to a
 // call), so that calls made under stream capture issue no attribute changes.
@@ -813,6 +821,8 @@ int flce_backward(const void* X, const void* W, const int64_t* labels, int64_t B
   if (workspace == nullptr) return FLCE_ERR_WORKSPACE;
   if ((int64_t)workspace_bytes < p.total || !aligned16(workspace))
     return FLCE_ERR_WORKSPACE;
+  if (grads_overlap(dX, p.N * p.H * ges, dW, p.V * p.H * ges, workspace, p.total))
+    return FLCE_ERR_ALIAS;
   hipStream_t s = (hipStream_t)stream;
   const int gf32 = grad_dtype == FLCE_DTYPE_F32 ? 1 : 0;
   if (p.N == 0) {
@@ -956,6 +966,8 @@ int flce_shard_backward(const void* X, const void* W, const int64_t* labels, int
   if (p.N > 0 && overlaps(dX_partial, p.N * p.H * 4, X, p.N * p.H * p.es)) return FLCE_ERR_ALIAS;
   if (workspace == nullptr) return FLCE_ERR_WORKSPACE;
   if ((int64_t)workspace_bytes < p.total || !aligned16(workspace)) return FLCE_ERR_WORKSPACE;
+  if (grads_overlap(dX_partial, p.N * p.H * 4, dW, p.V * p.H * ges, workspace, p.total))
+    return FLCE_ERR_ALIAS;
   hipStream_t s = (hipStream_t)stream;
   const int gf32 = grad_dtype == FLCE_DTYPE_F32 ? 1 : 0;
   if (p.N == 0) {
@@ -1007,6 +1019,7 @@ int flce_chunked(const void* X, const void* W, const int64_t* labels, int64_t B,
     return FLCE_ERR_ALIGN;
   if (overlaps(dW, p.V * p.H * ges, W, p.V * p.H * p.es)) return FLCE_ERR_ALIAS;
   if (p.N > 0 && overlaps(dX, p.N * p.H * ges, X, p.N * p.H * p.es)) return FLCE_ERR_ALIAS;
+  if (grads_overlap(dX, p.N * p.H * ges, dW, p.V * p.H * ges, nullptr, 0)) return FLCE_ERR_ALIAS;
   hipStream_t s = (hipStream_t)stream;
   const int gf32 = grad_dtype == FLCE_DTYPE_F32 ? 1 : 0;
   if (p.N == 0) {
@@ -1019,6 +1032,8 @@ int flce_chunked(const void* X, const void* W, const int64_t* labels, int64_t B,
   if (workspace == nullptr) return FLCE_ERR_WORKSPACE;
   if ((int64_t)workspace_bytes < p.total || !aligned16(workspace))
     return FLCE_ERR_WORKSPACE;
+  if (grads_overlap(dX, p.N * p.H * ges, dW, p.V * p.H * ges, workspace, p.total))
+    return FLCE_ERR_ALIAS;
   if (dtype == FLCE_DTYPE_BF16)
     return chunked_impl<BF16>(p, X, W, labels, B, T, ignore_index, reduction, shift,
                               grad_scale, loss, lse, n_valid, dX, dW, gf32,
@@ -1086,7 +1101,8 @@ const char* flce_status_string(int code) {
     case FLCE_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
     case FLCE_ERR_HIP: return "a HIP launch failed";
     case FLCE_ERR_LABEL_RANGE: return "a label is neither ignore_index nor in [0, V)";
-    case FLCE_ERR_ALIAS: return "an output buffer overlaps an input buffer";
+    case FLCE_ERR_ALIAS:
+      return "an output buffer overlaps an input, the other output or the workspace";
     case FLCE_ERR_TOO_LARGE:
       return "the problem needs more scratch than the allocation-free entry point holds";
     default: return "unknown status code";

@@ -98,7 +98,7 @@ def bwd(**kw):
     a = dict(X=P, W=2 * P, labels=3 * P, B=1, T=16, H=128, V=50, dtype=F.FLCE_DTYPE_BF16,
              ignore_index=-100, reduction=F.FLCE_REDUCTION_MEAN, shift=0, lse=5 * P,
              grad_scale=0, dX=7 * P, dW=8 * P, grad_dtype=F.FLCE_DTYPE_BF16, dW_accumulate=0,
-             status=0, workspace=6 * P, workspace_bytes=1 << 30, stream=0)
+             status=0, workspace=16 * P, workspace_bytes=1 << 30, stream=0)
     a.update(kw)
     return F.flce_backward(*a.values())
 
@@ -120,6 +120,9 @@ def test_forward_host_checks(kw, code):
     (dict(lse=0), F.FLCE_ERR_NULL), (dict(grad_dtype=5), F.FLCE_ERR_DTYPE),
     (dict(dtype=F.FLCE_DTYPE_F32, grad_dtype=F.FLCE_DTYPE_BF16), F.FLCE_ERR_DTYPE),
     (dict(dX=P), F.FLCE_ERR_ALIAS), (dict(dW=2 * P + 64), F.FLCE_ERR_ALIAS),
+    # dX is 16 x 128 bf16 = 4 KiB at 7 P; the workspace starts at 16 P
+    (dict(dW=7 * P + 1024), F.FLCE_ERR_ALIAS), (dict(dX=16 * P + 4096), F.FLCE_ERR_ALIAS),
+    (dict(dW=16 * P), F.FLCE_ERR_ALIAS),
     (dict(workspace_bytes=10), F.FLCE_ERR_WORKSPACE), (dict(reduction=9), F.FLCE_ERR_REDUCTION),
     (dict(dW=8 * P + 4), F.FLCE_ERR_ALIGN),
 ])
@@ -131,7 +134,7 @@ def chk(**kw):
     a = dict(X=P, W=2 * P, labels=3 * P, B=1, T=16, H=128, V=50, dtype=F.FLCE_DTYPE_BF16,
              ignore_index=-100, reduction=F.FLCE_REDUCTION_MEAN, shift=0, chunk_rows=0,
              grad_scale=0, loss=4 * P, lse=5 * P, n_valid=0, dX=7 * P, dW=8 * P,
-             grad_dtype=F.FLCE_DTYPE_BF16, dW_accumulate=0, status=0, workspace=6 * P,
+             grad_dtype=F.FLCE_DTYPE_BF16, dW_accumulate=0, status=0, workspace=16 * P,
              workspace_bytes=1 << 30, stream=0)
     a.update(kw)
     return F.flce_chunked(*a.values())
@@ -145,6 +148,8 @@ def chk(**kw):
     (dict(X=P + 8), F.FLCE_ERR_ALIGN), (dict(dtype=3), F.FLCE_ERR_DTYPE),
     (dict(grad_dtype=5), F.FLCE_ERR_DTYPE), (dict(reduction=3), F.FLCE_ERR_REDUCTION),
     (dict(dX=P), F.FLCE_ERR_ALIAS), (dict(dW=2 * P + 64), F.FLCE_ERR_ALIAS),
+    (dict(dW=7 * P + 1024), F.FLCE_ERR_ALIAS), (dict(dX=16 * P + 4096), F.FLCE_ERR_ALIAS),
+    (dict(dW=16 * P), F.FLCE_ERR_ALIAS),
     (dict(workspace=0), F.FLCE_ERR_WORKSPACE), (dict(workspace_bytes=64), F.FLCE_ERR_WORKSPACE),
     (dict(V=-5), F.FLCE_ERR_SHAPE), (dict(chunk_rows=-1), F.FLCE_ERR_SHAPE),
 ])
@@ -208,7 +213,7 @@ def sbwd(**kw):
     a = dict(X=P, W=2 * P, labels=3 * P, B=1, T=16, H=128, V=50, v_begin=10, V_total=100,
              dtype=F.FLCE_DTYPE_BF16, ignore_index=-100, reduction=F.FLCE_REDUCTION_MEAN,
              shift=0, lse=5 * P, grad_scale=0, dX_partial=7 * P, dW=8 * P,
-             grad_dtype=F.FLCE_DTYPE_BF16, dW_accumulate=0, status=0, workspace=6 * P,
+             grad_dtype=F.FLCE_DTYPE_BF16, dW_accumulate=0, status=0, workspace=16 * P,
              workspace_bytes=1 << 30, stream=0)
     a.update(kw)
     return F.flce_shard_backward(*a.values())
@@ -228,6 +233,7 @@ def test_shard_forward_host_checks(kw, code):
     (dict(v_begin=51), F.FLCE_ERR_SHAPE), (dict(dX_partial=0), F.FLCE_ERR_NULL),
     (dict(dW=0), F.FLCE_ERR_NULL), (dict(reduction=3), F.FLCE_ERR_REDUCTION),
     (dict(dX_partial=P), F.FLCE_ERR_ALIAS), (dict(grad_dtype=5), F.FLCE_ERR_DTYPE),
+    (dict(dW=7 * P + 4096), F.FLCE_ERR_ALIAS), (dict(dX_partial=16 * P + 64), F.FLCE_ERR_ALIAS),
     (dict(workspace=0), F.FLCE_ERR_WORKSPACE),
 ])
 def test_shard_backward_host_checks(kw, code):

@@ -50,26 +50,19 @@ struct Plan {
   int64_t total;
 };
 
-// The dX tiles of a launch number (token tiles) x (hidden tiles), each with a
-// K loop over the whole vocabulary block.  Where that count is small (narrow
-// H, few rows) a launch would last as long as one dX tile while most compute
-// units idle, so the block's vocabulary range is cut into parts, each with its
-// own FP32 accumulator, until about `target` dX tiles are in flight (at most
-// kMaxDxSplit parts).  The recompute path's launches also carry the G tiles
-// (three tile kinds of equal total work, the chunked mode's two), and its
-// token-tile count is a bound that the valid rows may not reach, hence the
-// larger target.
+// dX tiles in flight per launch that the vocabulary parts aim at
+// (dx_parts_for).  The recompute path's launches also carry the G tiles (three
+// tile kinds of equal total work, the chunked mode's two), and its token-tile
+// count is a bound that the valid rows may not reach, hence the larger target.
+// The recompute path fixes the part count on the host from that bound; the
+// chunked mode sets it per chunk on the device from the chunk's rows, so the
+// short last chunk gets more parts than the full ones.
 #ifndef FLCE_DX_TILES
 #define FLCE_DX_TILES 256
 #endif
 #ifndef FLCE_DX_TILES_CHUNKED
 #define FLCE_DX_TILES_CHUNKED 176
 #endif
-constexpr int64_t kMaxDxSplit = 8;
-int64_t dx_split_for(int64_t hidden_tiles, int64_t token_tiles, int64_t target) {
-  return std::min<int64_t>(kMaxDxSplit,
-                           std::max<int64_t>(1, cdiv(target, hidden_tiles * token_tiles)));
-}
 
 int make_plan(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, Plan* p) {
   if (B < 0 || T < 0 || H <= 0 || V <= 0) return FLCE_ERR_SHAPE;
@@ -98,7 +91,7 @@ int make_plan(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, Plan* p) {
   vb = std::max<int64_t>(kTile, vb / kTile * kTile);
   vb = std::min<int64_t>(vb, round_up(V, kTile));
   q.Vb = vb;
-  q.dx_split = dx_split_for(cdiv(H, kTile), q.TT, FLCE_DX_TILES);
+  q.dx_split = dx_parts_for((int)cdiv(H, kTile), (int)q.TT, FLCE_DX_TILES, -1);
   // 32-bit offsets inside the kernels
   if (q.rows_pad * q.Vb * q.es > kMaxI32 || (int64_t)kTile * H * q.es * 2 > kMaxI32)
     return FLCE_ERR_SHAPE;
@@ -437,7 +430,9 @@ struct ChunkPlan {
   int64_t N, rows_pad, H, V, Vp, es, TT, VT;
   int64_t C, nchunks;       // chunk rows (multiple of 256), chunks covering rows_pad
   int64_t VB;               // vocabulary block of the dX / dW launches
-  int64_t dx_split;         // dX tiles per (token tile, hidden tile) and block
+  int64_t dx_split;         // dX parts of a full chunk
+  int64_t part_tiles;       // token tiles the extra dX parts' buffer holds
+  int64_t dx_blocks;        // workgroups of a launch's dX tiles, at most
   int64_t o_ctr, o_idx, o_tgt, o_rowpos, o_xc, o_zt, o_lse_c, o_lse2, o_rloss, o_bsum, o_cctr;
   int64_t o_blk;
   int64_t o_rs;
@@ -502,11 +497,21 @@ int make_chunk_plan(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, int64
   q.o_redo_t = take(4 * (q.C / kTile));
   q.o_xs = take(q.C * H * q.es);
   q.o_slab = take(q.C * q.Vp * q.es);
-  q.dx_split = dx_split_for(cdiv(H, kTile), q.C / kTile, FLCE_DX_TILES_CHUNKED);
+  // dX parts: a full chunk's as its token tiles ask; the buffer of the extra
+  // parts holds that many full chunks' rows, and at least half a chunk's, so
+  // a short last chunk (few token tiles) can take more parts.  The parts
+  // cover one chunk's rows and are folded into the main FP32 sum after it.
+  const int HT = (int)cdiv(H, kTile), TTc = (int)(q.C / kTile);
+  q.dx_split = dx_parts_for(HT, TTc, FLCE_DX_TILES_CHUNKED, -1);
+  q.part_tiles = std::max<int64_t>((q.dx_split - 1) * TTc, cdiv(TTc, 2));
+  q.dx_blocks = 0;
+  for (int tt = 1; tt <= TTc; ++tt)
+    q.dx_blocks = std::max<int64_t>(
+        q.dx_blocks,
+        (int64_t)dx_parts_for(HT, tt, FLCE_DX_TILES_CHUNKED, (int)q.part_tiles) * HT * tt);
+  q.dx_blocks = pad8(q.dx_blocks);
   q.o_dx32 = take(4 * q.rows_pad * H);
-  // the extra vocabulary parts of dX cover one chunk's rows; they are folded
-  // into the main FP32 sum after each chunk
-  q.o_dx32p = take(4 * (q.dx_split - 1) * q.C * H);
+  q.o_dx32p = take(4 * q.part_tiles * kTile * H);
   q.P = pow2_at_least(q.rows_pad);
   q.o_keys = take(16 * q.P);
   q.o_oh = take(4 * q.rows_pad * H);
@@ -594,6 +599,10 @@ int chunked_impl(const ChunkPlan& pl, const void* X, const void* W, const int64_
     ca.redo = redo;
     ca.redo_t = redo_t;
     ca.Xs = xs;
+    ca.dx32p = dx32p;
+    ca.HT = HT;
+    ca.dx_target = FLCE_DX_TILES_CHUNKED;
+    ca.part_tiles = (int)pl.part_tiles;
     const int nbz = (int)pad8(pl.VT * TTc);
     hipLaunchKernelGGL((k_chunk_z<E, 0>), dim3((unsigned)nbz), dim3(kThreads), kChunkZLdsBytes,
                        stream,
@@ -616,9 +625,8 @@ int chunked_impl(const ChunkPlan& pl, const void* X, const void* W, const int64_
     b.tgt = tgt;
     b.dx32 = dx32 + (int64_t)ca.row0 * pl.H;
     b.dx32p = dx32p;
-    b.dx_stride = (int64_t)C * pl.H;
-    b.dx_split = (int)pl.dx_split;
-    if (pl.dx_split > 1) zero_fill(dx32p, 4 * (pl.dx_split - 1) * C * pl.H, stream);
+    b.dx_stride = 0;
+    b.dx_split = 0;   // the chunk's part count, from its counters (k_chunk_lse)
     b.dW = (char*)dW;
     b.ctr = cctr + ch;
     b.H = (int)pl.H;
@@ -638,20 +646,19 @@ int chunked_impl(const ChunkPlan& pl, const void* X, const void* W, const int64_
       b.vb = (int)std::min<int64_t>(pl.VB, pl.V - v0);
       b.VTb = (int)cdiv(b.vb, kTile);
       b.G = slab + v0 * E::kBytes;
-      const int nb_dx = (int)pad8((int64_t)pl.dx_split * HT * TTc);
+      const int nb_dx = (int)pl.dx_blocks;
       const int nb_dw = (int)pad8((int64_t)HT * b.VTb);
       hipLaunchKernelGGL(k_bwd<E>, dim3((unsigned)(nb_dx + nb_dw)), dim3(kThreads), kBwdLdsBytes,
                          stream, b, b, nb_dx, nb_dw, 0, C > cdiv(b.vb, pl.dx_split) ? 1 : 0);
       L.check();
     }
-    if (pl.dx_split > 1 && L.err == hipSuccess) {
-      // the chunk's extra vocabulary parts into the main sum, in part order
-      // (the last chunk may reach past rows_pad: only its rows inside it)
-      const int64_t rows = std::min<int64_t>(C, pl.rows_pad - ca.row0);
-      const int64_t count4 = rows * pl.H / 4;
+    if (L.err == hipSuccess) {
+      // the chunk's extra vocabulary parts (if it has any) into the main sum,
+      // in part order, over the chunk's rows
+      const int64_t count4 = (int64_t)C * pl.H / 4;
       hipLaunchKernelGGL(k_dx_fold, dim3((unsigned)std::min<int64_t>(cdiv(count4, 256), 4096)),
                          dim3(256), 0, stream, b.dx32, (const float*)dx32p,
-                         (int)pl.dx_split - 1, (int64_t)C * pl.H, count4);
+                         (const Counters*)(cctr + ch), (int)pl.H);
       L.check();
     }
   }

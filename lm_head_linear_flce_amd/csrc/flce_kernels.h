@@ -36,7 +36,27 @@ struct Counters {
   int status;    // 0 or FLCE_ERR_LABEL_RANGE
   float c;       // gradient scale (backward)
   int fwd_p;     // forward: vocabulary ranges per token tile
+  int dx_parts;  // chunked mode, per chunk: vocabulary parts of the dX tiles
 };
+
+// The dX tiles of a backward launch number (vocabulary parts) x (hidden
+// tiles) x (token tiles).  With few token tiles (narrow H, few rows, the
+// short last row chunk) one part per tile would leave most compute units
+// idle for a whole block's K loop, so the block's vocabulary range is cut
+// into parts, each summed in its own FP32 buffer, until about `target` dX
+// tiles are in flight: at most kMaxDxParts, and, where the extra parts share
+// a buffer of `part_tiles` token tiles, only as many as it holds
+// (part_tiles < 0: no such bound).
+constexpr int kMaxDxParts = 8;
+__host__ __device__ inline int dx_parts_for(int hidden_tiles, int token_tiles, int target,
+                                            int part_tiles) {
+  if (token_tiles <= 0) return 1;
+  const int per = hidden_tiles * token_tiles;
+  int s = (target + per - 1) / per;
+  if (s > kMaxDxParts) s = kMaxDxParts;
+  if (part_tiles >= 0 && s > 1 + part_tiles / token_tiles) s = 1 + part_tiles / token_tiles;
+  return s < 1 ? 1 : s;
+}
 
 
 constexpr int kStatusLabelRange = 8;
@@ -490,7 +510,9 @@ struct BwdArgs {
   float* dx32p;        // parts 1 .. dx_split - 1, [rows_pad, H] each, dx_stride
   int64_t dx_stride;   //   floats apart
   int dx_split;        // dX tiles per (token tile, hidden tile): the block's
-                       // vocabulary range cut into this many parts
+                       // vocabulary range cut into this many parts; 0: the
+                       // count is ctr->dx_parts and the parts lie TTn * 256
+                       // rows apart (chunked mode, set per chunk on the device)
   char* dW;            // [V, H] output (grad dtype)
   const Counters* ctr;
   int H, V, rows_pad, Vb;
@@ -869,12 +891,12 @@ __device__ __forceinline__ void dw_tile(const BwdArgs& a, int b, lds_t* smem) {
 // the load returns zeros and the store is dropped.
 template <bool kMasked>
 __device__ __forceinline__ void dx_add(const BwdArgs& a, const f32x16 (&acc)[4][4],
-                                       int part, int tau, int ht, int wm, int wn, int lane,
+                                       float* sum, int tau, int ht, int wm, int wn, int lane,
                                        int nlim, int hlim, lds_t* smem) {
-  // the descriptor starts at the token tile's first row (64-bit base), so
-  // the offsets stay below 256 * H * 4 bytes whatever the row count
-  float* base = (part == 0 ? a.dx32 : a.dx32p + (part - 1) * a.dx_stride) +
-                (int64_t)tau * kTile * a.H;
+  // sum: the part's [rows, H] FP32 array.  The descriptor starts at the token
+  // tile's first row (64-bit base), so the offsets stay below 256 * H * 4
+  // bytes whatever the row count
+  float* base = sum + (int64_t)tau * kTile * a.H;
   const rsrc_t xr = make_rsrc(base, (int64_t)kTile * a.H * 4);
   const int wave = threadIdx.x >> 6;
   auto offset = [&](int o, int x0) {
@@ -903,13 +925,15 @@ template <class E>
 __device__ __forceinline__ void dx_tile(const BwdArgs& a, int b, lds_t* smem) {
   const int n = a.ctr->n;
   const int TTn = (n + kTile - 1) / kTile;
+  const int S = a.dx_split > 0 ? a.dx_split : a.ctr->dx_parts;
+  const int64_t pstride = a.dx_split > 0 ? a.dx_stride : (int64_t)TTn * kTile * a.H;
   const int per_part = a.HT * TTn;
-  const int item = live_item(b, a.dx_split * per_part);
+  const int item = live_item(b, S * per_part);
   if (item < 0) return;
   const int part = item / per_part;
   int ht, tau;
   grouped(item - part * per_part, a.HT, TTn, ht, tau);
-  const int pw = (((a.vb + a.dx_split - 1) / a.dx_split) + 63) & ~63;
+  const int pw = (((a.vb + S - 1) / S) + 63) & ~63;
   const int m0 = part * pw;
   if (m0 >= a.vb) return;
   const int len = a.vb - m0 < pw ? a.vb - m0 : pw;
@@ -933,10 +957,11 @@ __device__ __forceinline__ void dx_tile(const BwdArgs& a, int b, lds_t* smem) {
   zero_acc(acc);
   gemm_tile<E, LoadMN<E>, LoadDirect>(A, B, steps, smem, wm, wn, acc);
 
+  float* const sum = part == 0 ? a.dx32 : a.dx32p + (part - 1) * pstride;
   const int nlim = n - tau * kTile, hlim = a.H - ht * kTile;
   if (nlim >= kTile && hlim >= kTile)
-    dx_add<false>(a, acc, part, tau, ht, wm, wn, lane, 0, 0, smem);
-  else dx_add<true>(a, acc, part, tau, ht, wm, wn, lane, nlim, hlim, smem);
+    dx_add<false>(a, acc, sum, tau, ht, wm, wn, lane, 0, 0, smem);
+  else dx_add<true>(a, acc, sum, tau, ht, wm, wn, lane, nlim, hlim, smem);
 }
 
 // One backward launch: nb_dx dX tiles and nb_dw dW tiles of block `cur`,
@@ -1009,7 +1034,9 @@ struct ChunkArgs {
   int* redo;            // [rows_pad] 1: the row is stored against its max
   int* redo_t;          // [C / 256] some row of the chunk's token tile is
   char* Xs;             // [C, H] the chunk's rows times fk (the dW operand)
+  float* dx32p;         // the dX tiles' extra vocabulary parts, part_tiles * 256 rows
   int H, V, Vp, C, row0, VT, TTc;
+  int HT, dx_target, part_tiles;   // the chunk's dX part count (dx_parts_for)
 };
 
 __device__ __forceinline__ int chunk_rows(const ChunkArgs& a) {
@@ -1172,13 +1199,23 @@ __global__ __launch_bounds__(256) void k_chunk_lse(ChunkArgs a) {
   const int lane = threadIdx.x & 63;
   const int kl = blockIdx.x * 4 + (threadIdx.x >> 6), k = a.row0 + kl;
   const int nc = chunk_rows(a);
+  const int ttc = (nc + kTile - 1) / kTile;
+  const int parts = dx_parts_for(a.HT, ttc, a.dx_target, a.part_tiles);
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     Counters c = *a.ctr;
     c.n = nc;
     c.fwd_p = 0;
+    c.dx_parts = parts;
     *a.cctr = c;
   }
   if (kl >= a.C) return;
+  // the row's FP32 sums of the extra dX parts start at zero (parts lie
+  // ttc * 256 rows apart; the dX tiles and k_dx_fold touch rows < nc only)
+  if (kl < nc)
+    for (int q = 1; q < parts; ++q) {
+      i32x4* d = (i32x4*)(a.dx32p + ((int64_t)(q - 1) * ttc * kTile + kl) * a.H);
+      for (int c = lane; c < a.H / 4; c += 64) d[c] = i32x4{0, 0, 0, 0};
+    }
   const int pieces = a.H * E::kBytes / 16;
   i32x4* xs = (i32x4*)(a.Xs + (int64_t)kl * a.H * E::kBytes);
   if (kl >= nc) {
@@ -1664,11 +1701,16 @@ __global__ __launch_bounds__(256) void k_oh_final(const uint64_t* __restrict__ k
 
 // dst[k, :] += sum over p = 0 .. parts - 1 of src_p[k, :] (src_p = src + p *
 // stride floats), in that order, for rows k < rows of H floats: folds a row
-// chunk's extra vocabulary parts of dX into the main FP32 sum.  Grid-stride,
-// 4 floats per thread step.
+// chunk's extra vocabulary parts of dX into the main FP32 sum.  The chunk's
+// counters give rows (n), parts + 1 (dx_parts) and the stride (the chunk's
+// token tiles times 256 rows).  Grid-stride, 4 floats per thread step.
 __global__ __launch_bounds__(256) void k_dx_fold(float* __restrict__ dst,
-                                                 const float* __restrict__ src, int parts,
-                                                 int64_t stride, int64_t count4) {
+                                                 const float* __restrict__ src,
+                                                 const Counters* __restrict__ cctr, int H) {
+  const int rows = cctr->n, parts = cctr->dx_parts - 1;
+  if (parts <= 0) return;
+  const int64_t stride = (int64_t)((rows + kTile - 1) / kTile) * kTile * H;
+  const int64_t count4 = (int64_t)rows * H / 4;
   for (int64_t i = blockIdx.x * 256ll + threadIdx.x; i < count4;
        i += (int64_t)gridDim.x * 256) {
     f32x4 v = *(const f32x4*)(dst + 4 * i);

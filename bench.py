@@ -78,6 +78,12 @@ MFMA_PROFILE_COMMANDS = (
     "--vendor-gemm-only",
     "python $R/bench.py --summarize-mfma $R/gpurun_out",
 )
+# the matrix cores' sustained rate with no memory traffic, by operand data
+# (profiles/mfma_ceiling.md): context for the roofline's published peak
+CEILING_COMMANDS = (
+    "$R/lm_head_linear_flce_amd/mfma_ceiling > $R/gpurun_out/mfma_ceiling.txt",
+    "python $R/bench.py --summarize-ceiling $R/gpurun_out",
+)
 # every bf16 workload through the bench (profiles/flce_workloads_bench.md)
 BENCH_WORKLOADS = ("tiny_f32", "qwen2_7b_head", "qwen3_sft_batch", "long_context", "ragged_vocab")
 WORKLOAD_BENCH_COMMANDS = tuple(
@@ -118,6 +124,8 @@ def parse():
     ap.add_argument("--summarize-workloads", metavar="DIR",
                     help="summarise DIR/bench_<workload>.json of WORKLOAD_BENCH_COMMANDS into "
                          "profiles/")
+    ap.add_argument("--summarize-ceiling", metavar="DIR",
+                    help="wrap DIR/mfma_ceiling.txt of CEILING_COMMANDS into profiles/")
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--summarize", metavar="DIR",
                     help="summarise the rocprofv3 output of PROFILE_COMMANDS under DIR "
@@ -377,6 +385,31 @@ def summarize_mfma(prof_dir):
     print(md)
 
 
+def summarize_ceiling(prof_dir):
+    """The ceiling probe's table (DIR/mfma_ceiling.txt) -> profiles/."""
+    with open(os.path.join(prof_dir, "mfma_ceiling.txt")) as f:
+        rows = [l.rstrip("\n") for l in f if l.startswith("|")]
+    if len(rows) < 3:
+        raise SystemExit("mfma_ceiling.txt holds no table")
+    out = ["# Matrix-core ceiling by operand data (MI355X, no memory traffic)", "",
+           "Commands ($R = repository root):", "", "```", *CEILING_COMMANDS, "```", "",
+           "One 256-thread workgroup per compute unit (one wave per SIMD), each wave 16 "
+           "independent 32x32 FP32 accumulators fed by v_mfma_f32_32x32x16_bf16 from operands "
+           "held in registers (no loads, no LDS), every MFMA pairing a different operand "
+           "combination; a few seconds per operand set. The clock column is the rate over "
+           "the published 2500 TFLOP/s times 2.4 GHz: the clock the matrix cores would need "
+           "at 100 % busy. The chip holds its top clock when the operand bits stay put and "
+           "lowers it when they toggle: the second and third rows are about the most a bf16 "
+           "contraction of such data can expect from the matrix cores on this chip (its "
+           "loads, LDS traffic and other instructions draw on the same power budget).", "",
+           *rows]
+    md = os.path.join(PROFILES, "mfma_ceiling.md")
+    with open(md, "w") as f:
+        f.write("\n".join(out) + "\n")
+    print(md)
+    return md
+
+
 def summarize_workloads(prof_dir):
     """One table over the bench lines of every workload -> profiles/."""
     rows = []
@@ -532,6 +565,9 @@ def main():
         return
     if args.summarize_workloads:
         summarize_workloads(args.summarize_workloads)
+        return
+    if args.summarize_ceiling:
+        summarize_ceiling(args.summarize_ceiling)
         return
     if args.summarize_mfma:
         summarize_mfma(args.summarize_mfma)

@@ -1,9 +1,10 @@
-"""Build libflce.so (the HIP kernels and the C ABI) in-tree for gfx950.
+"""Build libflce.so (the HIP kernels and the C ABI) in-tree for gfx950, and
+the matrix-core ceiling probe bench.py runs for context (mfma_ceiling).
 
     python lm_head_linear_flce_amd/build.py
 
-Cross-compiles on a machine without a GPU.  The library lands next to this file,
-where the Python binding loads it from.
+Cross-compiles on a machine without a GPU.  Both land next to this file, where
+the Python binding loads the library from.
 """
 from __future__ import annotations
 
@@ -18,6 +19,8 @@ LIB = os.path.join(HERE, "libflce.so")
 SOURCES = [os.path.join(CSRC, "flce_api.hip")]
 DEPS = SOURCES + [os.path.join(CSRC, f) for f in ("flce_tile.h", "flce_kernels.h")] + \
     [os.path.join(ROOT, "include", "flce.h")]
+CEILING = os.path.join(HERE, "mfma_ceiling")
+CEILING_SOURCE = os.path.join(CSRC, "mfma_ceiling.hip")
 
 
 def hipcc() -> str:
@@ -39,9 +42,17 @@ def command(out: str = LIB):
     ]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = command(tmp)
+def ceiling_command(out: str = CEILING):
+    return [
+        hipcc(), "--offload-arch=gfx950", "-O3", "-std=c++17",
+        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        "-o", out, CEILING_SOURCE,
+    ]
+
+
+def _run(cmd, out, verbose):
+    tmp = out + ".tmp"
+    cmd = cmd(tmp)
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -51,8 +62,14 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({r.returncode}):\n{err}")
     if verbose and err.strip():
         print(err)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile libflce.so and the ceiling probe; returns the library's path."""
+    _run(ceiling_command, CEILING, verbose)
+    return _run(command, LIB, verbose)
 
 
 def stale() -> bool:

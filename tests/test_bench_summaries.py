@@ -104,3 +104,18 @@ def test_workload_table_has_one_row_per_bench_line(out):
                     "nan | nan | nan | 5000 |",
                     "| qwen2_7b_head: N=8192 | 22.50 | 3.64e+05 | 2500 | 47.6 | 1.86 | 18.00 | "
                     "59.5 | 34.00 | 14.9 | 5.05 | 390 |"]
+
+
+def test_ceiling_summary_keeps_the_probe_table(out):
+    table = ["| operands | TFLOP/s | % of 2500 TFLOP/s | clock at 100 % busy (GHz) |",
+             "|---|---|---|---|",
+             "| constant operands (1.0) | 2434 | 97.4 | 2.34 |",
+             "| random sign and mantissa, one exponent (2^-7) | 1900 | 76.0 | 1.82 |"]
+    (out / "mfma_ceiling.txt").write_text("\n".join(["probe noise"] + table) + "\n")
+    md = open(bench.summarize_ceiling(str(out))).read()
+    for row in table:
+        assert row in md
+    assert "mfma_ceiling > $R/gpurun_out/mfma_ceiling.txt" in md
+    (out / "mfma_ceiling.txt").write_text("no table\n")
+    with pytest.raises(SystemExit):
+        bench.summarize_ceiling(str(out))

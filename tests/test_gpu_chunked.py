@@ -70,6 +70,23 @@ def test_chunked_several_chunks():
     check(w, got32, ref, what="chunked several fp32")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_short_last_chunk_takes_more_dx_parts(dtype):
+    """2100 rows in chunks of 1024: the last chunk holds 52 rows (one token
+    tile) and cuts its dX tiles into 8 vocabulary parts where the full chunks
+    (8 hidden x 4 token tiles) use 6, inside the same part buffer; every part
+    is summed once, in order, into that chunk's rows."""
+    w = synth.make_workload("short_last_chunk", B=1, T=2100, H=2048, V=3001, dtype=dtype,
+                            seed=919, shift=False, reduction="mean")
+    print(f"[chunked] short last chunk {dtype} N={w.N} H={w.H} V={w.V}", flush=True)
+    ref = oracle.flce(w.X, w.W, w.labels, ignore_index=w.ignore_index,
+                      reduction=w.reduction, shift=w.shift, mode="rows", chunk=1024)
+    assert ref["n_valid"] == 2100
+    check(w, run_chunked(w, chunk_rows=1024), ref, what=f"short last chunk {dtype}")
+    check(w, run_chunked(w, chunk_rows=1024, grad_dtype=torch.float32), ref,
+          what=f"short last chunk {dtype} fp32 grads")
+
+
 @pytest.mark.parametrize("chunk_rows", [256, 700])
 def test_chunked_explicit_chunk_rows(chunk_rows):
     # the pages' CHUNK_SIZE knob: many small chunks give the same result

@@ -393,10 +393,11 @@ def summarize_ceiling(prof_dir):
         raise SystemExit("mfma_ceiling.txt holds no table")
     out = ["# Matrix-core ceiling by operand data (MI355X, no memory traffic)", "",
            "Commands ($R = repository root):", "", "```", *CEILING_COMMANDS, "```", "",
-           "One 256-thread workgroup per compute unit (one wave per SIMD), each wave 16 "
-           "independent 32x32 FP32 accumulators fed by v_mfma_f32_32x32x16_bf16 from operands "
-           "held in registers (no loads, no LDS), every MFMA pairing a different operand "
-           "combination; a few seconds per operand set. The clock column is the rate over "
+           "One 256-thread workgroup per compute unit (one wave per SIMD), each wave a 128 x 128 "
+           "block of FP32 accumulators (all 256 AGPRs): 16 of v_mfma_f32_32x32x16_bf16 or 64 of "
+           "v_mfma_f32_16x16x32_bf16, fed from operands held in registers (no loads, no LDS), "
+           "every MFMA pairing a different operand combination; a few seconds per run. The "
+           "clock column is the rate over "
            "the published 2500 TFLOP/s times 2.4 GHz: the clock the matrix cores would need "
            "at 100 % busy. The chip holds its top clock when the operand bits stay put and "
            "lowers it when they toggle: the second and third rows are about the most a bf16 "

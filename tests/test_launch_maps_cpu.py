@@ -63,3 +63,32 @@ def test_backward_items(TT, TTn, tiles_per_row):
     # G / dX / dW tiles: grid pad8(kinds x TT) sized for the bound, real items
     # over the valid rows' TTn token tiles
     assert covered(pad8(tiles_per_row * TT), tiles_per_row * TTn)
+
+
+def dx_parts_for(hidden_tiles, token_tiles, target, part_tiles):
+    # the vocabulary parts of a launch's dX tiles (flce_kernels.h)
+    if token_tiles <= 0:
+        return 1
+    per = hidden_tiles * token_tiles
+    s = min(-(-target // per), 8)
+    if part_tiles >= 0:
+        s = min(s, 1 + part_tiles // token_tiles)
+    return max(s, 1)
+
+
+@pytest.mark.parametrize("H,C", [(3584, 3328), (4096, 3328), (2048, 3328), (1024, 1792),
+                                 (256, 256), (2048, 1024), (65536, 256)])
+def test_chunked_dx_grid_covers_every_chunk(H, C):
+    # chunked mode: the part count is set per chunk on the device from the
+    # chunk's rows; the host sizes the dX workgroups for the largest count any
+    # chunk of at most C rows can take, and the part buffer for the extra parts
+    HT, TTc, target = -(-H // 256), C // 256, 176
+    full = dx_parts_for(HT, TTc, target, -1)
+    part_tiles = max((full - 1) * TTc, -(-TTc // 2))
+    blocks = pad8(max(dx_parts_for(HT, tt, target, part_tiles) * HT * tt
+                      for tt in range(1, TTc + 1)))
+    assert dx_parts_for(HT, TTc, target, part_tiles) == full   # full chunks unchanged
+    for tt in range(1, TTc + 1):
+        s = dx_parts_for(HT, tt, target, part_tiles)
+        assert (s - 1) * tt <= part_tiles                      # the parts fit the buffer
+        assert covered(blocks, s * HT * tt)

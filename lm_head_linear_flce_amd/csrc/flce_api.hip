@@ -60,6 +60,8 @@ struct Plan {
 #ifndef FLCE_DX_TILES
 #define FLCE_DX_TILES 256
 #endif
+// token tiles of extra dX parts kept for a short last chunk (at most)
+constexpr int64_t kShortChunkTiles = 16;
 #ifndef FLCE_DX_TILES_CHUNKED
 #define FLCE_DX_TILES_CHUNKED 176
 #endif
@@ -498,12 +500,14 @@ int make_chunk_plan(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, int64
   q.o_xs = take(q.C * H * q.es);
   q.o_slab = take(q.C * q.Vp * q.es);
   // dX parts: a full chunk's as its token tiles ask; the buffer of the extra
-  // parts holds that many full chunks' rows, and at least half a chunk's, so
-  // a short last chunk (few token tiles) can take more parts.  The parts
-  // cover one chunk's rows and are folded into the main FP32 sum after it.
+  // parts holds that many full chunks' rows, and at least half a chunk's (at
+  // most 16 token tiles of it), so a short last chunk (few token tiles) can
+  // take more parts.  The parts cover one chunk's rows and are folded into the
+  // main FP32 sum after it.
   const int HT = (int)cdiv(H, kTile), TTc = (int)(q.C / kTile);
   q.dx_split = dx_parts_for(HT, TTc, FLCE_DX_TILES_CHUNKED, -1);
-  q.part_tiles = std::max<int64_t>((q.dx_split - 1) * TTc, cdiv(TTc, 2));
+  q.part_tiles = std::max<int64_t>((q.dx_split - 1) * TTc,
+                                   std::min<int64_t>(cdiv(TTc, 2), kShortChunkTiles));
   q.dx_blocks = 0;
   for (int tt = 1; tt <= TTc; ++tt)
     q.dx_blocks = std::max<int64_t>(

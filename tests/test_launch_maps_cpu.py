@@ -77,14 +77,14 @@ def dx_parts_for(hidden_tiles, token_tiles, target, part_tiles):
 
 
 @pytest.mark.parametrize("H,C", [(3584, 3328), (4096, 3328), (2048, 3328), (1024, 1792),
-                                 (256, 256), (2048, 1024), (65536, 256)])
+                                 (256, 256), (2048, 1024), (65536, 256), (4096, 65536)])
 def test_chunked_dx_grid_covers_every_chunk(H, C):
     # chunked mode: the part count is set per chunk on the device from the
     # chunk's rows; the host sizes the dX workgroups for the largest count any
     # chunk of at most C rows can take, and the part buffer for the extra parts
     HT, TTc, target = -(-H // 256), C // 256, 176
     full = dx_parts_for(HT, TTc, target, -1)
-    part_tiles = max((full - 1) * TTc, -(-TTc // 2))
+    part_tiles = max((full - 1) * TTc, min(-(-TTc // 2), 16))
     blocks = pad8(max(dx_parts_for(HT, tt, target, part_tiles) * HT * tt
                       for tt in range(1, TTc + 1)))
     assert dx_parts_for(HT, TTc, target, part_tiles) == full   # full chunks unchanged

@@ -80,3 +80,54 @@ def test_per_token_bad_label_is_nan():
     loss, _, _, st = F.forward(X, W, lab, w.ignore_index, w.shift, "none")
     torch.cuda.synchronize()
     assert int(st) == F.FLCE_ERR_LABEL_RANGE and torch.isnan(loss).all()
+
+
+@pytest.mark.parametrize("mode", ["recompute", "chunked"])
+def test_per_token_full_size_against_stored_oracle(mode):
+    """Reduction "none" at the full Qwen2-7B-like head (N = 8192, V = 152064):
+    every valid row's loss against the stored float64 lse minus the row's
+    target logit (a float64 dot product), and the stored dX rows scaled by the
+    row's upstream gradient: dX_i = g_i (softmax - onehot)_i W, where the stored
+    mean-reduction rows carry the factor grad_scale / n."""
+    import os
+    from test_gpu_parity import GOLDEN
+    path = os.path.join(GOLDEN, "full_qwen2_7b_head.npz")
+    if not os.path.exists(path):
+        pytest.skip(f"{path} not generated (tests/golden/make_full_expected.py)")
+    e = np.load(path)
+    w = synth.workload("qwen2_7b_head")
+    y, valid = oracle.targets(w.labels, w.shift, w.ignore_index)
+    n, gs = int(e["n_valid"]), float(e["grad_scale"])
+    assert n == int(valid.sum())
+    rng = np.random.Generator(np.random.PCG64(4242))
+    g = (rng.uniform(0.5, 1.5, size=w.N) * rng.choice([-1.0, 1.0], size=w.N)).astype(np.float32)
+    print(f"[per-token full] {mode}", flush=True)
+    X, W, lab = to_device(w)
+    gt = torch.from_numpy(g).to(DEV)
+    if mode == "recompute":
+        loss, lse, _, st = F.forward(X, W, lab, w.ignore_index, w.shift, "none")
+        dX, _, bst = F.backward(X, W, lab, lse, grad_scale=gt, ignore_index=w.ignore_index,
+                                shift=w.shift, reduction="none")
+    else:
+        loss, _, _, dX, _, st = F.chunked(X, W, lab, grad_scale=gt, ignore_index=w.ignore_index,
+                                          shift=w.shift, reduction="none")
+        bst = st
+    torch.cuda.synchronize()
+    assert int(st) == 0 and int(bst) == 0
+    got = loss.double().cpu().numpy().reshape(-1)
+    zt = np.einsum("ij,ij->i", w.X[valid].astype(np.float64), w.W[y[valid]].astype(np.float64))
+    want = np.zeros(w.N)
+    want[valid] = e["lse"].astype(np.float64)[valid] - zt
+    tol = TOL[w.dtype]
+    err = np.abs(got - want)
+    assert err[valid].max() <= LSE_ABS + tol["loss_rel"] * np.abs(want[valid]).max(), err.max()
+    assert np.all(got[~valid] == 0.0)
+    dXh = dX.reshape(w.N, w.H).double().cpu().numpy()
+    for q, r in enumerate(e["dx_rows"]):
+        b = e["dx"][q].astype(np.float64) * (float(g[r]) * n / gs)
+        a = dXh[r]
+        if not np.any(b):
+            assert not np.any(a), f"dX row {r}"
+            continue
+        assert oracle.cosine(a, b) >= 0.999, f"dX row {r}"
+        assert np.abs(a - b).max() <= 1e-2 * np.abs(b).max(), f"dX row {r}"

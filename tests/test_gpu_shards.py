@@ -84,3 +84,53 @@ def test_single_shard_is_the_plain_forward():
     torch.cuda.synchronize()
     assert torch.equal(lse_s, lse)
     assert abs(float(loss2) - float(loss)) <= 1e-6 * abs(float(loss))
+
+
+def test_eight_shards_full_size_against_stored_oracle():
+    """The full Qwen2-7B-like head cut into 8 uneven vocabulary shards (the
+    per-device share of an 8-way column-parallel output layer, ~19K rows
+    each): the merged loss and every row's lse against the stored float64
+    values, the summed FP32 dX partials (one rounding) and the concatenated
+    shard dW rows on the stored sampled rows."""
+    import os
+    from gpu_util import check_sampled_rows
+    from test_gpu_parity import GOLDEN
+    path = os.path.join(GOLDEN, "full_qwen2_7b_head.npz")
+    if not os.path.exists(path):
+        pytest.skip(f"{path} not generated (tests/golden/make_full_expected.py)")
+    e = np.load(path)
+    w = synth.workload("qwen2_7b_head")
+    print("[shards full] 8 shards", flush=True)
+    X, W, lab = to_device(w)
+    parts = _cuts(w.V, 8)
+    lses, zts = [], []
+    for v0, v1 in parts:
+        lse_s, zt_s, st = F.shard_forward(X, W[v0:v1], lab, v0, w.V,
+                                          ignore_index=w.ignore_index, shift=w.shift)
+        assert int(st) == 0
+        lses.append(lse_s)
+        zts.append(zt_s)
+    loss, lse, n_valid, st = F.shard_merge(torch.stack(lses), torch.stack(zts), lab, w.V,
+                                           ignore_index=w.ignore_index, shift=w.shift,
+                                           reduction=w.reduction)
+    dX32 = torch.zeros((w.N, w.H), dtype=torch.float32, device=DEV)
+    dWs = []
+    for v0, v1 in parts:
+        dXp, dW_s, bst = F.shard_backward(X, W[v0:v1], lab, lse, v0, w.V,
+                                          ignore_index=w.ignore_index, shift=w.shift,
+                                          reduction=w.reduction)
+        assert int(bst) == 0
+        dX32 += dXp.reshape(w.N, w.H)
+        dWs.append(dW_s)
+    torch.cuda.synchronize()
+    assert int(st) == 0 and int(n_valid) == int(e["n_valid"])
+    tol = TOL[w.dtype]
+    _, valid = oracle.targets(w.labels, w.shift, w.ignore_index)
+    got_lse = lse.double().cpu().numpy()
+    assert np.abs(got_lse[valid] - e["lse"][valid]).max() <= LSE_ABS
+    assert np.all(got_lse[~valid] == 0.0)
+    assert abs(float(loss) - float(e["loss"])) <= tol["loss_rel"] * abs(float(e["loss"]))
+    got = dict(dX=dX32.to(X.dtype).double().cpu().numpy(),
+               dW=torch.cat(dWs).double().cpu().numpy())
+    check_sampled_rows(w, got, e, what="8 shards")
+    assert np.all(got["dX"][~valid] == 0.0)

@@ -313,6 +313,47 @@ def test_dW_accumulates_over_micro_batches(mode, grad_dtype):
 
 
 @pytest.mark.parametrize("mode", ["recompute", "chunked"])
+def test_full_size_fp32_gradients_accumulated_twice(mode):
+    """The full Qwen2-7B-like head with FP32 gradient outputs, the same batch
+    twice into one dW (dW_accumulate): the sampled dX rows equal the stored
+    oracle's, the sampled dW rows twice the stored ones."""
+    path = os.path.join(GOLDEN, "full_qwen2_7b_head.npz")
+    if not os.path.exists(path):
+        pytest.skip(f"{path} not generated (tests/golden/make_full_expected.py)")
+    e = np.load(path)
+    w = synth.workload("qwen2_7b_head")
+    print(f"[full fp32 accumulate] {mode}", flush=True)
+    X, W, lab = to_device(w)
+    dW = None
+    for k in range(2):
+        if mode == "recompute":
+            _, lse, _, st = F.forward(X, W, lab, w.ignore_index, w.shift, w.reduction)
+            dX, dW, bst = F.backward(X, W, lab, lse, ignore_index=w.ignore_index,
+                                     shift=w.shift, reduction=w.reduction,
+                                     grad_dtype=torch.float32, dW=dW, accumulate=k > 0)
+        else:
+            _, _, _, dX, dW, st = F.chunked(X, W, lab, ignore_index=w.ignore_index,
+                                            shift=w.shift, reduction=w.reduction,
+                                            grad_dtype=torch.float32, dW=dW,
+                                            accumulate=k > 0)
+            bst = st
+        torch.cuda.synchronize()
+        assert int(st) == 0 and int(bst) == 0
+    assert dX.dtype == torch.float32 and dW.dtype == torch.float32
+    dXh = dX.reshape(w.N, w.H)[torch.from_numpy(e["dx_rows"]).to(DEV)].double().cpu().numpy()
+    dWh = dW[torch.from_numpy(e["dw_rows"]).to(DEV)].double().cpu().numpy()
+    for name, got, want in (("dX", dXh, e["dx"].astype(np.float64)),
+                            ("dW", dWh, 2.0 * e["dw"].astype(np.float64))):
+        assert oracle.cosine(got, want) >= 0.9999, name
+        for q in range(len(want)):
+            if not np.any(want[q]):
+                assert not np.any(got[q]), (name, q)
+                continue
+            assert oracle.cosine(got[q], want[q]) >= 0.999, (name, q)
+            assert np.abs(got[q] - want[q]).max() <= 1e-2 * np.abs(want[q]).max(), (name, q)
+
+
+@pytest.mark.parametrize("mode", ["recompute", "chunked"])
 def test_one_target_over_many_rows(mode):
     """Most rows share one target, so that target's rows span many
     256-position blocks of the sorted (target, row) order and its one-hot sum

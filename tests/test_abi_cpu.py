@@ -322,3 +322,15 @@ def test_long_sequences_are_accepted(B, T, H, V):
         assert 0 < ws < B * T * V * 2
         cws = F.flce_chunked_workspace_size(B, T, H, V, dt)
         assert 0 < cws < B * T * V * 2
+
+
+def test_huge_vocabulary_recompute_only():
+    # V past 2^24: the recompute path plans it (workspace linear in V for the
+    # one-hot map, not in N * V); the chunked mode refuses it, as one 256-row
+    # chunk of its [C, V] slab would pass 2^31 bytes
+    V = 2 ** 24 + 43
+    ws = F.flce_workspace_size(1, 256, 64, V, F.FLCE_DTYPE_BF16)
+    assert 0 < ws < 256 * V * 2
+    with pytest.raises(F.FlceError) as e:
+        F.flce_chunked_workspace_size(1, 256, 64, V, F.FLCE_DTYPE_BF16)
+    assert e.value.code == F.FLCE_ERR_SHAPE

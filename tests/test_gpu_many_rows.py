@@ -98,3 +98,52 @@ def test_rows_times_hidden_past_2_30():
     2^31 bytes of X, so their loaders rebase the buffer descriptor at every K
     step."""
     _long_rows_case(532480, 2048, 97, 7723)
+
+
+def test_vocabulary_past_2_24_weight_past_2_31_bytes():
+    """V = 2^24 + 43 at H = 64: W holds 2.1 GB of bf16 (past 2^31 bytes), the
+    forward walks 65537 vocabulary tiles per token tile, the backward 33
+    launches of 2^19-column blocks, and dW is written past 2^31 bytes.  Every
+    valid row's lse, the loss, sampled dX rows and dW rows at the ends of the
+    vocabulary, around 2^24 and on block edges, against the float64 oracle.
+    (The chunked mode refuses this shape: one 256-row chunk of the softmax
+    slab would pass 2^31 bytes.)"""
+    T, H, V = 256, 64, 2 ** 24 + 43
+    w = synth.make_workload("huge_vocab", B=1, T=T, H=H, V=V, dtype="bf16", seed=7733,
+                            labels="uniform", mask="count", mask_arg=21, shift=False,
+                            reduction="mean")
+    print(f"[huge-vocab] N={w.N} H={H} V={V} bf16", flush=True)
+    X = torch.from_numpy(w.X).to(DEV).to(torch.bfloat16)
+    W = torch.from_numpy(w.W).to(DEV).to(torch.bfloat16)
+    lab = torch.from_numpy(w.labels).to(DEV)
+    loss, lse, n_valid, status = F.forward(X, W, lab, w.ignore_index, w.shift, w.reduction)
+    dX, dW, bstatus = F.backward(X, W, lab, lse, ignore_index=w.ignore_index, shift=w.shift,
+                                 reduction=w.reduction)
+    torch.cuda.synchronize()
+    y, valid = oracle.targets(w.labels, w.shift, w.ignore_index)
+    n = int(valid.sum())
+    assert int(status) == 0 and int(bstatus) == 0 and int(n_valid) == n
+    # the whole-vocabulary logits of 16 rows at a time (2.1 GB of float64)
+    ref = oracle.forward_rows(w.X, w.W, w.labels, ignore_index=w.ignore_index, chunk=16)
+    got_lse = lse.double().cpu().numpy()
+    assert np.abs(got_lse[valid] - ref["lse"][valid]).max() <= LSE_ABS
+    assert np.all(got_lse[~valid] == 0.0)
+    assert abs(float(loss) - ref["loss"]) <= TOL["bf16"]["loss_rel"] * abs(ref["loss"])
+    c = 1.0 / n
+    xrows = np.concatenate([np.flatnonzero(valid)[[0, 1, n // 2, n - 1]],
+                            np.flatnonzero(~valid)[:2]])
+    want_x = oracle.dx_rows(w.X, w.W, y, valid, ref["lse"], c, xrows)
+    got_x = dX.reshape(w.N, H)[torch.from_numpy(xrows).to(DEV)].double().cpu().numpy()
+    block = 1 << 19
+    vids = np.unique(np.concatenate([
+        [0, 1, 255, 256, block - 1, block, 2 ** 24 - 1, 2 ** 24, 2 ** 24 + 1, V - 2, V - 1],
+        y[valid][:6]]))
+    want_w = oracle.dw_rows(w.X, w.W, y, valid, ref["lse"], c, vids)
+    got_w = dW[torch.from_numpy(vids).to(DEV)].double().cpu().numpy()
+    for name, got, want in (("dX", got_x, want_x), ("dW", got_w, want_w)):
+        for q in range(len(want)):
+            if not np.any(want[q]):
+                assert not np.any(got[q]), (name, q)
+                continue
+            assert oracle.cosine(got[q], want[q]) >= 0.999, (name, q)
+            assert np.abs(got[q] - want[q]).max() <= 1e-2 * np.abs(want[q]).max(), (name, q)

@@ -334,3 +334,12 @@ def test_huge_vocabulary_recompute_only():
     with pytest.raises(F.FlceError) as e:
         F.flce_chunked_workspace_size(1, 256, 64, V, F.FLCE_DTYPE_BF16)
     assert e.value.code == F.FLCE_ERR_SHAPE
+
+
+def test_rows_bound_by_the_softmax_slab():
+    # the narrowest vocabulary block (256 columns) of a rows_pad-row slab must
+    # stay below 2^31 bytes: 2^22 - 256 bf16 rows pass, one more tile does not
+    assert F.flce_workspace_size(1, 2 ** 22 - 256, 8, 300, F.FLCE_DTYPE_BF16) > 0
+    with pytest.raises(F.FlceError) as e:
+        F.flce_workspace_size(1, 2 ** 22, 8, 300, F.FLCE_DTYPE_BF16)
+    assert e.value.code == F.FLCE_ERR_SHAPE

@@ -147,3 +147,12 @@ def test_vocabulary_past_2_24_weight_past_2_31_bytes():
                 continue
             assert oracle.cosine(got[q], want[q]) >= 0.999, (name, q)
             assert np.abs(got[q] - want[q]).max() <= 1e-2 * np.abs(want[q]).max(), (name, q)
+
+
+def test_rows_at_the_softmax_slab_bound():
+    """N = 2^22 - 256 rows at H = 8: the narrowest vocabulary block (256
+    columns) of the softmax slab then spans 2^31 - 131072 bytes, the last
+    slab offset before the 32-bit bound the plan enforces (one more token
+    tile is FLCE_ERR_SHAPE), and the dW tiles' K loop over 4 million rows runs
+    with per-step descriptors."""
+    _long_rows_case(2 ** 22 - 256, 8, 300, 7725)

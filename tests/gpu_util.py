@@ -131,7 +131,7 @@ def soft_tolerance(w):
     bf16 with relative rounding 2^-9 per entry); the one-hot part is added in
     FP32 to the gradient sums.  With bf16 inputs the rebuilt soft parts then
     carry only that per-entry rounding noise plus the FP32 accumulation:
-    cosine >= 0.999 and the norm within 0.5 % (SURVEY's diagnostic bar).  A
+    cosine >= 0.999 and the norm within 0.5 %.  A
     missing or misplaced softmax term gives a cosine near 0, a wrong scale a
     norm ratio far from 1."""
     if w.dtype == "f32":

@@ -105,7 +105,7 @@ def parse():
     ap.add_argument("--no-chunked", action="store_true",
                     help="skip the chunked-mode measurement")
     ap.add_argument("--chunk-rows", type=int, default=0,
-                    help="rows per chunk of the chunked mode (0 = 1 GiB slab budget)")
+                    help="rows per chunk of the chunked mode (0 = as many as a 2 GiB slab holds)")
     ap.add_argument("--chunked-only", action="store_true",
                     help="measure only the chunked mode and print its figures (for "
                          "CHUNKED_PROFILE_COMMANDS)")

@@ -417,10 +417,13 @@ void zero_fill(void* p, int64_t bytes, hipStream_t s) {
 // Chunked mode (one call for loss, lse, dX and dW)
 // ---------------------------------------------------------------------------
 #ifndef FLCE_CHUNK_MIB
-#define FLCE_CHUNK_MIB 1024
+#define FLCE_CHUNK_MIB 2048
 #endif
 // the [C, Vp] softmax-gradient slab of one row chunk holds at most this many
-// bytes (unless one 256-row tile of it already needs more)
+// bytes (unless one 256-row tile of it already needs more); by default as
+// many rows as the slab's 32-bit offsets reach (2^31 - 1 bytes): larger
+// chunks give the dW tiles, whose K loop runs over the chunk's rows, deeper
+// loops, and fewer chunks fewer launches and short last chunks
 constexpr int64_t kChunkBudget = (int64_t)FLCE_CHUNK_MIB << 20;
 // vocabulary block of the dX / dW launches inside a chunk
 #ifndef FLCE_CHUNK_VB
@@ -445,7 +448,7 @@ struct ChunkPlan {
 };
 
 // chunk_rows: rows per chunk wanted (rounded up to 256); 0 = as many as the
-// 1 GiB slab budget allows.  Never more than the padded row count or what
+// slab budget allows.  Never more than the padded row count or what
 // 32-bit slab offsets reach.
 int make_chunk_plan(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, int64_t chunk_rows,
                     ChunkPlan* p) {

@@ -76,7 +76,8 @@ def dx_parts_for(hidden_tiles, token_tiles, target, part_tiles):
     return max(s, 1)
 
 
-@pytest.mark.parametrize("H,C", [(3584, 3328), (4096, 3328), (2048, 3328), (1024, 1792),
+@pytest.mark.parametrize("H,C", [(3584, 6912), (4096, 6912), (2048, 6912), (1024, 3840),
+                                 (3584, 3328), (2048, 3328), (1024, 1792),
                                  (256, 256), (2048, 1024), (65536, 256), (4096, 65536)])
 def test_chunked_dx_grid_covers_every_chunk(H, C):
     # chunked mode: the part count is set per chunk on the device from the

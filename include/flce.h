@@ -253,9 +253,10 @@ int flce_shard_backward(const void* X, const void* W, const int64_t* labels,
  * of memory proportional to the chunk.
  *
  * chunk_rows (both calls, which must agree): rows per chunk, rounded up to a
- * multiple of 256 (the pages' CHUNK_SIZE); 0 = as many as a slab of 2^31 - 1
- * bytes holds (6912 rows at V = 152064 bf16).  Capped at the padded row count
- * and at 2^31 - 1 bytes of slab.
+ * multiple of 256 (the pages' CHUNK_SIZE); 0 = as many as a 2 GiB slab holds
+ * (6912 rows at V = 152064 bf16).  Capped at the padded row count.  A 256-row
+ * tile of the slab must stay below 2^31 bytes (V <= 4194048 for bf16,
+ * 2096896 for fp32), else FLCE_ERR_SHAPE.
  *
  * flce_chunked_workspace_size -- bytes of device scratch flce_chunked needs
  * (host-only arithmetic).  Other arguments as flce_workspace_size.

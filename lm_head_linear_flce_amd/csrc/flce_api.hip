@@ -420,10 +420,11 @@ void zero_fill(void* p, int64_t bytes, hipStream_t s) {
 #define FLCE_CHUNK_MIB 2048
 #endif
 // the [C, Vp] softmax-gradient slab of one row chunk holds at most this many
-// bytes (unless one 256-row tile of it already needs more); by default as
-// many rows as the slab's 32-bit offsets reach (2^31 - 1 bytes): larger
-// chunks give the dW tiles, whose K loop runs over the chunk's rows, deeper
-// loops, and fewer chunks fewer launches and short last chunks
+// bytes (unless one 256-row tile of it already needs more): 6912 rows at
+// V = 152064 bf16.  Larger chunks give the dW tiles, whose K loop runs over
+// the chunk's rows, deeper loops, and fewer chunks fewer launches and short
+// last chunks; past 2 GiB the steps gain little more (about 2 % for four
+// times the memory), so a caller with memory to spare passes chunk_rows
 constexpr int64_t kChunkBudget = (int64_t)FLCE_CHUNK_MIB << 20;
 // vocabulary block of the dX / dW launches inside a chunk
 #ifndef FLCE_CHUNK_VB
@@ -448,8 +449,7 @@ struct ChunkPlan {
 };
 
 // chunk_rows: rows per chunk wanted (rounded up to 256); 0 = as many as the
-// slab budget allows.  Never more than the padded row count or what
-// 32-bit slab offsets reach.
+// slab budget allows.  Never more than the padded row count.
 int make_chunk_plan(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, int64_t chunk_rows,
                     ChunkPlan* p) {
   Plan base;
@@ -465,12 +465,13 @@ int make_chunk_plan(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, int64
   q.VT = base.VT;
   q.Vp = q.VT * kTile;
   if (chunk_rows < 0) return FLCE_ERR_SHAPE;
+  // one token tile of the slab within 32-bit offsets (each tile's accesses
+  // start from its own 64-bit base)
+  if (kTile * q.Vp * q.es > kMaxI32) return FLCE_ERR_SHAPE;
   int64_t c = chunk_rows > 0 ? round_up(chunk_rows, kTile)
-                             : std::min(kChunkBudget, kMaxI32) / (q.Vp * q.es) / kTile * kTile;
-  c = std::min(c, kMaxI32 / (q.Vp * q.es) / kTile * kTile);
+                             : kChunkBudget / (q.Vp * q.es) / kTile * kTile;
   if (c < kTile) c = kTile;
   q.C = std::min(c, q.rows_pad);
-  if (q.C * q.Vp * q.es > kMaxI32) return FLCE_ERR_SHAPE;
   q.nchunks = cdiv(q.rows_pad, q.C);
   // vocabulary block of the dX / dW launches: its W rows stay below 2^31
   // bytes (one descriptor per dX tile operand)

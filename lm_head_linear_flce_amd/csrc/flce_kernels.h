@@ -1089,10 +1089,13 @@ __device__ __forceinline__ void z_store(const ChunkArgs& a, const f32x16 (&acc)[
     sum[j] += v;
     return v * sc[j];
   };
-  const rsrc_t er = make_rsrc(a.E, (int64_t)a.C * a.Vp * E::kBytes);
+  // the descriptor starts at the token tile's first slab row (64-bit base), so
+  // the offsets stay below 256 * Vp * 4 bytes whatever the chunk's row count
+  const rsrc_t er = make_rsrc(a.E + (int64_t)tau * kTile * a.Vp * E::kBytes,
+                              (int64_t)kTile * a.Vp * E::kBytes);
   const int wave = threadIdx.x >> 6;
   if constexpr (E::kBytes == 2) {
-    const int tok0 = tau * kTile + wn * 128, voc0 = vt * kTile + wm * 128;
+    const int tok0 = wn * 128, voc0 = vt * kTile + wm * 128;   // tok0: within the tile
     store_quarter_bf16(
         smem + wave * 32768, lane, val,
         [&](int o, int x0, i32x4 v) {
@@ -1107,7 +1110,7 @@ __device__ __forceinline__ void z_store(const ChunkArgs& a, const f32x16 (&acc)[
     for (int j = 0; j < 4; ++j) {
       __builtin_amdgcn_sched_barrier(0);
       begin(j);
-      const int tok = tau * kTile + acc_col(wn, j, lane);
+      const int tok = acc_col(wn, j, lane);   // within the tile
       const bool st = (keep[j] >> (lane & 31)) & 1;
 #pragma unroll
       for (int i = 0; i < 4; ++i)

@@ -190,6 +190,21 @@ def test_chunked_workspace_is_bounded_by_the_chunk():
     assert w2 < 32768 * V * 2                # far below the logits
 
 
+def test_chunk_rows_past_the_2_31_byte_slab():
+    # explicit chunks whose slab passes 2^31 bytes are accepted (each token
+    # tile of the slab has its own 64-bit base); a vocabulary whose 256-row
+    # slab tile passes 2^31 bytes is refused
+    H, V = 4096, 151936
+    vp = (V + 255) // 256 * 256
+    w = F.flce_chunked_workspace_size(1, 16384, H, V, F.FLCE_DTYPE_BF16, 10240)
+    assert w >= 10240 * vp * 2 > (1 << 31)
+    for V, dt in ((4194048, F.FLCE_DTYPE_BF16), (2096896, F.FLCE_DTYPE_F32)):
+        assert F.flce_chunked_workspace_size(1, 512, 64, V, dt) > 0
+        with pytest.raises(F.FlceError) as e:
+            F.flce_chunked_workspace_size(1, 512, 64, V + 1, dt)
+        assert e.value.code == F.FLCE_ERR_SHAPE
+
+
 def test_chunk_rows_parameter():
     # explicit chunk sizes round up to 256 rows; the slab is chunk x padded V
     H, V, es = 1024, 50000, 2

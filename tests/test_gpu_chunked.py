@@ -221,6 +221,29 @@ def test_full_size_chunked_against_stored_oracle(name, grad_dtype):
     assert np.all(got["dX"][~valid] == 0.0)
 
 
+@pytest.mark.parametrize("name,chunk_rows", [("qwen3_sft_batch", 10240),
+                                             ("long_context", 24576)])
+def test_full_size_one_chunk_slab_past_2_31_bytes(name, chunk_rows):
+    """All valid rows in one chunk whose softmax slab passes 2^31 bytes (3.1 GB
+    for the Qwen3 batch, 7.5 GB, past 2^32, at long context): every token
+    tile of the slab is stored and read from its own 64-bit base, against the
+    oracle's stored values at the full size."""
+    path = os.path.join(GOLDEN, f"full_{name}.npz")
+    if not os.path.exists(path):
+        pytest.skip(f"{path} not generated (tests/golden/make_full_expected.py)")
+    e = np.load(path)
+    w = synth.workload(name)
+    vp = (w.V + 255) // 256 * 256
+    assert int(e["n_valid"]) <= chunk_rows and chunk_rows * vp * 2 > (1 << 31)
+    print(f"[full chunked, one chunk] {name} chunk_rows={chunk_rows}", flush=True)
+    got = run_chunked(w, chunk_rows=chunk_rows)
+    ref = dict(n_valid=int(e["n_valid"]), loss=float(e["loss"]), lse=e["lse"],
+               dX=e["dx"], dW=e["dw"])
+    check(w, got, ref, dx_rows=e["dx_rows"], dw_rows=e["dw_rows"],
+          what=f"chunked {name} one chunk")
+    check_sampled_rows(w, got, e, what=f"chunked {name} one chunk")
+
+
 def test_round_once_over_many_chunks():
     """bf16 gradients over many row chunks: with round_once the chunked mode
     keeps dW in FP32 across the chunks and rounds once, so it matches the

@@ -19,8 +19,16 @@ constexpr int64_t kAlign = 256;
 #define FLCE_SLAB_MIB 512
 #endif
 // backward: both softmax-gradient slabs together hold at most this many bytes
-// (unless a single 256-wide vocabulary tile per row already needs more)
+// (unless a single 256-wide vocabulary tile per row already needs more), or
+// up to twice as many to bring blocks narrower than kMinVocabBlock closer to
+// it: a dX tile's K loop runs over the block, and below 128 steps its fixed
+// cost (first loads, the FP32 read-modify-write epilogue) weighs more than
+// the larger slabs cost
 constexpr int64_t kSlabBudget = (int64_t)FLCE_SLAB_MIB << 20;
+#ifndef FLCE_MIN_VB
+#define FLCE_MIN_VB 8192
+#endif
+constexpr int64_t kMinVocabBlock = FLCE_MIN_VB;
 constexpr int64_t kMaxI32 = 0x7FFFFFFFll;
 
 int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
@@ -88,8 +96,10 @@ int make_plan(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, Plan* p) {
   // this many rows, whatever V is (and narrow enough for 32-bit offsets)
   // (the dX tiles address a whole block of W rows, and the dW tiles the
   // whole slab, from one descriptor each: both below 2^31 bytes)
-  int64_t vb = std::min<int64_t>({kSlabBudget / (2 * q.rows_pad * q.es),
-                                  kMaxI32 / (q.rows_pad * q.es), kMaxI32 / (H * q.es)});
+  const int64_t per_col = 2 * q.rows_pad * q.es;   // both slabs, one column
+  int64_t vb = std::max<int64_t>(kSlabBudget / per_col,
+                                 std::min<int64_t>(kMinVocabBlock, 2 * kSlabBudget / per_col));
+  vb = std::min<int64_t>({vb, kMaxI32 / (q.rows_pad * q.es), kMaxI32 / (H * q.es)});
   vb = std::max<int64_t>(kTile, vb / kTile * kTile);
   vb = std::min<int64_t>(vb, round_up(V, kTile));
   q.Vb = vb;

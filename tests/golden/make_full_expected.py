@@ -31,14 +31,16 @@ N_DW = 12
 
 def block_widths(N, H, V, es):
     """Vocabulary block widths of the backward at this shape: the recompute
-    path's (two softmax-gradient slabs within 512 MiB for the padded rows,
-    W rows of a block and the slab below 2^31 bytes, a multiple of 256) and
+    path's (two softmax-gradient slabs within 512 MiB for the padded rows, or
+    within 1 GiB to come closer to 8192 columns; W rows of a block and the
+    slab below 2^31 bytes; a multiple of 256) and
     the chunked mode's (32768, or narrower so that a block's W rows stay below
     2^31 bytes).  They only place samples: a change of the library's blocking
     moves the edges away from the samples, it does not make a sample wrong."""
     rows_pad = -(-N // 256) * 256
-    vb = min((512 << 20) // (2 * rows_pad * es), 0x7FFFFFFF // (rows_pad * es),
-             0x7FFFFFFF // (H * es))
+    per_col = 2 * rows_pad * es
+    vb = max((512 << 20) // per_col, min(8192, (1024 << 20) // per_col))
+    vb = min(vb, 0x7FFFFFFF // (rows_pad * es), 0x7FFFFFFF // (H * es))
     vb = max(256, vb // 256 * 256)
     vb = min(vb, -(-V // 256) * 256)
     cb = max(256, min(32768, 0x7FFFFFFF // (H * es)) // 256 * 256)

@@ -383,14 +383,19 @@ void k_fwd_lse(FwdArgs a) {
 #pragma unroll
   for (int j = 0; j < 4; ++j) ms_s[j][t] = make_float2(-INFINITY, 0.f);
   f32x16 acc[4][4];
-  for (int vt = vt0; vt < vt1; ++vt) {
+  auto w_tile = [&](int v) {
     Opnd A;
-    A.base = a.W + (int64_t)vt * kTile * ldb;
-    A.bytes = (int64_t)(a.V - vt * kTile) * ldb;
+    A.base = a.W + (int64_t)v * kTile * ldb;
+    A.bytes = (int64_t)(a.V - v * kTile) * ldb;
     A.ldb = ldb;
     A.kbytes = ldb;
+    return A;
+  };
+  for (int vt = vt0; vt < vt1; ++vt) {
+    const Opnd A = w_tile(vt);
     zero_acc(acc);
-    gemm_tile<E, LoadDirect, LoadDirect>(A, B, steps, smem, wm, wn, acc, opaque_tid());
+    if (vt == vt0) gemm_tile<E, LoadDirect, LoadDirect>(A, B, steps, smem, wm, wn, acc, opaque_tid());
+    else gemm_tile_prefetched<E>(A, B, steps, smem, wm, wn, acc, opaque_tid());
     // rows at or past V (last tile only) take no part in the reduction
     const int vlim = a.V - vt * kTile;
     float m[4], s[4];
@@ -399,6 +404,13 @@ void k_fwd_lse(FwdArgs a) {
       const float2 v = ms_s[j][t];
       m[j] = v.x;
       s[j] = v.y;
+    }
+    // the next tile's first two steps go straight into the (now idle) LDS
+    // slabs while this tile's softmax update runs in registers
+    if (vt + 1 < vt1) {
+      const int tid = opaque_tid();
+      prefetch_direct(w_tile(vt + 1), smem, steps, tid);
+      prefetch_direct(B, smem + 2 * kSlab, steps, tid);
     }
     if (vlim >= kTile) lse_update<false>(acc, m, s, 0);
     else lse_update<true>(acc, m, s, vlim - wm * 128 - 4 * (lane >> 5));

@@ -449,16 +449,34 @@ struct TilePipe {
   // slab k ^ 1, the loads of step s + 2 are issued into registers k.  Steps
   // at or past `steps` load zeros, so the loop needs no peeled tail (an odd
   // count runs one all-zero step).
-  template <int k>
+  // kCommit = false: slab k ^ 1 already holds step s + 1 (a prefetched tile's
+  // first step)
+  template <int k, bool kCommit = true>
   __device__ __forceinline__ void step(int s, f32x16 (&acc)[4][4]) {
     const bool live = s + 2 < steps;
     mma_slab<E>(sa + k * kSlab, sb + k * kSlab, fa, fb, acc, [&](int part) {
-      la[k ^ 1].commit_part(sa + (k ^ 1) * kSlab, part, tid);
-      lb[k ^ 1].commit_part(sb + (k ^ 1) * kSlab, part, tid);
+      if constexpr (kCommit) {
+        la[k ^ 1].commit_part(sa + (k ^ 1) * kSlab, part, tid);
+        lb[k ^ 1].commit_part(sb + (k ^ 1) * kSlab, part, tid);
+      }
       la[k].template issue_part<E>(A, s + 2, part, live, tid);
       lb[k].template issue_part<E>(B, s + 2, part, live, tid);
     });
     __syncthreads();
+  }
+  // run() for a tile whose steps 0 and 1 were put into slabs 0 and 1 by
+  // prefetch_direct (during the previous tile's epilogue): wait for those
+  // loads, then the same loop without the first loads and stores
+  __device__ __forceinline__ void run_prefetched(f32x16 (&acc)[4][4]) {
+    if (steps <= 0) return;
+    __builtin_amdgcn_s_waitcnt(0);   // every counter: the direct-to-LDS loads
+    __syncthreads();
+    step<0, false>(0, acc);
+    step<1>(1, acc);
+    for (int s = 2; s < steps; s += 2) {
+      step<0>(s, acc);
+      step<1>(s + 1, acc);
+    }
   }
   __device__ __forceinline__ void run(f32x16 (&acc)[4][4]) {
     if (steps <= 0) return;
@@ -494,6 +512,45 @@ __device__ __forceinline__ void gemm_tile(const Opnd& A, const Opnd& B, int step
                                           f32x16 (&acc)[4][4], int tid = threadIdx.x) {
   TilePipe<E, LA, LB> pipe(A, B, steps, smem, wm, wn, tid);
   pipe.run(acc);
+}
+
+// The second and later tiles of a kernel's tile loop, after prefetch_direct
+// put their first two steps into LDS.
+template <class E>
+__device__ __forceinline__ void gemm_tile_prefetched(const Opnd& A, const Opnd& B, int steps,
+                                                     lds_t* smem, int wm, int wn,
+                                                     f32x16 (&acc)[4][4], int tid) {
+  TilePipe<E, LoadDirect, LoadDirect> pipe(A, B, steps, smem, wm, wn, tid);
+  pipe.run_prefetched(acc);
+}
+
+// Steps 0 and 1 of a K-contiguous operand straight from memory into LDS
+// slabs 0 and 1 of that operand (slab0, slab0 + kSlab), in LoadDirect's
+// swizzled layout, with no registers in between (buffer_load_dwordx4 ... lds:
+// lane l of a wave writes 16 bytes at the wave's LDS address + 16 l, and an
+// offset past the descriptor reads zeros).  Wave w fills rows 64 w .. 64 w +
+// 63, eight rows (1 KiB) per instruction: lane l takes row 8 j + l / 8 of its
+// block and the chunk whose swizzled slot is l % 8.  Steps at or past
+// `steps`, and chunks past the rows' K extent, read zeros, as LoadDirect's.
+// Only for slabs nothing else reads or writes until run_prefetched's wait.
+__device__ __forceinline__ void prefetch_direct(const Opnd& o, lds_t* slab0, int steps,
+                                                int tid) {
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t span = (int64_t)kTile * o.ldb;
+  const rsrc_t r = make_rsrc(o.base, o.bytes < span ? o.bytes : span);
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row0 = 64 * w + 8 * j, row = row0 + (lane >> 3);
+      const int c = (lane & 7) ^ (row & 7) ^ ((row >> 3) & 1);
+      const int kb = s * kRowBytes + c * 16;
+      const int off = s < steps && kb < o.kbytes ? row * o.ldb + kb : (int)0x80000000u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          r, (__attribute__((address_space(3))) void*)(slab0 + s * kSlab + row0 * kRowBytes), 16,
+          off, 0, 0, 0);
+    }
 }
 
 __device__ __forceinline__ int opaque_tid() {

@@ -190,6 +190,22 @@ def test_chunked_workspace_is_bounded_by_the_chunk():
     assert w2 < 32768 * V * 2                # far below the logits
 
 
+def test_recompute_slabs_bounded():
+    # the backward's two softmax-gradient slabs: 512 MiB, or up to 1 GiB where
+    # that widens blocks toward 8192 columns (long context: 32768 rows get
+    # 8192-column blocks, 1 GiB); never more, however many rows
+    H, V, es = 2048, 152064, 2
+    small = F.flce_workspace_size(1, 8192, H, V, F.FLCE_DTYPE_BF16)
+    long_ = F.flce_workspace_size(1, 32768, H, V, F.FLCE_DTYPE_BF16)
+    # beside the per-row buffers (FP32 dX sums, X_c, FP32 one-hot sums: 10 H
+    # bytes, plus a few words), the slabs grew from 512 MiB to 1 GiB
+    grown = long_ - small - (32768 - 8192) * (4 * H + H * es + 4 * H)
+    assert (512 << 20) <= grown < (512 << 20) + (24 << 20)
+    assert long_ < (1 << 30) + 32768 * (10 * H + 80) + (2048 * 256 * 8) + 4 * V + (8 << 20)
+    huge = F.flce_workspace_size(1, 1 << 20, 1024, 32000, F.FLCE_DTYPE_BF16)
+    assert huge < (1 << 30) + (1 << 20) * (4 * 1024 + 2 * 1024 + 4 * 1024 + 64 + 16) + (64 << 20)
+
+
 def test_chunk_rows_past_the_2_31_byte_slab():
     # explicit chunks whose slab passes 2^31 bytes are accepted (each token
     # tile of the slab has its own 64-bit base); a vocabulary whose 256-row

@@ -93,3 +93,28 @@ def test_chunked_dx_grid_covers_every_chunk(H, C):
         s = dx_parts_for(HT, tt, target, part_tiles)
         assert (s - 1) * tt <= part_tiles                      # the parts fit the buffer
         assert covered(blocks, s * HT * tt)
+
+
+def swz(row, chunk):
+    # LDS byte offset of 16-byte chunk `chunk` of tile row `row` in a K-contiguous
+    # slab (128-byte rows, flce_tile.h)
+    return row * 128 + ((chunk ^ (row & 7) ^ ((row >> 3) & 1)) << 4)
+
+
+def test_direct_to_lds_prefetch_fills_the_loaders_layout():
+    # prefetch_direct: wave w, instruction j writes 1 KiB at the slab's row
+    # 64 w + 8 j; lane l lands at 16 l past it and must fetch the (row, chunk)
+    # that the register loader's commit stores at that address
+    seen = {}
+    for w in range(4):
+        for j in range(8):
+            row0 = 64 * w + 8 * j
+            for lane in range(64):
+                row = row0 + lane // 8
+                chunk = (lane & 7) ^ (row & 7) ^ ((row >> 3) & 1)
+                addr = row0 * 128 + 16 * lane
+                assert swz(row, chunk) == addr
+                assert (row, chunk) not in seen
+                seen[(row, chunk)] = addr
+    assert len(seen) == 256 * 8                       # every chunk of the slab once
+    assert sorted(seen.values()) == list(range(0, 256 * 128, 16))

@@ -528,6 +528,11 @@ int make_chunk_plan(int64_t B, int64_t T, int64_t H, int64_t V, int dtype, int64
         q.dx_blocks,
         (int64_t)dx_parts_for(HT, tt, FLCE_DX_TILES_CHUNKED, (int)q.part_tiles) * HT * tt);
   q.dx_blocks = pad8(q.dx_blocks);
+  // every launch within a dispatch's 32-bit work-item count (blocks x 256
+  // threads): the logits tiles of a chunk, and a block's dX and dW tiles
+  constexpr int64_t kMaxBlocks = ((int64_t)1 << 32) / kThreads - 8;
+  if (pad8(q.VT * TTc) > kMaxBlocks || q.dx_blocks + pad8(HT * cdiv(q.VB, kTile)) > kMaxBlocks)
+    return FLCE_ERR_SHAPE;
   q.o_dx32 = take(4 * q.rows_pad * H);
   q.o_dx32p = take(4 * q.part_tiles * kTile * H);
   q.P = pow2_at_least(q.rows_pad);

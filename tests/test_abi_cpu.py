@@ -221,6 +221,18 @@ def test_chunk_rows_past_the_2_31_byte_slab():
         assert e.value.code == F.FLCE_ERR_SHAPE
 
 
+def test_chunked_grid_within_a_dispatch():
+    # one chunk of 2^22 - 256 rows over a 4194048-entry vocabulary would need
+    # 2.7e8 logits workgroups, past a dispatch's 2^32 work items: refused
+    # (whatever the memory, before any launch); the same rows in the default
+    # chunks are planned
+    N, V = 2 ** 22 - 256, 4194048
+    with pytest.raises(F.FlceError) as e:
+        F.flce_chunked_workspace_size(1, N, 8, V, F.FLCE_DTYPE_BF16, N)
+    assert e.value.code == F.FLCE_ERR_SHAPE
+    assert F.flce_chunked_workspace_size(1, N, 8, V, F.FLCE_DTYPE_BF16) > 0
+
+
 def test_chunk_rows_parameter():
     # explicit chunk sizes round up to 256 rows; the slab is chunk x padded V
     H, V, es = 1024, 50000, 2

@@ -256,7 +256,9 @@ int flce_shard_backward(const void* X, const void* W, const int64_t* labels,
  * multiple of 256 (the pages' CHUNK_SIZE); 0 = as many as a 2 GiB slab holds
  * (6912 rows at V = 152064 bf16).  Capped at the padded row count.  A 256-row
  * tile of the slab must stay below 2^31 bytes (V <= 4194048 for bf16,
- * 2096896 for fp32), else FLCE_ERR_SHAPE.
+ * 2096896 for fp32), and a chunk's 256 x 256 logits tiles, like a vocabulary
+ * block's dX and dW tiles, must fit one dispatch (fewer than 2^24
+ * workgroups of 256 threads); else FLCE_ERR_SHAPE.
  *
  * flce_chunked_workspace_size -- bytes of device scratch flce_chunked needs
  * (host-only arithmetic).  Other arguments as flce_workspace_size.

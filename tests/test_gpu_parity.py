@@ -30,6 +30,11 @@ SMALL = [
     ("ragged_vocab", dict(T=1031, H=128, V=4099, seed=51)),
     # N large enough that the backward splits the vocabulary into blocks
     ("qwen2_7b_head", dict(T=8193, H=64, V=40013, seed=61)),
+    # forward work items of several vocabulary tiles (the later ones start
+    # from LDS stages filled during the previous tile's epilogue) with H
+    # ending in a partial K step (bf16: 400 of 512 bytes; fp32: 800 of 896)
+    ("qwen2_7b_head", dict(T=6600, H=200, V=20011, seed=71)),
+    ("tiny_f32", dict(B=2, T=3300, H=200, V=20011, seed=72)),
 ]
 
 
